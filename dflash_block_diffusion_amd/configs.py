@@ -83,7 +83,8 @@ class PairConfig:
         t = replace(self.target, n_layers=target_layers,
                     layer_kinds=kinds if self.target.layer_kinds else ())
         d = replace(self.drafter, n_layers=drafter_layers)
-        sel = tuple(sorted(set(min(l, target_layers - 1) for l in self.sel_layers)))
+        # keep up to two conditioning layers: the first layers of the reduced stack
+        sel = tuple(range(min(2, len(self.sel_layers), target_layers)))
         return replace(self, name=f"{self.name}-L{target_layers}d{drafter_layers}",
                        target=t, drafter=d, sel_layers=sel)
 

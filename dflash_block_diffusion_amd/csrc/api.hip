@@ -1,0 +1,725 @@
+// Host side of libdflash: the C ABI declared in include/dflash.h.
+//
+// Orchestrates the kernels of one draft+verify step on a caller's stream:
+//   draft   context projection (fc + RMSNorm) of the rows the previous verify
+//           committed, embedding of [anchor, mask x (B-1)], drafter layers
+//           (block queries over committed-context + block keys, bidirectional),
+//           final norm, the TARGET's lm-head + argmax (drafts d_1..d_{B-1});
+//   verify  embedding of the block, target layers (causal over context and
+//           block; GatedDeltaNet layers record their tape), conditioning-layer
+//           outputs copied to the drafter's context buffer, lm-head + argmax;
+//   accept  longest matching prefix + correction;
+//   commit  GDN tape replay, n += a+1, token log, pending context rows.
+// Every length that changes per step is read by the kernels from device
+// memory, so one step can be captured once as a hipGraph and replayed.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "dflash.h"
+
+using namespace dfl;
+
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(x)                                                                          \
+  do {                                                                                     \
+    hipError_t e_ = (x);                                                                   \
+    if (e_ != hipSuccess) return fail(DFLASH_E_DEVICE, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" const char* dflash_last_error(void) { return g_err.c_str(); }
+
+extern "C" int dflash_device_count(int* h_count) {
+  if (!h_count) return fail(DFLASH_E_INVALID, "h_count is null");
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) { *h_count = 0; return fail(DFLASH_E_DEVICE, hipGetErrorString(e)); }
+  *h_count = n;
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ weights
+static bool fmt_ok(int fmt) { return fmt >= DFLASH_FMT_F32 && fmt <= DFLASH_FMT_W4A16; }
+
+static int check_gemm_shape(int fmt, int n, int k, int gate_up) {
+  if (n <= 0 || k <= 0) return fail(DFLASH_E_SHAPE, "GEMM dims must be positive");
+  if (n % (gate_up ? 32 : 16)) return fail(DFLASH_E_SHAPE, "GEMM N must be a multiple of 16 (32 for gate/up)");
+  if (fmt != DFLASH_FMT_F32 && k % tile_k(fmt))
+    return fail(DFLASH_E_SHAPE, "GEMM K must be a multiple of " + std::to_string(tile_k(fmt)) + " for this format");
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_packed_bytes(int fmt, int n, int k, size_t* wb, size_t* sb) {
+  if (!fmt_ok(fmt) || !wb || !sb) return fail(DFLASH_E_INVALID, "bad format or null output");
+  int rc = check_gemm_shape(fmt, n, k, 0);
+  if (rc) return rc;
+  packed_bytes(fmt, n, k, wb, sb);
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_pack_weight(int fmt, int n, int k, int gate_up, const void* src, const void* src_scales,
+                                  void* dst, void* dst_scales, void* stream) {
+  if (!fmt_ok(fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
+  if (!src || !dst) return fail(DFLASH_E_INVALID, "null source or destination");
+  if ((fmt == DFLASH_FMT_W8A16 || fmt == DFLASH_FMT_W4A16) && (!src_scales || !dst_scales))
+    return fail(DFLASH_E_INVALID, "quantised formats need scales");
+  int rc = check_gemm_shape(fmt, n, k, gate_up);
+  if (rc) return rc;
+  HIPCHK(launch_pack(fmt, n, k, gate_up, src, src_scales, dst, dst_scales, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+static GemmW mkw(int fmt, int n, int k, int gu, const void* w, const void* s);
+
+// ------------------------------------------------------------------ one linear
+struct LinearWs {
+  size_t ws_off, ctr_off, amv_off, ami_off, lg_off, total;
+};
+
+static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
+  LinearWs L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
+  L.ws_off = take(std::max<size_t>(gemm_ws_floats(fmt, n, k, m), 1) * 4);
+  L.ctr_off = take((size_t)(n / 16 + 1) * 4);
+  const int am = std::max(1, gemm_am_blocks(fmt, n, m));
+  L.amv_off = take((size_t)am * 64 * 4);
+  L.ami_off = take((size_t)am * 64 * 4);
+  L.lg_off = take(fmt == DFLASH_FMT_F32 ? (size_t)MAX_ROWS * n * 4 : 4);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m) {
+  if (!fmt_ok(fmt) || check_gemm_shape(fmt, n, k, 0) || m < 1 || m > MAX_ROWS) return 0;
+  return linear_ws_layout(fmt, n, k, m).total;
+}
+
+extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* sc, const void* x, int m,
+                             int epilogue, float* out, int32_t* am, void* ws, size_t ws_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
+  int rc = check_gemm_shape(fmt, n, k, 0);
+  if (rc) return rc;
+  if (m < 1 || m > MAX_ROWS) return fail(DFLASH_E_SHAPE, "m must be in [1, 64]");
+  if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
+  if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");
+  if (epilogue == 1 && !am) return fail(DFLASH_E_INVALID, "epilogue 1 needs d_argmax");
+  if (epilogue != 0 && epilogue != 1) return fail(DFLASH_E_INVALID, "unknown epilogue");
+  const LinearWs L = linear_ws_layout(fmt, n, k, m);
+  if (ws_bytes < L.total) return fail(DFLASH_E_INVALID, "workspace too small");
+  char* b = (char*)ws;
+  Workspace W;
+  W.ws = (float*)(b + L.ws_off); W.ws_floats = gemm_ws_floats(fmt, n, k, m);
+  W.counters = (int*)(b + L.ctr_off); W.n_counters = n / 16 + 1;
+  W.am_val = (float*)(b + L.amv_off); W.am_idx = (int*)(b + L.ami_off);
+  W.am_cap = std::max(1, gemm_am_blocks(fmt, n, m));
+  W.logits_tmp = (float*)(b + L.lg_off);
+  GemmW g = mkw(fmt, n, k, 0, w, sc);
+  GemmCall c;
+  c.W = &g; c.x = x; c.ldx = k; c.m = m;
+  c.epi = epilogue == 0 ? EPI_STORE : EPI_ARGMAX;
+  c.out = out; c.ldo = n; c.otype = T_F32;
+  c.side = nullptr; c.ld_side = 0; c.side_type = 0;
+  c.logits = epilogue == 1 ? out : nullptr; c.ldl = n; c.row0 = 0; c.am_out = am;
+  HIPCHK(launch_gemm(c, W, (hipStream_t)stream, nullptr, nullptr));
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ models
+struct Layer {
+  int kind;
+  const float *in_norm, *post_norm, *q_norm, *k_norm;
+  GemmW qkv, o, gu, down;
+};
+
+struct dflash_model {
+  dflash_model_desc d;
+  std::vector<Layer> layers;
+  GemmW lm{}, fc{};
+  const dflash_model* target = nullptr;   // drafter: bound target
+  bool drafter = false;
+  int act = T_F32;                        // residual / KV / q type
+  int gin = T_F32;                        // GEMM input type
+  int n_gdn = 0;
+};
+
+static GemmW mkw(int fmt, int n, int k, int gu, const void* w, const void* s) {
+  GemmW g;
+  g.fmt = fmt; g.n = n; g.k = k; g.gate_up = gu; g.w = w; g.s = s;
+  return g;
+}
+
+extern "C" int dflash_model_create(const dflash_model_desc* desc, dflash_model** out) {
+  if (!desc || !out) return fail(DFLASH_E_INVALID, "null desc or out");
+  *out = nullptr;
+  const dflash_model_desc& d = *desc;
+  if (!fmt_ok(d.fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
+  if (d.n_layers <= 0 || !d.layers) return fail(DFLASH_E_INVALID, "no layers");
+  if (d.hidden <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.ffn <= 0 || d.vocab <= 1)
+    return fail(DFLASH_E_SHAPE, "non-positive dimension");
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(DFLASH_E_SHAPE, "head_dim must be 64 or 128");
+  if (d.fmt != DFLASH_FMT_F32 && d.head_dim != 128)
+    return fail(DFLASH_E_SHAPE, "16-bit attention needs head_dim 128");
+  if (d.n_q_heads % d.n_kv_heads) return fail(DFLASH_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (d.hidden % 16) return fail(DFLASH_E_SHAPE, "hidden must be a multiple of 16");
+  const bool drafter = d.w_fc != nullptr;
+  if (!drafter && (!d.embed || !d.w_lm || !d.final_norm))
+    return fail(DFLASH_E_INVALID, "a target needs embed, w_lm and final_norm");
+  if (drafter && (!d.hidden_norm || !d.final_norm || d.n_sel <= 0 || d.n_sel > 8))
+    return fail(DFLASH_E_INVALID, "a drafter needs w_fc, hidden_norm, final_norm and 1..8 sel_layers");
+  if (drafter && (d.mask_token < 0 || d.mask_token >= d.vocab)) return fail(DFLASH_E_INVALID, "mask_token out of range");
+  auto* m = new dflash_model();
+  m->d = d;
+  m->drafter = drafter;
+  m->act = d.fmt == DFLASH_FMT_F32 ? T_F32 : T_BF16;
+  m->gin = d.fmt == DFLASH_FMT_F32 ? T_F32 : d.fmt == DFLASH_FMT_BF16 ? T_BF16 : T_F16;
+  const int H = d.hidden, F = d.ffn, hq = d.n_q_heads, hkv = d.n_kv_heads, hd = d.head_dim;
+  int rc = DFLASH_OK;
+  for (int l = 0; l < d.n_layers && rc == DFLASH_OK; ++l) {
+    const dflash_layer_desc& L = d.layers[l];
+    Layer y;
+    y.kind = L.kind;
+    y.in_norm = L.in_norm; y.post_norm = L.post_norm; y.q_norm = L.q_norm; y.k_norm = L.k_norm;
+    if (!L.in_norm || !L.post_norm || !L.w_qkv || !L.w_o || !L.w_gu || !L.w_down) {
+      rc = fail(DFLASH_E_INVALID, "layer " + std::to_string(l) + " is missing a tensor");
+      break;
+    }
+    if (L.kind == DFLASH_LAYER_ATTN) {
+      if (!L.q_norm || !L.k_norm) { rc = fail(DFLASH_E_INVALID, "attention layer needs q/k norms"); break; }
+      y.qkv = mkw(d.fmt, (hq + 2 * hkv) * hd, H, 0, L.w_qkv, L.s_qkv);
+      y.o = mkw(d.fmt, H, hq * hd, 0, L.w_o, L.s_o);
+    } else if (L.kind == DFLASH_LAYER_GDN) {
+      if (drafter) { rc = fail(DFLASH_E_UNSUPPORTED, "GatedDeltaNet layers are supported in targets only"); break; }
+      const int gh = d.gdn_heads, dk = d.gdn_dk, dv = d.gdn_dv;
+      if (!((dk == 128 && dv == 128) || (dk == 32 && dv == 32)) || gh <= 0) {
+        rc = fail(DFLASH_E_SHAPE, "GatedDeltaNet needs dk == dv in {32, 128}");
+        break;
+      }
+      y.qkv = mkw(d.fmt, gh * (2 * dk + dv) + 2 * gh, H, 0, L.w_qkv, L.s_qkv);
+      y.o = mkw(d.fmt, H, gh * dv, 0, L.w_o, L.s_o);
+      m->n_gdn++;
+    } else {
+      rc = fail(DFLASH_E_INVALID, "unknown layer kind");
+      break;
+    }
+    y.gu = mkw(d.fmt, 2 * F, H, 1, L.w_gu, L.s_gu);
+    y.down = mkw(d.fmt, H, F, 0, L.w_down, L.s_down);
+    for (const GemmW* g : {&y.qkv, &y.o, &y.gu, &y.down}) {
+      if (rc == DFLASH_OK) rc = check_gemm_shape(g->fmt, g->n, g->k, g->gate_up);
+      if (rc == DFLASH_OK && g->fmt >= DFLASH_FMT_W8A16 && !g->s) rc = fail(DFLASH_E_INVALID, "missing scales");
+    }
+    m->layers.push_back(y);
+  }
+  if (rc == DFLASH_OK && !drafter) {
+    m->lm = mkw(d.fmt, d.vocab, H, 0, d.w_lm, d.s_lm);
+    rc = check_gemm_shape(d.fmt, d.vocab, H, 0);
+  }
+  if (rc == DFLASH_OK && drafter) {
+    m->fc = mkw(d.fmt, H, d.n_sel * H, 0, d.w_fc, d.s_fc);
+    rc = check_gemm_shape(d.fmt, H, d.n_sel * H, 0);
+  }
+  if (rc != DFLASH_OK) { delete m; return rc; }
+  m->d.layers = nullptr;   // the caller's array is not kept
+  *out = m;
+  return DFLASH_OK;
+}
+
+extern "C" void dflash_model_destroy(dflash_model* m) { delete m; }
+
+extern "C" int dflash_drafter_bind(dflash_model* drafter, const dflash_model* target) {
+  if (!drafter || !target) return fail(DFLASH_E_INVALID, "null model");
+  if (!drafter->drafter || target->drafter) return fail(DFLASH_E_INVALID, "bind(drafter, target) arguments swapped");
+  if (drafter->d.hidden != target->d.hidden || drafter->d.vocab != target->d.vocab)
+    return fail(DFLASH_E_SHAPE, "drafter and target must share hidden size and vocab");
+  if (drafter->act != target->act) return fail(DFLASH_E_SHAPE, "drafter and target activation types differ");
+  for (int i = 0; i < drafter->d.n_sel; ++i) {
+    const int l = drafter->d.sel_layers[i];
+    if (l < 0 || l >= target->d.n_layers || (i > 0 && l <= drafter->d.sel_layers[i - 1]))
+      return fail(DFLASH_E_SHAPE, "conditioning layers must be ascending target layer indices");
+  }
+  drafter->target = target;
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ state
+struct ProfRec { const char* name; double bytes; hipEvent_t a, b; };
+
+struct dflash_state {
+  const dflash_model* t = nullptr;
+  const dflash_model* dr = nullptr;
+  int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
+  char* base = nullptr;
+  size_t bytes = 0;
+  int32_t* scal = nullptr;
+  int32_t* tokens = nullptr;
+  int32_t* acc_log = nullptr;
+  int acc_log_len = 4096;
+  float* cos_t = nullptr;
+  float* sin_t = nullptr;
+  int32_t* pt = nullptr;
+  std::vector<void*> tk, tv, dk, dv;
+  void* x = nullptr;      // residual [64][H] act
+  void* bu = nullptr;     // norm outputs / QKV input [64][H] gin
+  void* ba = nullptr;     // attention or GDN output [64][max(hq*d, gh*dv)] gin
+  void* bf = nullptr;     // SiLU*mul output [64][F] gin
+  void* bqkv = nullptr;   // QKV / GDN projection [64][Nqkv] act
+  void* bq = nullptr;     // q after norm+rope [B][hq][d] act
+  void* fco = nullptr;    // fc output [64][H] act
+  void* side = nullptr;   // drafter context input [64][n_sel*H] drafter gin
+  float* o_part = nullptr;
+  float* ml_part = nullptr;
+  Workspace ws{};
+  int32_t* ybuf = nullptr;   // [64] prefill argmax scratch
+  int32_t* blk = nullptr;    // [64] prefill draft scratch
+  float* gdn_S = nullptr;
+  float* gdn_snap = nullptr;
+  float* gdn_tape = nullptr;
+  int snap_n = -1;
+  bool prof = false;
+  std::vector<ProfRec> prof_recs;
+  std::vector<hipEvent_t> ev_pool;
+};
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(char* b) : base(b) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+static int gdn_rec(const dflash_model* t) { return t->d.gdn_dk + t->d.gdn_dv + 2; }
+
+static void carve(dflash_state* s, Carver& c) {
+  const dflash_model *t = s->t, *d = s->dr;
+  const int H = t->d.hidden, B = s->B;
+  const int eb = t->act == T_F32 ? 4 : 2;
+  s->scal = c.take<int32_t>(SC_COUNT);
+  s->tokens = c.take<int32_t>(s->capacity + 64);
+  s->acc_log = c.take<int32_t>(s->acc_log_len);
+  s->cos_t = c.take<float>((size_t)s->capacity * (t->d.head_dim / 2));
+  s->sin_t = c.take<float>((size_t)s->capacity * (t->d.head_dim / 2));
+  s->pt = c.take<int32_t>(s->pages);
+  const size_t tkv = (size_t)s->pages * t->d.n_kv_heads * PAGE * t->d.head_dim * eb;
+  s->tk.assign(t->d.n_layers, nullptr);
+  s->tv.assign(t->d.n_layers, nullptr);
+  for (int l = 0; l < t->d.n_layers; ++l)
+    if (t->layers[l].kind == DFLASH_LAYER_ATTN) { s->tk[l] = c.take<char>(tkv); s->tv[l] = c.take<char>(tkv); }
+  const size_t dkv = (size_t)s->pages * d->d.n_kv_heads * PAGE * d->d.head_dim * eb;
+  s->dk.assign(d->d.n_layers, nullptr);
+  s->dv.assign(d->d.n_layers, nullptr);
+  for (int l = 0; l < d->d.n_layers; ++l) { s->dk[l] = c.take<char>(dkv); s->dv[l] = c.take<char>(dkv); }
+  int qkv_n = 0, att_w = 0, F = 0;
+  for (const dflash_model* m : {t, d}) {
+    for (const Layer& L : m->layers) {
+      qkv_n = std::max(qkv_n, L.qkv.n);
+      att_w = std::max(att_w, L.o.k);
+    }
+    F = std::max(F, m->d.ffn);
+  }
+  s->x = c.take<char>((size_t)MAX_ROWS * H * 4);
+  s->bu = c.take<char>((size_t)MAX_ROWS * H * 4);
+  s->ba = c.take<char>((size_t)MAX_ROWS * att_w * 4);
+  s->bf = c.take<char>((size_t)MAX_ROWS * F * 4);
+  s->bqkv = c.take<char>((size_t)MAX_ROWS * qkv_n * 4);
+  s->bq = c.take<char>((size_t)B * t->d.n_q_heads * t->d.head_dim * 4 + (size_t)B * d->d.n_q_heads * d->d.head_dim * 4);
+  s->fco = c.take<char>((size_t)MAX_ROWS * H * 4);
+  s->side = c.take<char>((size_t)MAX_ROWS * d->d.n_sel * H * 4);
+  const int hq = std::max(t->d.n_q_heads, d->d.n_q_heads), hd = std::max(t->d.head_dim, d->d.head_dim);
+  s->o_part = c.take<float>((size_t)s->max_splits * B * hq * hd);
+  s->ml_part = c.take<float>((size_t)s->max_splits * B * hq * 2);
+  // GEMM workspaces: the largest need over every weight of both stacks
+  size_t wsf = 0;
+  int am = 0, ctr = 1;
+  auto need = [&](const GemmW& g, int m) {
+    wsf = std::max(wsf, gemm_ws_floats(g.fmt, g.n, g.k, m));
+    ctr = std::max(ctr, g.n / 16);
+  };
+  for (const Layer& L : t->layers) { need(L.qkv, B); need(L.o, B); need(L.gu, B); need(L.down, B); }
+  for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.gu, B); need(L.down, B); }
+  need(d->fc, B);
+  need(t->lm, B);
+  am = std::max(1, gemm_am_blocks(t->lm.fmt, t->lm.n, B));
+  s->ws.ws = c.take<float>(std::max<size_t>(wsf, 64));
+  s->ws.ws_floats = wsf;
+  s->ws.counters = c.take<int>(ctr);
+  s->ws.n_counters = ctr;
+  s->ws.am_val = c.take<float>((size_t)am * 64);
+  s->ws.am_idx = c.take<int>((size_t)am * 64);
+  s->ws.am_cap = am;
+  s->ws.logits_tmp = t->d.fmt == DFLASH_FMT_F32 ? c.take<float>((size_t)MAX_ROWS * t->d.vocab) : nullptr;
+  s->ybuf = c.take<int32_t>(64);
+  s->blk = c.take<int32_t>(64);
+  const size_t sf = (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk;
+  s->gdn_S = t->n_gdn ? c.take<float>(sf) : nullptr;
+  s->gdn_snap = t->n_gdn ? c.take<float>(sf) : nullptr;
+  s->gdn_tape = t->n_gdn ? c.take<float>((size_t)t->n_gdn * B * t->d.gdn_heads * gdn_rec(t)) : nullptr;
+}
+
+static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model* d, int max_ctx, int block) {
+  if (!t || !d) return fail(DFLASH_E_INVALID, "null model");
+  if (d->target != t) return fail(DFLASH_E_INVALID, "the drafter is not bound to this target");
+  if (block != 16 && block != 32) return fail(DFLASH_E_SHAPE, "block must be 16 or 32");
+  if (max_ctx < 1) return fail(DFLASH_E_SHAPE, "max_ctx must be positive");
+  s->t = t; s->dr = d; s->B = block; s->max_ctx = max_ctx;
+  const int need = max_ctx + 2 * block;
+  s->pages = (need + PAGE - 1) / PAGE;
+  s->capacity = s->pages * PAGE;
+  s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  return DFLASH_OK;
+}
+
+extern "C" size_t dflash_state_bytes(const dflash_model* t, const dflash_model* d, int max_ctx, int block) {
+  dflash_state s;
+  if (setup_dims(&s, t, d, max_ctx, block) != DFLASH_OK) return 0;
+  Carver c(nullptr);
+  carve(&s, c);
+  return c.off + 256;
+}
+
+extern "C" int dflash_state_init(dflash_state** out, const dflash_model* t, const dflash_model* d, void* arena,
+                                 size_t arena_bytes, int max_ctx, int block) {
+  if (!out || !arena) return fail(DFLASH_E_INVALID, "null out or arena");
+  *out = nullptr;
+  auto* s = new dflash_state();
+  int rc = setup_dims(s, t, d, max_ctx, block);
+  if (rc) { delete s; return rc; }
+  Carver probe(nullptr);
+  carve(s, probe);
+  if (probe.off + 256 > arena_bytes) {
+    delete s;
+    return fail(DFLASH_E_CAPACITY, "arena too small: need " + std::to_string(probe.off + 256) + " bytes");
+  }
+  char* base = (char*)(((uintptr_t)arena + 255) & ~(uintptr_t)255);
+  Carver c(base);
+  carve(s, c);
+  s->base = base;
+  s->bytes = c.off;
+  // zero the whole arena (KV pages are read whole: unwritten slots must be finite)
+  hipError_t e = launch_fill_i32((int32_t*)base, c.off / 4, 0, nullptr);
+  // RoPE table: angle pos * base^(-2i/d) in double, cos/sin rounded to fp32
+  const int half = t->d.head_dim / 2;
+  std::vector<float> cs((size_t)s->capacity * half), sn((size_t)s->capacity * half);
+  for (int p = 0; p < s->capacity; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow(t->d.rope_base, -2.0 * i / t->d.head_dim);
+      const double ang = (double)p * inv;
+      cs[(size_t)p * half + i] = (float)std::cos(ang);
+      sn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+  std::vector<int32_t> pt(s->pages);
+  for (int i = 0; i < s->pages; ++i) pt[i] = i;     // pages handed out in order
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(s->cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(s->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(s->pt, pt.data(), pt.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    delete s;
+    return fail(DFLASH_E_DEVICE, std::string("state init: ") + hipGetErrorString(e));
+  }
+  *out = s;
+  return DFLASH_OK;
+}
+
+extern "C" void dflash_state_destroy(dflash_state* s) {
+  if (!s) return;
+  for (auto& r : s->prof_recs) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
+  for (auto ev : s->ev_pool) hipEventDestroy(ev);
+  delete s;
+}
+
+// ------------------------------------------------------------------ helpers
+static hipEvent_t take_event(dflash_state* s) {
+  if (!s->ev_pool.empty()) { hipEvent_t e = s->ev_pool.back(); s->ev_pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  hipEventCreate(&e);
+  return e;
+}
+
+static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, void* out, int ldo,
+                int otype, hipStream_t st, void* side = nullptr, int ld_side = 0, int side_type = 0,
+                float* logits = nullptr, int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
+  GemmCall c;
+  c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi; c.out = out; c.ldo = ldo; c.otype = otype;
+  c.side = side; c.ld_side = ld_side; c.side_type = side_type;
+  c.logits = logits; c.ldl = ldl; c.row0 = row0; c.am_out = am_out;
+  const char* name = nullptr;
+  double bytes = 0;
+  hipEvent_t ea = nullptr, eb = nullptr;
+  if (s->prof) { ea = take_event(s); eb = take_event(s); hipEventRecord(ea, st); }
+  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes);
+  if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, ea, eb}); }
+  if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm: ") + hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+#define RC(x) do { int rc_ = (x); if (rc_) return rc_; } while (0)
+
+static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer& L, bool draft, hipStream_t st) {
+  const int H = m->d.hidden, B = s->B, hq = m->d.n_q_heads, hkv = m->d.n_kv_heads, hd = m->d.head_dim;
+  const int rows = draft ? 2 * B : B;
+  HIPCHK(launch_rmsnorm(s->x, m->act, H, s->bu, m->gin, H, L.in_norm, B, H, m->d.eps, st));
+  RC(gemm(s, L.qkv, s->bu, H, rows, EPI_STORE, s->bqkv, L.qkv.n, m->act, st));
+  RopeCall rc;
+  rc.qkv = s->bqkv; rc.ldqkv = L.qkv.n; rc.atype = m->act;
+  rc.block_rows = B; rc.ctx_rows = draft ? B : 0;
+  rc.dev_n = s->scal + SC_N; rc.dev_p = draft ? s->scal + SC_P : nullptr;
+  rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = m->d.eps;
+  rc.cos_t = s->cos_t; rc.sin_t = s->sin_t; rc.q_out = s->bq;
+  rc.kc = draft ? s->dk[l] : s->tk[l]; rc.vc = draft ? s->dv[l] : s->tv[l];
+  rc.page_table = s->pt; rc.capacity = s->capacity; rc.hq = hq; rc.hkv = hkv; rc.d = hd;
+  HIPCHK(launch_qk_rope(rc, st));
+  AttnCall ac;
+  ac.q = s->bq; ac.atype = m->act; ac.kc = rc.kc; ac.vc = rc.vc; ac.page_table = s->pt;
+  ac.dev_n = s->scal + SC_N; ac.block_rows = B; ac.causal = draft ? 0 : 1;
+  ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits;
+  ac.o_part = s->o_part; ac.ml_part = s->ml_part; ac.out = s->ba; ac.otype = m->gin; ac.ldo = hq * hd;
+  HIPCHK(launch_attention(ac, st));
+  RC(gemm(s, L.o, s->ba, hq * hd, B, EPI_RESID, s->x, H, m->act, st));
+  return DFLASH_OK;
+}
+
+static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, hipStream_t st, void* side, int ld_side,
+               int side_type) {
+  const int H = m->d.hidden, F = m->d.ffn, B = s->B;
+  HIPCHK(launch_rmsnorm(s->x, m->act, H, s->bu, m->gin, H, L.post_norm, B, H, m->d.eps, st));
+  RC(gemm(s, L.gu, s->bu, H, B, EPI_SILU, s->bf, F, m->gin, st));
+  RC(gemm(s, L.down, s->bf, F, B, EPI_RESID, s->x, H, m->act, st, side, ld_side, side_type));
+  return DFLASH_OK;
+}
+
+static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t st) {
+  const dflash_model *t = s->t, *d = s->dr;
+  const int H = d->d.hidden, B = s->B;
+  // context projection of the rows the last verify committed -> QKV input rows B..2B-1
+  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_STORE, s->fco, H, d->act, st));
+  HIPCHK(launch_rmsnorm(s->fco, d->act, H, (char*)s->bu + (size_t)B * H * elem_bytes(d->gin), d->gin, H,
+                        d->d.hidden_norm, B, H, d->d.eps, st));
+  HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 1, d->d.mask_token, B, s->x, H,
+                      s->scal + SC_STATUS, st));
+  for (int l = 0; l < d->d.n_layers; ++l) {
+    RC(attn_layer(s, d, l, d->layers[l], true, st));
+    RC(ffn(s, d, d->layers[l], st, nullptr, 0, 0));
+  }
+  HIPCHK(launch_rmsnorm(s->x, d->act, H, s->bu, t->gin, H, d->d.final_norm, B, H, d->d.eps, st));
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 1, block + 1));
+  return DFLASH_OK;
+}
+
+static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, hipStream_t st) {
+  const dflash_model *t = s->t, *d = s->dr;
+  const int H = t->d.hidden, B = s->B;
+  HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 0, 0, B, s->x, H, s->scal + SC_STATUS, st));
+  int sel = 0, g = 0;
+  for (int l = 0; l < t->d.n_layers; ++l) {
+    const Layer& L = t->layers[l];
+    if (L.kind == DFLASH_LAYER_ATTN) {
+      RC(attn_layer(s, t, l, L, false, st));
+    } else {
+      const int gh = t->d.gdn_heads, dkk = t->d.gdn_dk, dvv = t->d.gdn_dv;
+      HIPCHK(launch_rmsnorm(s->x, t->act, H, s->bu, t->gin, H, L.in_norm, B, H, t->d.eps, st));
+      RC(gemm(s, L.qkv, s->bu, H, B, EPI_STORE, s->bqkv, L.qkv.n, t->act, st));
+      GdnCall gc;
+      gc.proj = s->bqkv; gc.ldp = L.qkv.n; gc.atype = t->act; gc.rows = B; gc.gh = gh; gc.dk = dkk; gc.dv = dvv;
+      gc.S = s->gdn_S + (size_t)g * gh * dvv * dkk;
+      gc.tape = s->gdn_tape + (size_t)g * B * gh * gdn_rec(t);
+      gc.out = s->ba; gc.otype = t->gin; gc.ldo = gh * dvv;
+      HIPCHK(launch_gdn_verify(gc, st));
+      RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_RESID, s->x, H, t->act, st));
+      ++g;
+    }
+    void* side = nullptr;
+    if (sel < d->d.n_sel && d->d.sel_layers[sel] == l) {
+      side = (char*)s->side + (size_t)sel * H * elem_bytes(d->gin);
+      ++sel;
+    }
+    RC(ffn(s, t, L, st, side, d->d.n_sel * H, d->gin));
+  }
+  HIPCHK(launch_rmsnorm(s->x, t->act, H, s->bu, t->gin, H, t->d.final_norm, B, H, t->d.eps, st));
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 0, argmax));
+  return DFLASH_OK;
+}
+
+static int do_commit(dflash_state* s, const int32_t* d_acc, int host_count, const int32_t* emit, hipStream_t st) {
+  const dflash_model* t = s->t;
+  if (t->n_gdn)
+    HIPCHK(launch_gdn_replay(s->gdn_S, s->gdn_tape, t->n_gdn, s->B, t->d.gdn_heads, t->d.gdn_dk, t->d.gdn_dv,
+                             d_acc, host_count, s->scal, s->capacity, st));
+  HIPCHK(launch_commit(s->scal, d_acc, host_count, emit, s->tokens, s->acc_log, s->acc_log_len, s->capacity,
+                       s->B, st));
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ ABI
+extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_tokens, int32_t* d_first,
+                              void* stream) {
+  if (!s || !d_tokens || !d_first) return fail(DFLASH_E_INVALID, "null argument");
+  if (n_tokens < 1) return fail(DFLASH_E_SHAPE, "empty prompt");
+  if (n_tokens + 2 * s->B > s->capacity || n_tokens > s->max_ctx)
+    return fail(DFLASH_E_CAPACITY, "prompt longer than the state's max_ctx");
+  hipStream_t st = (hipStream_t)stream;
+  const dflash_model* t = s->t;
+  HIPCHK(launch_set_scalars(s->scal, 0, 0, 1, st));
+  HIPCHK(launch_copy_tokens(d_tokens, s->tokens, n_tokens, st));
+  if (t->n_gdn)
+    HIPCHK(launch_fill_i32((int32_t*)s->gdn_S,
+                           (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk, 0, st));
+  int last = 0;
+  for (int c0 = 0; c0 < n_tokens; c0 += s->B) {
+    const int len = std::min(s->B, n_tokens - c0);
+    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, st));
+    RC(do_commit(s, nullptr, len, nullptr, st));
+    RC(do_draft(s, s->blk, nullptr, st));          // appends the chunk's drafter context rows
+    last = len;
+  }
+  HIPCHK(launch_copy_tokens(s->ybuf + last - 1, s->tokens + n_tokens, 1, st));
+  HIPCHK(launch_copy_tokens(s->ybuf + last - 1, d_first, 1, st));
+  HIPCHK(launch_set_scalars(s->scal, -1, 0, 0, st));
+  s->snap_n = -1;
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_draft_block(dflash_state* s, int32_t* d_block, float* d_logits, void* stream) {
+  if (!s || !d_block) return fail(DFLASH_E_INVALID, "null argument");
+  return do_draft(s, d_block, d_logits, (hipStream_t)stream);
+}
+
+extern "C" int dflash_verify_block(dflash_state* s, const int32_t* d_block, int32_t* d_argmax, float* d_logits,
+                                   void* stream) {
+  if (!s || !d_block || !d_argmax) return fail(DFLASH_E_INVALID, "null argument");
+  return do_verify(s, d_block, d_argmax, d_logits, (hipStream_t)stream);
+}
+
+extern "C" int dflash_accept(const int32_t* d_block, const int32_t* d_argmax, int block, int32_t* d_accept,
+                             int32_t* d_emit, int32_t* d_next_anchor, void* stream) {
+  if (!d_block || !d_argmax || !d_accept || !d_emit) return fail(DFLASH_E_INVALID, "null argument");
+  if (block < 2 || block > 64) return fail(DFLASH_E_SHAPE, "block must be in [2, 64]");
+  HIPCHK(launch_accept(d_block, d_argmax, block, d_accept, d_emit, d_next_anchor, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_kv_commit(dflash_state* s, const int32_t* d_accept, const int32_t* d_emit, void* stream) {
+  if (!s || !d_accept) return fail(DFLASH_E_INVALID, "null argument");
+  return do_commit(s, d_accept, 0, d_emit, (hipStream_t)stream);
+}
+
+static int read_scalars(dflash_state* s, int32_t* h, hipStream_t st) {
+  HIPCHK(hipStreamSynchronize(st));
+  HIPCHK(hipMemcpy(h, s->scal, SC_COUNT * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_kv_rollback(dflash_state* s, int new_len, int32_t* d_block, void* stream) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t h[SC_COUNT];
+  RC(read_scalars(s, h, st));
+  if (new_len < 1 || new_len > h[SC_N]) return fail(DFLASH_E_SHAPE, "rollback length outside [1, n]");
+  if (s->t->n_gdn) {
+    if (s->snap_n != new_len)
+      return fail(DFLASH_E_UNSUPPORTED, "GatedDeltaNet rollback needs a snapshot taken at that length");
+    const size_t sf = (size_t)s->t->n_gdn * s->t->d.gdn_heads * s->t->d.gdn_dv * s->t->d.gdn_dk;
+    HIPCHK(launch_copy_f32(s->gdn_snap, s->gdn_S, sf, st));
+  }
+  HIPCHK(launch_rollback(s->scal, new_len, s->tokens, d_block, st));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_gdn_snapshot(dflash_state* s, void* stream) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t h[SC_COUNT];
+  RC(read_scalars(s, h, st));
+  if (s->t->n_gdn) {
+    const size_t sf = (size_t)s->t->n_gdn * s->t->d.gdn_heads * s->t->d.gdn_dv * s->t->d.gdn_dk;
+    HIPCHK(launch_copy_f32(s->gdn_S, s->gdn_snap, sf, st));
+  }
+  s->snap_n = h[SC_N];
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_inject(dflash_state* s, int32_t* d_block, const int32_t* d_ref, int ref_len,
+                             const int32_t* d_sched, int n_sched, const int32_t* d_filler, void* stream) {
+  if (!s || !d_block || !d_ref || !d_sched || !d_filler) return fail(DFLASH_E_INVALID, "null argument");
+  if (n_sched < 1 || ref_len < 1) return fail(DFLASH_E_SHAPE, "empty schedule or reference");
+  HIPCHK(launch_inject(s->scal, d_block, s->B, d_ref, ref_len, d_sched, n_sched, d_filler, s->t->d.vocab,
+                       (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_state_query(dflash_state* s, int32_t* h_out, void* stream) {
+  if (!s || !h_out) return fail(DFLASH_E_INVALID, "null argument");
+  int32_t h[SC_COUNT];
+  RC(read_scalars(s, h, (hipStream_t)stream));
+  h_out[0] = h[SC_N];
+  h_out[1] = h[SC_STEP];
+  h_out[2] = h[SC_STATUS];
+  h_out[3] = h[SC_P];
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_state_buffers(dflash_state* s, dflash_state_view* v) {
+  if (!s || !v) return fail(DFLASH_E_INVALID, "null argument");
+  v->tokens = s->tokens;
+  v->acc_log = s->acc_log;
+  v->acc_log_len = s->acc_log_len;
+  v->side = s->side;
+  v->ctx_feat = (char*)s->bu + (size_t)s->B * s->dr->d.hidden * elem_bytes(s->dr->gin);
+  v->gdn_state = s->gdn_S;
+  v->gdn_tape = s->gdn_tape;
+  v->tape_stride = gdn_rec(s->t);
+  v->n_gdn = s->t->n_gdn;
+  v->capacity = s->capacity;
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_prof_enable(dflash_state* s, int on) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  s->prof = on != 0;
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* launches, double* ms, double* bytes,
+                                int cap, int* h_n) {
+  if (!s || !h_n) return fail(DFLASH_E_INVALID, "null argument");
+  std::vector<const char*> nm;
+  std::vector<int64_t> cnt;
+  std::vector<double> tms, tb;
+  for (auto& r : s->prof_recs) {
+    HIPCHK(hipEventSynchronize(r.b));
+    float e = 0.f;
+    HIPCHK(hipEventElapsedTime(&e, r.a, r.b));
+    size_t i = 0;
+    while (i < nm.size() && std::strcmp(nm[i], r.name) != 0) ++i;
+    if (i == nm.size()) { nm.push_back(r.name); cnt.push_back(0); tms.push_back(0); tb.push_back(0); }
+    cnt[i] += 1;
+    tms[i] += e;
+    tb[i] += r.bytes;
+    s->ev_pool.push_back(r.a);
+    s->ev_pool.push_back(r.b);
+  }
+  s->prof_recs.clear();
+  *h_n = (int)nm.size();
+  for (int i = 0; i < (int)nm.size() && i < cap; ++i) {
+    if (names) names[i] = nm[i];
+    if (launches) launches[i] = cnt[i];
+    if (ms) ms[i] = tms[i];
+    if (bytes) bytes[i] = tb[i];
+  }
+  return DFLASH_OK;
+}

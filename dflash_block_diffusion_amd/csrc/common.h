@@ -1,0 +1,180 @@
+// Internal declarations shared by the HIP translation units of libdflash.
+// gfx950 only: wave64, MFMA f32_16x16x32_{f16,bf16}.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+// element types of activation buffers
+enum ElemType { T_F32 = 0, T_BF16 = 1, T_F16 = 2 };
+
+// weight formats (same values as DFLASH_FMT_*)
+enum WFmt { W_F32 = 0, W_BF16 = 1, W_W8 = 2, W_W4 = 3 };
+
+constexpr int PAGE = 64;         // tokens per KV page
+constexpr int ATTN_SPLIT = 256;  // keys per attention work-group (4 pages)
+constexpr int MAX_ROWS = 64;     // max GEMM rows (tokens) per call
+
+inline int elem_bytes(int t) { return t == T_F32 ? 4 : 2; }
+
+// K elements covered by one 1 KiB tile of 16 rows (each lane holds 16 bytes)
+inline __host__ __device__ constexpr int tile_k(int fmt) {
+  return fmt == W_BF16 ? 32 : (fmt == W_W8 ? 64 : 128);
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+
+// Load one activation element as fp32.
+__device__ __forceinline__ float load_act(const void* p, size_t i, int t) {
+  if (t == T_F32) return ((const float*)p)[i];
+  uint16_t h = ((const uint16_t*)p)[i];
+  if (t == T_BF16) return bf16_bits_to_f32(h);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Store an activation element.  bf16 is the materialisation format of all
+// 16-bit activations; T_F16 buffers hold the fp16 encoding of the same
+// bf16-rounded value (exact for |v| in [2^-17, 65504]), which is what the
+// fp16 MFMA of the quantised GEMMs consumes.  T_F32 stores v unrounded.
+__device__ __forceinline__ void store_act(void* p, size_t i, int t, float v) {
+  if (t == T_F32) { ((float*)p)[i] = v; return; }
+  uint32_t b = f32_to_bf16_bits(v);
+  if (t == T_BF16) { ((uint16_t*)p)[i] = (uint16_t)b; return; }
+  _Float16 h = (_Float16)bf16_bits_to_f32(b);
+  ((uint16_t*)p)[i] = __builtin_bit_cast(uint16_t, h);
+}
+// value the stored element will read back as
+__device__ __forceinline__ float act_round(int t, float v) { return t == T_F32 ? v : round_bf16(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ------------------------------------------------------------ GEMM interface
+struct GemmW {
+  int fmt, n, k, gate_up;
+  const void* w;      // packed
+  const void* s;      // packed scales (W8/W4) or null
+};
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+
+struct GemmCall {
+  const GemmW* W;
+  const void* x; int ldx;        // [rows][ldx] activations: F32 for W_F32, BF16 for W_BF16, F16 for W8/W4
+  int m;                         // valid rows (<= 64); kernels compute ceil(m/16)*16 rows
+  int epi;
+  void* out; int ldo; int otype; // STORE/SILU output, RESID residual stream (in place)
+  void* side; int ld_side; int side_type;   // RESID: optional copy of the new residual
+  // ARGMAX
+  float* logits; int ldl; int row0;         // optional fp32 logits of rows row0..m-1
+  int32_t* am_out;                          // argmax of rows row0..m-1 -> am_out[0..]
+};
+
+struct Workspace {
+  float* ws; size_t ws_floats;   // split-K partial tiles
+  int* counters; int n_counters; // split-K arrival counters (zero between launches)
+  float* am_val; int* am_idx; int am_cap;   // argmax partials [am_cap][64]
+  float* logits_tmp;             // F32 path: [64][V] logits scratch
+};
+
+struct ProfHook;  // per-launch timing (host side)
+
+hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
+                       double* bytes);
+hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, const void* src_scales,
+                       void* dst, void* dst_scales, hipStream_t s);
+void packed_bytes(int fmt, int n, int k, size_t* wb, size_t* sb);
+size_t gemm_ws_floats(int fmt, int n, int k, int m);
+int gemm_am_blocks(int fmt, int n, int m);
+
+// ------------------------------------------------------------ other kernels
+struct RopeCall {
+  const void* qkv; int ldqkv; int atype;   // GEMM output [rows][ldqkv] (act type)
+  int block_rows;                           // B: rows 0..B-1 at positions n+i
+  int ctx_rows;                             // drafter: rows B..B+ctx_rows-1 are context rows
+  const int* dev_n; const int* dev_p;       // committed length, pending context rows
+  const float* q_norm; const float* k_norm; float eps;
+  const float* cos_t; const float* sin_t;   // [capacity][d/2]
+  void* q_out;                              // [B][hq][d] act
+  void* kc; void* vc; const int* page_table; int capacity;
+  int hq, hkv, d;
+};
+hipError_t launch_qk_rope(const RopeCall& c, hipStream_t s);
+
+struct AttnCall {
+  const void* q; int atype;                  // [B][hq][d] act (bf16 or f32)
+  const void* kc; const void* vc; const int* page_table;
+  const int* dev_n; int block_rows; int causal;
+  int hq, hkv, d; int max_splits;
+  float* o_part; float* ml_part;              // [max_splits][B*hq][d], [max_splits][B*hq][2]
+  void* out; int otype; int ldo;              // [B][hq*d]
+};
+hipError_t launch_attention(const AttnCall& c, hipStream_t s);
+
+hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo,
+                          const float* gain, int rows, int h, float eps, hipStream_t s);
+hipError_t launch_embed(const void* table, int ttype, int h, int vocab, const int32_t* tokens,
+                        int mask_mode, int mask_token, int rows, void* out, int ldo,
+                        int32_t* status, hipStream_t s);
+hipError_t launch_argmax_final(const float* am_val, const int* am_idx, int nblocks, int row0,
+                               int rows, int32_t* out, hipStream_t s);
+hipError_t launch_argmax_rows(const float* logits, int ld, int vocab, int row0, int rows,
+                              int32_t* out, float* logits_copy, int ldc, hipStream_t s);
+hipError_t launch_accept(const int32_t* block, const int32_t* y, int B, int32_t* acc,
+                         int32_t* emit, int32_t* next_anchor, hipStream_t s);
+hipError_t launch_commit(int32_t* scal, const int32_t* d_acc, int host_count, const int32_t* emit,
+                         int32_t* tokens, int32_t* acc_log, int acc_log_len, int capacity, int B,
+                         hipStream_t s);
+hipError_t launch_set_scalars(int32_t* scal, int n, int p, int clear_status, hipStream_t s);
+hipError_t launch_copy_tokens(const int32_t* src, int32_t* dst, int count, hipStream_t s);
+hipError_t launch_rollback(int32_t* scal, int new_len, const int32_t* tokens, int32_t* block,
+                           hipStream_t s);
+hipError_t launch_inject(const int32_t* scal, int32_t* block, int B, const int32_t* ref, int ref_len,
+                         const int32_t* sched, int n_sched, const int32_t* filler, int vocab,
+                         hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, size_t count, int32_t v, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, size_t count, hipStream_t s);
+
+// GatedDeltaNet
+struct GdnCall {
+  const void* proj; int ldp; int atype;     // [B][gh*(2dk+dv)+2gh] GEMM output (act)
+  int rows; int gh, dk, dv;
+  const float* S;                            // committed state [gh][dv][dk]
+  float* tape;                               // [B][gh][dk+dv+2]
+  void* out; int otype; int ldo;             // o [B][gh*dv]
+};
+hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s);
+// replays cnt = a+1 (or host_count) tape tokens into every GDN layer's state;
+// skipped when the matching commit will be refused for capacity
+hipError_t launch_gdn_replay(float* S_all, const float* tape_all, int n_layers, int B, int gh, int dk,
+                             int dv, const int32_t* d_acc, int host_count, const int32_t* scal,
+                             int capacity, hipStream_t s);
+
+// scalar slots in the arena
+enum Scalar { SC_N = 0, SC_P = 1, SC_STEP = 2, SC_STATUS = 3, SC_SNAP_N = 4, SC_COUNT = 16 };
+
+}  // namespace dfl

@@ -1,0 +1,178 @@
+// GatedDeltaNet layers of the hybrid target: verify recurrence + tape, and
+// the tape replay that commits the accepted tokens.
+//
+// The dflash-mlx note ("Technical challenges") and the agentlens summary of
+// bstnxbt/dflash-mlx ("How it works") roll GatedDeltaNet state back by
+// replaying a tape recorded during verify instead of snapshotting it.  Per
+// head, with state S [dv][dk] (fp32):
+//   r = v - alpha * (S k);  u = beta * r;  S <- alpha * S + u k^T;  o = S q
+// q, k L2-normalised (q also scaled by 1/sqrt(dk)); alpha = sigmoid(-a) (the
+// same as exp(-softplus(a))), beta = sigmoid(b).
+//
+// Both kernels apply a token in the SAME pinned fp32 order, so the committed
+// state is bit-reproducible (and equals a from-scratch recompute over the
+// recorded tape):
+//   acc = halving-tree sum over j of (S[i][j] * k[j])   (each product rounded)
+//   p = alpha*acc; r = v[i] - p; u = beta*r; S[i][j] = (alpha*S[i][j]) + (u*k[j])
+// Thread layout: 4 consecutive lanes own value row i; lane r holds columns
+// j = r + 4m (m < dk/4).  The halving tree's strides dk/2 .. 4 stay inside a
+// lane; strides 2 and 1 are the xor-2 / xor-1 lane exchanges.
+// This file is compiled with -ffp-contract=off: no multiply-add fusion.
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace dfl {
+
+template <int DK>
+__device__ __forceinline__ float tree_dot(const float (&S)[DK / 4], const float* kv_lds, int r) {
+  float p[DK / 4];
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) p[m] = S[m] * kv_lds[r + 4 * m];
+#pragma unroll
+  for (int w = DK / 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int m = 0; m < w; ++m) p[m] = p[m] + p[m + w];
+  float x = p[0];
+  x = x + __shfl_xor(x, 2, 64);
+  x = x + __shfl_xor(x, 1, 64);
+  return x;
+}
+
+template <int DK>
+__device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_lds, float v_i, float alpha,
+                                            float beta, int r) {
+  const float acc = tree_dot<DK>(S, k_lds, r);
+  const float p = alpha * acc;
+  const float rr = v_i - p;
+  const float u = beta * rr;
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) {
+    const float a = alpha * S[m];
+    const float b = u * k_lds[r + 4 * m];
+    S[m] = a + b;
+  }
+}
+
+// Verify: one work-group per head, 4*dv threads; tokens applied in order to a
+// register copy of the committed state (which stays untouched).
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
+  constexpr int NT = 4 * DV;
+  constexpr int MAXT = 32;
+  constexpr int REC = DK + DV + 2;
+  __shared__ float kq[MAXT][2 * DK + DV + 2];   // k_hat, q_hat, v, alpha, beta per token
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = tid >> 2, r = tid & 3;
+  const int gh = c.gh;
+  const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
+  const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
+  const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
+
+  // per-token preprocessing: one wave per token
+  for (int t = wave; t < c.rows; t += NT / 64) {
+    const size_t rb = (size_t)t * c.ldp;
+    float qs = 0.f, ks = 0.f;
+    for (int e = lane; e < DK; e += 64) {
+      const float qv = load_act(c.proj, rb + qo + e, c.atype);
+      const float kv = load_act(c.proj, rb + ko + e, c.atype);
+      qs += qv * qv;
+      ks += kv * kv;
+    }
+    qs = wave_sum(qs);
+    ks = wave_sum(ks);
+    const float qn = 1.0f / sqrtf(qs + 1e-6f) * (1.0f / sqrtf((float)DK));
+    const float kn = 1.0f / sqrtf(ks + 1e-6f);
+    float* tape = c.tape + ((size_t)t * gh + h) * REC;
+    for (int e = lane; e < DK; e += 64) {
+      const float kh = load_act(c.proj, rb + ko + e, c.atype) * kn;
+      kq[t][e] = kh;
+      kq[t][DK + e] = load_act(c.proj, rb + qo + e, c.atype) * qn;
+      tape[e] = kh;
+    }
+    for (int e = lane; e < DV; e += 64) {
+      const float vv = load_act(c.proj, rb + vo + e, c.atype);
+      kq[t][2 * DK + e] = vv;
+      tape[DK + e] = vv;
+    }
+    if (lane == 0) {
+      const float av = load_act(c.proj, rb + ao, c.atype);
+      const float bv = load_act(c.proj, rb + bo, c.atype);
+      const float alpha = 1.0f / (1.0f + expf(av));
+      const float beta = 1.0f / (1.0f + expf(-bv));
+      kq[t][2 * DK + DV] = alpha;
+      kq[t][2 * DK + DV + 1] = beta;
+      tape[DK + DV] = alpha;
+      tape[DK + DV + 1] = beta;
+    }
+  }
+  __syncthreads();
+
+  float S[DK / 4];
+  const float* Sg = c.S + ((size_t)h * DV + i) * DK;
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+
+  for (int t = 0; t < c.rows; ++t) {
+    apply_token<DK>(S, kq[t], kq[t][2 * DK + i], kq[t][2 * DK + DV], kq[t][2 * DK + DV + 1], r);
+    const float o = tree_dot<DK>(S, kq[t] + DK, r);
+    if (r == 0) store_act(c.out, (size_t)t * c.ldo + (size_t)h * DV + i, c.otype, o);
+  }
+}
+
+hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
+  if (c.dk == 128 && c.dv == 128)
+    hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c);
+  else if (c.dk == 32 && c.dv == 32)
+    hipLaunchKernelGGL((gdn_verify_kernel<32, 32>), dim3(c.gh), dim3(128), 0, s, c);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Commit: every (layer, head) replays the first cnt tape records into its
+// committed state, in place.
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void gdn_replay_kernel(float* S_all, const float* tape_all, int B, int gh,
+                                                            const int32_t* d_acc, int host_count,
+                                                            const int32_t* scal, int capacity) {
+  constexpr int REC = DK + DV + 2;
+  __shared__ float rec[REC];
+  const int cnt = d_acc ? d_acc[0] + 1 : host_count;
+  if (scal[SC_N] + cnt + B > capacity) return;      // the commit will be refused
+  const int h = blockIdx.x, l = blockIdx.y;
+  const int tid = threadIdx.x, i = tid >> 2, r = tid & 3;
+  float* Sg = S_all + (((size_t)l * gh + h) * DV + i) * DK;
+  float S[DK / 4];
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+  const float* tape = tape_all + (size_t)l * B * gh * REC;
+  for (int t = 0; t < cnt; ++t) {
+    __syncthreads();
+    const float* tr = tape + ((size_t)t * gh + h) * REC;
+    for (int e = tid; e < REC; e += 4 * DV) rec[e] = tr[e];
+    __syncthreads();
+    apply_token<DK>(S, rec, rec[DK + i], rec[DK + DV], rec[DK + DV + 1], r);
+  }
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) Sg[r + 4 * m] = S[m];
+}
+
+hipError_t launch_gdn_replay(float* S_all, const float* tape_all, int n_layers, int B, int gh, int dk, int dv,
+                             const int32_t* d_acc, int host_count, const int32_t* scal, int capacity,
+                             hipStream_t s) {
+  if (n_layers <= 0) return hipSuccess;
+  dim3 grid(gh, n_layers);
+  if (dk == 128 && dv == 128)
+    hipLaunchKernelGGL((gdn_replay_kernel<128, 128>), grid, dim3(512), 0, s, S_all, tape_all, B, gh, d_acc,
+                       host_count, scal, capacity);
+  else if (dk == 32 && dv == 32)
+    hipLaunchKernelGGL((gdn_replay_kernel<32, 32>), grid, dim3(128), 0, s, S_all, tape_all, B, gh, d_acc,
+                       host_count, scal, capacity);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -25,6 +25,7 @@ They draw different numbers from the same seeds; each is deterministic.
 """
 from __future__ import annotations
 
+import os
 import zlib
 from dataclasses import dataclass
 from typing import Dict, List, Optional
@@ -61,31 +62,12 @@ def _to_bf16_values(x: np.ndarray) -> np.ndarray:
 
 
 def quantize_host(w: np.ndarray, fmt: int) -> Weight:
-    n, k = w.shape
-    w = w.astype(np.float32)
-    if fmt == FMT_W8A16:
-        amax = np.abs(w).max(axis=1)
-        s16 = (amax / np.float32(127.0)).astype(np.float16)
-        s = s16.astype(np.float32)[:, None]
-        with np.errstate(divide="ignore", invalid="ignore"):
-            q = np.where(s > 0, np.rint(w / np.where(s > 0, s, 1)), 0)
-        q = np.clip(q, -127, 127).astype(np.int8)
-        return Weight(fmt, n, k, codes=q, scales=s16)
-    if fmt == FMT_W4A16:
-        assert k % GROUP == 0
-        wg = w.reshape(n, k // GROUP, GROUP)
-        amax = np.abs(wg).max(axis=2)
-        s16 = (amax / np.float32(7.0)).astype(np.float16)
-        s = s16.astype(np.float32)[:, :, None]
-        with np.errstate(divide="ignore", invalid="ignore"):
-            q = np.where(s > 0, np.rint(wg / np.where(s > 0, s, 1)), 0)
-        q = np.clip(q, -8, 7).astype(np.int8).reshape(n, k)
-        return Weight(fmt, n, k, codes=q, scales=s16)
-    if fmt == FMT_BF16:
-        return Weight(fmt, n, k, values=_to_bf16_values(w))
-    if fmt == FMT_F32:
-        return Weight(fmt, n, k, values=w)
-    raise ValueError(fmt)
+    """Quantise a host fp32 matrix (torch CPU ops, several threads); returns
+    numpy arrays.  Same recipe as quantize_device."""
+    import torch
+    q = quantize_device(torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)), fmt)
+    cv = lambda t: None if t is None else t.numpy()
+    return Weight(fmt, q.n, q.k, values=cv(q.values), codes=cv(q.codes), scales=cv(q.scales))
 
 
 class HostSynth:
@@ -94,9 +76,29 @@ class HostSynth:
     def __init__(self, seed: int = 0):
         self.seed = seed
 
+    CHUNK = 1 << 20
+
     def normal(self, name: str, shape, std: float) -> np.ndarray:
-        rng = np.random.Generator(np.random.PCG64(subseed(self.seed, name)))
-        return rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+        """N(0, std^2) in fp32; drawn in fixed 1 Mi-element chunks, chunk c from
+        its own PCG64 stream (seed, name, c), so the result does not depend on
+        how many threads draw it."""
+        total = int(np.prod(shape))
+        out = np.empty(total, dtype=np.float32)
+        nch = (total + self.CHUNK - 1) // self.CHUNK
+
+        def draw(c):
+            lo, hi = c * self.CHUNK, min(total, (c + 1) * self.CHUNK)
+            rng = np.random.Generator(np.random.PCG64(subseed(self.seed, f"{name}#{c}")))
+            rng.standard_normal(out=out[lo:hi], dtype=np.float32)
+
+        if nch == 1:
+            draw(0)
+        else:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+                list(ex.map(draw, range(nch)))
+        out *= np.float32(std)
+        return out.reshape(shape)
 
     def weight(self, name: str, n: int, k: int, fmt: int, std: float = STD,
                row_std: Optional[np.ndarray] = None) -> Weight:

@@ -28,6 +28,6 @@ def tiny_hybrid_config():
     from dflash_block_diffusion_amd import configs as C
     base = C.tiny()
     kinds = (C.LAYER_GDN, C.LAYER_GDN, C.LAYER_GDN, C.LAYER_ATTN)
-    t = replace(base.target, n_layers=4, layer_kinds=kinds, gdn_heads=2, gdn_dk=32,
+    t = replace(base.target, n_layers=4, layer_kinds=kinds, gdn_heads=8, gdn_dk=32,
                 gdn_dv=32, fmt=C.FMT_F32)
     return replace(base, name="tiny-hybrid", target=t, sel_layers=(1, 3))

@@ -1,0 +1,155 @@
+"""GPU parity of the packed skinny GEMM (dflash_linear) against the oracle's
+float64 dequant-GEMM, on the same seeded weights and activations.
+
+Tolerance: fp32 accumulation of K products in a different order than the
+oracle; |err| <= 2e-6 * sum_k |x_k w_k| + 1e-7 per output (about 30x the
+unit roundoff: the sums below use K <= 20480).
+"""
+import numpy as np
+import pytest
+import torch
+from ctypes import c_size_t, byref
+
+from dflash_block_diffusion_amd import binding as bn
+from dflash_block_diffusion_amd import configs as C
+from dflash_block_diffusion_amd import synth
+from dflash_block_diffusion_amd.runtime import pack_weight, stream_handle
+from oracle.model import top2_margin
+from oracle.numerics import linear
+
+pytestmark = pytest.mark.gpu
+
+
+def x_values(rng, m, k, fmt):
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    if fmt != C.FMT_F32:
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    return x
+
+
+def x_device(x, fmt):
+    t = torch.from_numpy(x).cuda()
+    if fmt == C.FMT_F32:
+        return t.contiguous()
+    if fmt == C.FMT_BF16:
+        return t.to(torch.bfloat16).contiguous()
+    return t.to(torch.float16).contiguous()       # fp16 codes of bf16 values (exact here)
+
+
+def run_linear(w, x, fmt, epilogue=0, want_logits=True):
+    L = bn.lib()
+    m = x.shape[0]
+    dst, dsts = pack_weight(w)
+    ws_bytes = L.dflash_linear_workspace_bytes(fmt, w.n, w.k, m)
+    assert ws_bytes > 0
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    xd = x_device(x, fmt)
+    out = torch.full((m, w.n), float("nan"), device="cuda") if (epilogue == 0 or want_logits) else None
+    am = torch.full((m,), -1, dtype=torch.int32, device="cuda")
+    bn.check(L.dflash_linear(fmt, w.n, w.k, dst.data_ptr(), None if dsts is None else dsts.data_ptr(),
+                             xd.data_ptr(), m, epilogue, None if out is None else out.data_ptr(),
+                             am.data_ptr(), ws.data_ptr(), ws_bytes, stream_handle()))
+    torch.cuda.synchronize()
+    return (None if out is None else out.cpu().numpy().astype(np.float64)), am.cpu().numpy(), ws
+
+
+def bound(x, w, rows=None):
+    """2e-6 * sum_k |x_k w_k| + 1e-7, computed in row chunks."""
+    aw = synth.Weight(w.fmt, w.n, w.k,
+                      values=None if w.values is None else np.abs(w.values),
+                      codes=None if w.codes is None else np.abs(w.codes),
+                      scales=None if w.scales is None else np.abs(w.scales))
+    return linear(np.abs(x.astype(np.float64)), aw, rows=rows) * 2e-6 + 1e-7
+
+
+FMTS = [C.FMT_F32, C.FMT_BF16, C.FMT_W8A16, C.FMT_W4A16]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,m", [(48, 256, 16), (80, 384, 17), (1040, 512, 32), (272, 4096, 33),
+                                   (1024, 4096, 64), (64, 1024, 1)])
+def test_linear_parity_small(fmt, n, k, m):
+    # spans several row tiles, ragged row blocks (N/16 not a multiple of the
+    # tile group), ragged token blocks (m not a multiple of 16) and split-K
+    g = synth.HostSynth(100 + fmt)
+    w = g.weight(f"lin{n}x{k}", n, k, fmt)
+    x = x_values(np.random.default_rng(n + k + m), m, k, fmt)
+    y, _, ws = run_linear(w, x, fmt)
+    ref = linear(x, w)
+    assert np.all(np.isfinite(y))
+    assert np.all(np.abs(y - ref) <= bound(x, w))
+
+
+@pytest.mark.parametrize("fmt", [C.FMT_BF16, C.FMT_W4A16])
+def test_linear_repeat_is_bitwise_and_counters_reset(fmt):
+    # split-K partials are summed in a fixed order: two calls agree to the bit,
+    # and the arrival counters are zero again after every call
+    g = synth.HostSynth(7)
+    w = g.weight("rep", 512, 4096, fmt)
+    x = x_values(np.random.default_rng(3), 32, 4096, fmt)
+    y1, _, ws1 = run_linear(w, x, fmt)
+    y2, _, _ = run_linear(w, x, fmt)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_linear_argmax_small(fmt):
+    g = synth.HostSynth(9)
+    w = g.weight("am", 1024, 256, fmt)
+    x = x_values(np.random.default_rng(4), 16, 256, fmt)
+    logits, am, _ = run_linear(w, x, fmt, epilogue=1)
+    ref = linear(x, w)
+    assert np.all(np.abs(logits - ref) <= bound(x, w))
+    marg = top2_margin(ref)
+    ok = marg >= 1e-2
+    assert np.array_equal(am[ok], np.argmax(ref, axis=1)[ok])
+
+
+def test_linear_argmax_ties_take_lowest_index():
+    # identical rows 5 and 700 of W: equal logits, the lower index must win
+    w = synth.HostSynth(2).weight("tie", 1024, 256, C.FMT_BF16)
+    w.values[700] = w.values[5]
+    w.values[5] *= 0
+    w.values[5] += 0.5                         # make both rows the clear maximum
+    w.values[700] = w.values[5]
+    x = np.abs(x_values(np.random.default_rng(5), 4, 256, C.FMT_BF16))
+    _, am, _ = run_linear(w, x, C.FMT_BF16, epilogue=1, want_logits=False)
+    assert am.tolist() == [5, 5, 5, 5]
+
+
+# ------------------------------------------------------------ full sizes
+FULL = [  # (name, fmt, N, K, m): the weight-streaming GEMMs of the 8B / 27B block-32 step
+    ("8b_qkv_w4", C.FMT_W4A16, 6144, 4096, 32),
+    ("8b_gateup_w4", C.FMT_W4A16, 24576, 4096, 32),
+    ("8b_down_w4", C.FMT_W4A16, 4096, 12288, 32),
+    ("8b_drafter_qkv_w8", C.FMT_W8A16, 6144, 4096, 64),
+    ("8b_fc_w8", C.FMT_W8A16, 4096, 20480, 32),
+    ("27b_gateup_w4", C.FMT_W4A16, 34816, 5120, 32),
+    ("4b_gateup_bf16", C.FMT_BF16, 19456, 2560, 16),
+]
+
+
+@pytest.mark.parametrize("name,fmt,n,k,m", FULL)
+def test_linear_parity_full_size_sampled(name, fmt, n, k, m):
+    g = synth.HostSynth(11)
+    w = g.weight(name, n, k, fmt)
+    x = x_values(np.random.default_rng(12), m, k, fmt)
+    y, _, _ = run_linear(w, x, fmt)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(13)
+    for r0 in list(rng.integers(0, n // 16, 6) * 16) + [n - 16]:
+        ref = linear(x, w, rows=(int(r0), int(r0) + 16))
+        got = y[:, r0:r0 + 16]
+        assert np.all(np.abs(got - ref) <= bound(x, w, rows=(int(r0), int(r0) + 16))), (name, r0)
+
+
+def test_lm_head_argmax_full_size():
+    # 8B-class lm-head: 151936 x 4096 int4, every row's argmax (near ties excluded)
+    g = synth.HostSynth(21)
+    w = g.weight("lm_full", 151936, 4096, C.FMT_W4A16)
+    x = x_values(np.random.default_rng(22), 8, 4096, C.FMT_W4A16)
+    logits, am, _ = run_linear(w, x, C.FMT_W4A16, epilogue=1)
+    ref = linear(x, w)
+    assert np.max(np.abs(logits - ref) / (bound(x, w))) <= 1.0
+    ok = top2_margin(ref) >= 1e-2
+    assert np.array_equal(am[ok], np.argmax(ref, axis=1)[ok])

@@ -1,0 +1,202 @@
+"""GPU step parity: the whole draft+verify step through the C ABI against the
+oracle, in lockstep on the same seeded models and the same committed tokens.
+
+Per step both sides draft from the same committed context; both then verify
+the GPU's (possibly injected) block; the oracle commits the GPU's accepted
+count so the two stay on one token stream.  Compared:
+  * draft tokens d_1..d_{B-1}, verify argmax y_0..y_{B-1}, accepted count a:
+    bit-exact, except positions whose oracle top-2 logit margin is < 1e-2
+    (excluded and counted; a is compared when no excluded y lies in 0..a);
+  * logits: |err| <= 1e-4 (fp32 models) / 2e-2 (bf16 models);
+  * conditioning-layer hidden states: |err| <= 1e-4 (fp32) or
+    2e-2 + 2^-7 |ref| (bf16: the absolute bound plus one bf16 rounding step
+    of the value, since hidden values above 1 have bf16 steps above 2e-2).
+Depth-reduced configurations keep the real widths (hidden, heads, FFN,
+formats) with 2 target layers, 1 drafter layer and a 32768-token vocab;
+the full vocab lm-head is covered in test_gpu_linear.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from dflash_block_diffusion_amd import configs as C
+from dflash_block_diffusion_amd import synth
+from dflash_block_diffusion_amd.runtime import Pair
+from oracle.gdn import replay_pinned
+from oracle.model import argmax_first, top2_margin
+from oracle.spec import OraclePair, accept_length, greedy
+
+from conftest import tiny_hybrid_config
+
+pytestmark = pytest.mark.gpu
+TIE = 1e-2
+
+
+def tol_logits(cfg):
+    return 1e-4 if cfg.target.fmt == C.FMT_F32 else 2e-2
+
+
+def check_hidden(cfg, got, ref):
+    if cfg.drafter.fmt == C.FMT_F32:
+        assert np.max(np.abs(got - ref)) <= 1e-4
+    else:
+        assert np.all(np.abs(got - ref) <= 2e-2 + 2.0 ** -7 * np.abs(ref)), np.max(np.abs(got - ref))
+
+
+def reduced(name, layers=2, vocab=32768):
+    cfg = C.get(name).reduced(layers, 1)
+    return replace(cfg, target=replace(cfg.target, vocab=vocab), drafter=replace(cfg.drafter, vocab=vocab))
+
+
+def compare_tokens(got, ref, margin, stats):
+    ok = margin >= TIE
+    stats["excluded"] += int((~ok).sum())
+    stats["compared"] += int(ok.sum())
+    assert np.array_equal(np.asarray(got)[ok], np.asarray(ref)[ok]), (got, ref, margin)
+
+
+def lockstep(cfg, P, forced, gdn_exact=False):
+    """Run len(forced) injected steps on GPU and oracle in lockstep."""
+    B, V = cfg.block, cfg.target.vocab
+    ck = synth.make_pair(cfg)
+    prompt = synth.prompt(cfg, P)
+    max_ctx = P + (len(forced) + 4) * B + 64
+    pair = Pair(cfg, ck, max_ctx=max_ctx)
+    first = pair.prefill(prompt)
+    tapes = []
+    if gdn_exact:
+        assert P <= B, "the from-scratch GDN check needs a one-chunk prompt"
+        tp = pair.gdn_tape().cpu().numpy()
+        tapes.append(tp[:, :P])
+    pair.snapshot()
+    # reference stream for the injection: the GPU's own (lossless) output
+    while pair.query()["n"] < P + (len(forced) + 2) * B:
+        pair.step()
+    nref = pair.query()["n"]
+    ref = pair.tokens(nref + 1).clone()
+    pair.rollback(P)
+    if gdn_exact:
+        tapes = tapes[:1]
+    op = OraclePair(cfg, ck, cap=max_ctx + 2 * B)
+    op.prefill(prompt)
+    stats = {"excluded": 0, "compared": 0}
+    compare_tokens([first], [op.anchor], np.array([op.prefill_margin]), stats)
+    op.anchor = first
+    dlog = torch.empty(B - 1, V, device="cuda")
+    vlog = torch.empty(B, V, device="cuda")
+    sched = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fill = torch.as_tensor(synth.filler_tokens(cfg, len(forced)), device="cuda")
+    tl = tol_logits(cfg)
+    for s, k in enumerate(forced):
+        n = op.t.n
+        assert pair.query()["n"] == n
+        pair.draft(dlog)
+        raw = pair.block[1:B].cpu().numpy()
+        d_o, dl_o = op.d.draft(op.anchor, n)
+        compare_tokens(raw, d_o, top2_margin(dl_o), stats)
+        assert np.max(np.abs(dlog.cpu().numpy() - dl_o)) <= tl
+        sched.fill_(int(k))
+        pair.inject(ref, sched, fill[s:s + 1].contiguous())
+        block = pair.block[:B].cpu().numpy()
+        pair.verify(vlog)
+        y = pair.y[:B].cpu().numpy()
+        fwd = op.t.forward([int(t) for t in block])
+        vm = top2_margin(fwd["logits"])
+        compare_tokens(y, argmax_first(fwd["logits"]), vm, stats)
+        assert np.max(np.abs(vlog.cpu().numpy() - fwd["logits"])) <= tl
+        check_hidden(cfg, pair.side().cpu().numpy(), fwd["hidden"])
+        pair.accept()
+        pair.commit()
+        a = int(pair.acc.item())
+        a_o = accept_length(block[1:], argmax_first(fwd["logits"]))
+        if np.all(vm[:max(a, a_o) + 1] >= TIE):
+            assert a == a_o
+            assert a == k, "injected acceptance not realised"
+        emit = pair.emit[:a + 1].cpu().numpy()
+        assert emit.tolist() == [int(t) for t in block[1:a + 1]] + [int(y[a])]
+        if gdn_exact:
+            tapes.append(pair.gdn_tape().cpu().numpy()[:, :a + 1])
+        op.t.commit(fwd, a)
+        op.d.ctx_append(fwd["hidden"][:a + 1], n + np.arange(a + 1))
+        op.anchor = int(y[a])
+    q = pair.query()
+    assert q["n"] == op.t.n and q["status"] == 0
+    return pair, op, stats, tapes
+
+
+def test_tiny_generate_equals_oracle_greedy():
+    cfg = C.tiny()
+    ck = synth.make_pair(cfg)
+    pr = synth.prompt(cfg, 64)
+    ref = greedy(cfg, ck, pr, cfg.new_tokens, cap=256)
+    pair = Pair(cfg, ck, max_ctx=256)
+    out = pair.generate(pr, cfg.new_tokens)
+    assert out == ref
+
+
+def test_tiny_lockstep_injected():
+    cfg = C.tiny()
+    _, _, stats, _ = lockstep(cfg, 64, [0, 15, 7, 3, 15, 1, 0, 9])
+    assert stats["compared"] > 0
+
+
+def test_tiny_ragged_prompt():
+    cfg = C.tiny()
+    _, _, stats, _ = lockstep(cfg, 37, [2, 0, 15])
+
+
+@pytest.mark.parametrize("name,P", [("4b", 300), ("8b", 300), ("27b", 200)])
+def test_reduced_lockstep(name, P):
+    cfg = reduced(name)
+    forced = [0, cfg.block - 1, 5, 11]
+    _, _, stats, _ = lockstep(cfg, P, forced)
+    print(name, stats)
+    assert stats["compared"] >= 3 * len(forced) * cfg.block // 2
+
+
+def test_rollback_replays_identically():
+    cfg = reduced("8b")
+    ck = synth.make_pair(cfg)
+    prompt = synth.prompt(cfg, 100)
+    pair = Pair(cfg, ck, max_ctx=512)
+    pair.prefill(prompt)
+    for _ in range(5):
+        pair.step()
+    n1 = pair.query()["n"]
+    toks1 = pair.tokens(n1 + 1).cpu().numpy().copy()
+    pair.rollback(100)
+    for _ in range(5):
+        pair.step()
+    assert pair.query()["n"] == n1
+    assert np.array_equal(pair.tokens(n1 + 1).cpu().numpy(), toks1)
+
+
+def test_hybrid_gdn_replay_bitexact_vs_scratch_recompute():
+    cfg = reduced("hybrid", layers=4)
+    forced = [0, 15, 3, 7, 15, 1]
+    pair, op, stats, tapes = lockstep(cfg, 16, forced, gdn_exact=True)
+    S_gpu = pair.gdn_state().cpu().numpy()
+    cat = np.concatenate(tapes, axis=1)                   # [n_gdn, T, gh, rec]
+    dk = cfg.target.gdn_dk
+    dv = cfg.target.gdn_dv
+    for l in range(S_gpu.shape[0]):
+        t = cat[l]
+        S = replay_pinned(np.zeros(S_gpu.shape[1:], np.float32), t[:, :, :dk], t[:, :, dk:dk + dv],
+                          t[:, :, dk + dv], t[:, :, dk + dv + 1])
+        assert np.array_equal(S, S_gpu[l]), f"GDN layer {l} state differs from the scratch recompute"
+    # and against the oracle's own float64 state: tolerance
+    gdn_layers = [l for l, k in enumerate(cfg.target.kinds()) if k == C.LAYER_GDN]
+    for i, l in enumerate(gdn_layers):
+        assert np.max(np.abs(S_gpu[i] - op.t.S[l])) <= 2e-2
+
+
+def test_hybrid_long_prompt_and_snapshot_rollback():
+    cfg = reduced("hybrid", layers=4)
+    lockstep(cfg, 100, [3, 15, 0])
+
+
+def test_tiny_hybrid_lockstep():
+    cfg = tiny_hybrid_config()
+    lockstep(cfg, 16, [0, 15, 4, 9], gdn_exact=True)
