@@ -53,8 +53,8 @@ SIGNATURES = {
     "dflash_packed_bytes": (c_int, [c_int, c_int, c_int, POINTER(c_size_t), POINTER(c_size_t)]),
     "dflash_pack_weight": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_linear_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
-    "dflash_linear": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p,
-                              c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dflash_linear": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dflash_model_create": (c_int, [POINTER(ModelDesc), POINTER(c_void_p)]),
     "dflash_model_destroy": (None, [c_void_p]),
     "dflash_drafter_bind": (c_int, [c_void_p, c_void_p]),

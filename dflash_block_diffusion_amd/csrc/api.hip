@@ -105,12 +105,13 @@ extern "C" size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m) {
   return linear_ws_layout(fmt, n, k, m).total;
 }
 
-extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* sc, const void* x, int m,
+extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx, int m,
                              int epilogue, float* out, int32_t* am, void* ws, size_t ws_bytes, void* stream) {
   if (!fmt_ok(fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
   int rc = check_gemm_shape(fmt, n, k, 0);
   if (rc) return rc;
   if (m < 1 || m > MAX_ROWS) return fail(DFLASH_E_SHAPE, "m must be in [1, 64]");
+  if (fmt == DFLASH_FMT_F32 && ldx < k) return fail(DFLASH_E_SHAPE, "ldx must be >= k");
   if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
   if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");
   if (epilogue == 1 && !am) return fail(DFLASH_E_INVALID, "epilogue 1 needs d_argmax");
@@ -126,7 +127,7 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   W.logits_tmp = (float*)(b + L.lg_off);
   GemmW g = mkw(fmt, n, k, 0, w, sc);
   GemmCall c;
-  c.W = &g; c.x = x; c.ldx = k; c.m = m;
+  c.W = &g; c.x = x; c.ldx = ldx; c.m = m;
   c.epi = epilogue == 0 ? EPI_STORE : EPI_ARGMAX;
   c.out = out; c.ldo = n; c.otype = T_F32;
   c.side = nullptr; c.ld_side = 0; c.side_type = 0;
@@ -453,10 +454,11 @@ static hipEvent_t take_event(dflash_state* s) {
 
 static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, void* out, int ldo,
                 int otype, hipStream_t st, void* side = nullptr, int ld_side = 0, int side_type = 0,
-                float* logits = nullptr, int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
+                float* logits = nullptr, int ldl = 0, int row0 = 0, int32_t* am_out = nullptr,
+                int side_col0 = 0) {
   GemmCall c;
   c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi; c.out = out; c.ldo = ldo; c.otype = otype;
-  c.side = side; c.ld_side = ld_side; c.side_type = side_type;
+  c.side = side; c.ld_side = ld_side; c.side_type = side_type; c.side_col0 = side_col0;
   c.logits = logits; c.ldl = ldl; c.row0 = row0; c.am_out = am_out;
   const char* name = nullptr;
   double bytes = 0;
@@ -495,11 +497,12 @@ static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer
 }
 
 static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, hipStream_t st, void* side, int ld_side,
-               int side_type) {
+               int side_type, int side_col0) {
   const int H = m->d.hidden, F = m->d.ffn, B = s->B;
   HIPCHK(launch_rmsnorm(s->x, m->act, H, s->bu, m->gin, H, L.post_norm, B, H, m->d.eps, st));
   RC(gemm(s, L.gu, s->bu, H, B, EPI_SILU, s->bf, F, m->gin, st));
-  RC(gemm(s, L.down, s->bf, F, B, EPI_RESID, s->x, H, m->act, st, side, ld_side, side_type));
+  RC(gemm(s, L.down, s->bf, F, B, EPI_RESID, s->x, H, m->act, st, side, ld_side, side_type, nullptr, 0, 0,
+          nullptr, side_col0));
   return DFLASH_OK;
 }
 
@@ -514,7 +517,7 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
                       s->scal + SC_STATUS, st));
   for (int l = 0; l < d->d.n_layers; ++l) {
     RC(attn_layer(s, d, l, d->layers[l], true, st));
-    RC(ffn(s, d, d->layers[l], st, nullptr, 0, 0));
+    RC(ffn(s, d, d->layers[l], st, nullptr, 0, 0, 0));
   }
   HIPCHK(launch_rmsnorm(s->x, d->act, H, s->bu, t->gin, H, d->d.final_norm, B, H, d->d.eps, st));
   RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 1, block + 1));
@@ -544,11 +547,13 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       ++g;
     }
     void* side = nullptr;
+    int col0 = 0;
     if (sel < d->d.n_sel && d->d.sel_layers[sel] == l) {
-      side = (char*)s->side + (size_t)sel * H * elem_bytes(d->gin);
+      side = s->side;                  // conditioning rows: columns sel*H.. of the fc input
+      col0 = sel * H;
       ++sel;
     }
-    RC(ffn(s, t, L, st, side, d->d.n_sel * H, d->gin));
+    RC(ffn(s, t, L, st, side, d->d.n_sel * H, d->gin, col0));
   }
   HIPCHK(launch_rmsnorm(s->x, t->act, H, s->bu, t->gin, H, t->d.final_norm, B, H, t->d.eps, st));
   RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 0, argmax));

@@ -307,9 +307,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
     if (e1 < d) acc1 += w * op[e1];
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const size_t ob = (size_t)tok * ldo + (size_t)qh * d;
-  if (e0 < d) store_act(out, ob + e0, otype, acc0 * inv);
-  if (e1 < d) store_act(out, ob + e1, otype, acc1 * inv);
+  // 16-bit outputs feed the O projection: tiled layout with K = hq*d
+  const int fmK = otype == T_F32 ? 0 : hq * d;
+  if (e0 < d) store_act(out, act_index(tok, qh * d + e0, ldo, fmK), otype, acc0 * inv);
+  if (e1 < d) store_act(out, act_index(tok, qh * d + e1, ldo, fmK), otype, acc1 * inv);
 }
 
 hipError_t launch_attention(const AttnCall& c, hipStream_t s) {

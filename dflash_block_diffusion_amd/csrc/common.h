@@ -62,6 +62,20 @@ __device__ __forceinline__ void store_act(void* p, size_t i, int t, float v) {
 // value the stored element will read back as
 __device__ __forceinline__ float act_round(int t, float v) { return t == T_F32 ? v : round_bf16(v); }
 
+// Fragment-major ("tiled") layout of 16-bit GEMM inputs X[t][k] with K
+// columns: 16-token blocks are outermost and contiguous; inside a block,
+// every 32-column step is one 1 KiB MFMA operand fragment in lane order
+// (lane = t%16 + 16*((k%32)/8), 8 consecutive k per lane).  A wave then
+// loads each operand fragment with one contiguous 1 KiB read.
+__host__ __device__ __forceinline__ size_t fm_index(int t, int k, int K) {
+  return ((size_t)(t >> 4) * (K >> 5) + (k >> 5)) * 512 + (size_t)(((t & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7));
+}
+// index of element (t, k) of a GEMM input: tiled when fmK > 0 (fmK = K),
+// row-major with leading dimension ld otherwise (fp32 inputs)
+__device__ __forceinline__ size_t act_index(int t, int k, int ld, int fmK) {
+  return fmK ? fm_index(t, k, fmK) : (size_t)t * ld + k;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -84,11 +98,13 @@ enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
 
 struct GemmCall {
   const GemmW* W;
-  const void* x; int ldx;        // [rows][ldx] activations: F32 for W_F32, BF16 for W_BF16, F16 for W8/W4
+  const void* x; int ldx;        // activations: F32 row-major [rows][ldx] for W_F32; tiled
+                                 // (fm_index with K) BF16 for W_BF16, F16 for W8/W4
   int m;                         // valid rows (<= 64); kernels compute ceil(m/16)*16 rows
   int epi;
   void* out; int ldo; int otype; // STORE/SILU output, RESID residual stream (in place)
   void* side; int ld_side; int side_type;   // RESID: optional copy of the new residual
+  int side_col0;                            // at columns side_col0.. of the side buffer (K = ld_side)
   // ARGMAX
   float* logits; int ldl; int row0;         // optional fp32 logits of rows row0..m-1
   int32_t* am_out;                          // argmax of rows row0..m-1 -> am_out[0..]
@@ -135,8 +151,9 @@ struct AttnCall {
 };
 hipError_t launch_attention(const AttnCall& c, hipStream_t s);
 
+// out: tiled with K = h when otype is 16-bit and tiled != 0, else row-major [rows][ldo]
 hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo,
-                          const float* gain, int rows, int h, float eps, hipStream_t s);
+                          const float* gain, int rows, int h, float eps, hipStream_t s, int tiled = 1);
 hipError_t launch_embed(const void* table, int ttype, int h, int vocab, const int32_t* tokens,
                         int mask_mode, int mask_token, int rows, void* out, int ldo,
                         int32_t* status, hipStream_t s);

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   for (int t = 0; t < c.rows; ++t) {
     apply_token<DK>(S, kq[t], kq[t][2 * DK + i], kq[t][2 * DK + DV], kq[t][2 * DK + DV + 1], r);
     const float o = tree_dot<DK>(S, kq[t] + DK, r);
-    if (r == 0) store_act(c.out, (size_t)t * c.ldo + (size_t)h * DV + i, c.otype, o);
+    if (r == 0)
+      store_act(c.out, act_index(t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
   }
 }
 

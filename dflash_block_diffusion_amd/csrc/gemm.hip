@@ -18,13 +18,21 @@
 // [16l, 16l+16), which hold row (l % 16) and, for each 32-wide MFMA sub-step
 // ss of the tile, the 8 columns KT*t + 32*ss + 8*(l/16) + e, e = 0..7 --
 // exactly the A-operand of v_mfma_f32_16x16x32 for that lane.  So every wave
-// load is one fully coalesced 1 KiB read and needs no shuffling.
+// load is one fully coalesced 1 KiB read and needs no shuffling.  The
+// activations come in the matching tiled layout (fm_index in common.h), so
+// their operand fragments are contiguous 1 KiB reads as well: with row-major
+// activations each fragment is a 16-row gather, and those gathers saturated
+// the texture addresser long before HBM.
 //
-// Work split: a work-group (4 waves) owns R row-tiles (16R rows) and one of
-// `splits` K ranges; its 4 waves split that range again.  The 4 wave partials
-// are summed in LDS in a fixed order; with splits > 1 the last-arriving
-// work-group of a row block sums the split partials in a fixed order (so the
-// result is bit-reproducible) and runs the epilogue.
+// Work split: a work-group (4 waves) owns R row tiles (16R rows) over the full
+// K; wave w takes the w-th quarter of the K tiles and prefetches the next tile
+// while it multiplies the current one.  The 4 wave partials are summed in LDS
+// in a fixed order, so results are bit-reproducible.  R is chosen per shape
+// so that even the narrow projections (N = 4096) launch one work-group per
+// CU.  (No cross-work-group split-K: a release/acquire handoff between
+// work-groups writes back the L2 and costs far more than it saves here.)
+#include <cstdio>
+
 #include "common.h"
 
 namespace dfl {
@@ -143,66 +151,77 @@ __device__ __forceinline__ uint32_t u32(half2v h) { return __builtin_bit_cast(ui
 
 // 8 int4 codes (one dword, offset binary, nibble slots as packed) -> 8 halves
 // 0x6400 | u is the fp16 value 1024 + u; (0x6400 | 16u) scaled by 1/16 is 64 + u.
-__device__ __forceinline__ half8 deq_w4(uint32_t w) {
+// mlo = 0x000F000F, mhi = 0x00F000F0, magic = 0x64006400 (register operands).
+__device__ __forceinline__ half8 deq_w4(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic) {
   const half2v c0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2v s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2v c1 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t w2 = w >> 8;
-  half2v a = h2((w & 0x000F000Fu) | 0x64006400u) + c0;
-  half2v b = h2((w & 0x00F000F0u) | 0x64006400u) * s16 + c1;
-  half2v c = h2((w2 & 0x000F000Fu) | 0x64006400u) + c0;
-  half2v d = h2((w2 & 0x00F000F0u) | 0x64006400u) * s16 + c1;
+  half2v a = h2((w & mlo) | magic) + c0;
+  half2v b = h2((w & mhi) | magic) * s16 + c1;
+  half2v c = h2((w2 & mlo) | magic) + c0;
+  half2v d = h2((w2 & mhi) | magic) * s16 + c1;
   half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   return r;
 }
 
-// 8 int8 codes (two dwords, bytes in column order, offset binary) -> 8 halves
-__device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi) {
+// 8 int8 codes (two dwords, bytes in column order, offset binary) -> 8 halves:
+// byte pairs are spread to the low bytes of two fp16 lanes over the magic 0x64.
+__device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi, uint32_t magic) {
   const half2v c = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  half2v a = h2((lo & 0xFFu) | ((lo & 0xFF00u) << 8) | 0x64006400u) + c;
-  half2v b = h2(((lo >> 16) & 0xFFu) | ((lo >> 8) & 0xFF0000u) | 0x64006400u) + c;
-  half2v d = h2((hi & 0xFFu) | ((hi & 0xFF00u) << 8) | 0x64006400u) + c;
-  half2v e = h2(((hi >> 16) & 0xFFu) | ((hi >> 8) & 0xFF0000u) | 0x64006400u) + c;
+  half2v a = h2(__builtin_amdgcn_perm(magic, lo, 0x05010500u)) + c;
+  half2v b = h2(__builtin_amdgcn_perm(magic, lo, 0x05030502u)) + c;
+  half2v d = h2(__builtin_amdgcn_perm(magic, hi, 0x05010500u)) + c;
+  half2v e = h2(__builtin_amdgcn_perm(magic, hi, 0x05030502u)) + c;
   half8 r = {a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
   return r;
-}
-
-__device__ __forceinline__ float half_at(const uint4& v, int i) {
-  const uint32_t d = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
-  const uint16_t h = (i & 1) ? (uint16_t)(d >> 16) : (uint16_t)(d & 0xffffu);
-  return (float)__builtin_bit_cast(_Float16, h);
 }
 
 // ------------------------------------------------------------------ kernel
 struct GemmArgs {
   const uint8_t* w; const uint16_t* s; const uint16_t* x; int ldx;
-  int n, k, ktiles, ntile16, nrb, splits, m;
+  int n, k, ktiles, ntile16, m;
   int epi; void* out; int ldo; int otype;
-  void* side; int ld_side; int side_type;
+  void* side; int ld_side; int side_type; int side_col0;
   float* logits; int ldl; int row0;
   float* am_val; int* am_idx;
-  float* ws; int* ctr;
+  // dequant bit masks, passed as arguments so that they live in registers
+  // (gfx9 VOP3 encodings take no literal constants)
+  uint32_t mlo, mhi, magic;
 };
 
 template <int FMT, int R, int MB>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
+struct Frag {          // one K tile's operands for one wave
+  uint4 w[R];
+  uint4 s[R];
+  uint4 x[MB][tile_k(FMT) / 32];
+};
+
+// Work-group = 4 waves on R row tiles (16R weight rows) over the full K; wave
+// w takes the w-th quarter of the K tiles; the quarters are summed in LDS in a
+// fixed order (bit-reproducible).  Loads of the next K tile are issued before
+// the current one is consumed (register double buffering).
+template <int FMT, int R, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_mfma_kernel(GemmArgs a) {
   constexpr int KT = tile_k(FMT);
   constexpr int SS = KT / 32;
+  // ring depth (K tiles in flight per wave): as many stages as fit ~128 VGPRs
+  constexpr int STAGE = 4 * R * (FMT == W_W4 ? 2 : 1) + 4 * MB * SS;
+  constexpr int U = 4 * STAGE <= 128 ? 4 : (3 * STAGE <= 128 ? 3 : 2);
   constexpr int ROWS = 16 * R;          // weight rows of this work-group
   constexpr int TOK = 16 * MB;          // token rows computed
   constexpr int TS = ROWS * TOK;        // tile floats
   __shared__ float red[3][R * MB * 4][64];
   __shared__ float tileT[TOK][ROWS + 1];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int rb = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
-  const int rt0 = rb * R;
-  const int nsl = a.splits * 4, q = sp * 4 + wave;
-  const int t0 = (int)((long long)a.ktiles * q / nsl);
-  const int t1 = (int)((long long)a.ktiles * (q + 1) / nsl);
+  const int rt0 = blockIdx.x * R;
+  const int t0 = (int)((long long)a.ktiles * wave / 4);
+  const int t1 = (int)((long long)a.ktiles * (wave + 1) / 4);
+  const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
 
   floatx4 acc[R][MB];
 #pragma unroll
@@ -210,45 +229,48 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[r][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // activations are tiled (fm_index): the fragment of token block mb and
+  // 32-column step kb is the contiguous 1 KiB at ((mb * K/32) + kb) * 512
   const uint16_t* xrow[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    // rows past m are recomputed from row m-1 (never read past the caller's [m][k])
-    const int row = min(mb * 16 + lr, a.m - 1);
-    xrow[mb] = a.x + (size_t)row * a.ldx + 8 * g;
+  for (int mb = 0; mb < MB; ++mb) xrow[mb] = a.x + (size_t)mb * (a.k >> 5) * 512 + lane * 8;
+  const uint8_t* wbase[R];
+  const uint16_t* sbase[R];
+  bool live[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rt0 + r;
+    live[r] = rt < a.ntile16;
+    const int rtc = live[r] ? rt : a.ntile16 - 1;     // clamped: dead tiles re-read a valid one
+    wbase[r] = a.w + (size_t)rtc * a.ktiles * 1024 + lane * 16;
+    sbase[r] = (FMT == W_W4) ? a.s + (size_t)rtc * a.ktiles * 32 + g * 8 : nullptr;
   }
 
-  for (int t = t0; t < t1; ++t) {
-    uint4 wr[R];
-    uint4 sc[R];
+  auto load = [&](int t, Frag<FMT, R, MB>& f) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int rt = rt0 + r;
-      if (rt < a.ntile16) {
-        wr[r] = *(const uint4*)(a.w + ((size_t)rt * a.ktiles + t) * 1024 + lane * 16);
-        if (FMT == W_W4) sc[r] = *(const uint4*)(a.s + ((size_t)rt * a.ktiles + t) * 32 + g * 8);
-      } else {
-        wr[r] = uint4{0, 0, 0, 0};
-        sc[r] = uint4{0, 0, 0, 0};
-      }
+      f.w[r] = *(const uint4*)(wbase[r] + (size_t)t * 1024);
+      if (FMT == W_W4) f.s[r] = *(const uint4*)(sbase[r] + (size_t)t * 32);
     }
-    uint4 xf[MB][SS];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int ss = 0; ss < SS; ++ss) xf[mb][ss] = *(const uint4*)(xrow[mb] + (size_t)t * KT + 32 * ss);
+      for (int ss = 0; ss < SS; ++ss) f.x[mb][ss] = *(const uint4*)(xrow[mb] + ((size_t)t * SS + ss) * 512);
+  };
 
+  auto compute = [&](const Frag<FMT, R, MB>& f) {
+    const uint4 (&xf)[MB][SS] = f.x;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (FMT == W_BF16) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, wr[r]);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, f.w[r]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               av, __builtin_bit_cast(bf16x8, xf[mb][0]), acc[r][mb], 0, 0, 0);
       } else if (FMT == W_W8) {
-        const half8 a0 = deq_w8(wr[r].x, wr[r].y);
-        const half8 a1 = deq_w8(wr[r].z, wr[r].w);
+        const half8 a0 = deq_w8(f.w[r].x, f.w[r].y, magic);
+        const half8 a1 = deq_w8(f.w[r].z, f.w[r].w, magic);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -257,26 +279,57 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
               a1, __builtin_bit_cast(half8, xf[mb][1]), acc[r][mb], 0, 0, 0);
         }
       } else {  // W4: two 64-wide groups per tile, sub-steps (0,1) and (2,3)
-        const uint32_t wd[4] = {wr[r].x, wr[r].y, wr[r].z, wr[r].w};
+        const uint32_t wd[4] = {f.w[r].x, f.w[r].y, f.w[r].z, f.w[r].w};
+        const uint32_t sd[4] = {f.s[r].x, f.s[r].y, f.s[r].z, f.s[r].w};
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
-          const half8 a0 = deq_w4(wd[2 * gg]);
-          const half8 a1 = deq_w4(wd[2 * gg + 1]);
-          float s4[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) s4[v] = half_at(sc[r], gg * 4 + v);
+          const half8 a0 = deq_w4(wd[2 * gg], mlo, mhi, magic);
+          const half8 a1 = deq_w4(wd[2 * gg + 1], mlo, mhi, magic);
+          const half2v s01 = __builtin_bit_cast(half2v, sd[2 * gg]);
+          const half2v s23 = __builtin_bit_cast(half2v, sd[2 * gg + 1]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 a0, __builtin_bit_cast(half8, xf[mb][2 * gg]), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 a1, __builtin_bit_cast(half8, xf[mb][2 * gg + 1]), tmp, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[r][mb][v] += s4[v] * tmp[v];
+            acc[r][mb][0] += (float)s01[0] * tmp[0];
+            acc[r][mb][1] += (float)s01[1] * tmp[1];
+            acc[r][mb][2] += (float)s23[0] * tmp[2];
+            acc[r][mb][3] += (float)s23[1] * tmp[3];
           }
         }
       }
     }
+  };
+
+  // Operands stream through a ring of U register stages: each stage holds one
+  // K tile's weights (HBM), scales and activations (L2), so U tiles of loads
+  // are in flight per wave while the oldest is multiplied.  The main loop is
+  // branch-free (every load unconditional, the last round re-reads a clamped
+  // valid tile) so the compiler can wait for one stage at a time instead of
+  // draining all outstanding loads; leftover tiles run in a short tail loop.
+  const int full = (t1 - t0) / U;
+  if (full > 0) {
+    Frag<FMT, R, MB> ring[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(t0 + u, ring[u]);
+    // keep the scheduler from sinking loads next to their uses (it would
+    // trade the in-flight depth for registers)
+    __builtin_amdgcn_sched_barrier(0);
+    for (int rd = 0; rd < full; ++rd) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        compute(ring[u]);
+        load(min(t0 + (rd + 1) * U + u, t1 - 1), ring[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  for (int t = t0 + full * U; t < t1; ++t) {
+    Frag<FMT, R, MB> f;
+    load(t, f);
+    compute(f);
   }
 
   // ---- fixed-order reduction of the 4 wave partials
@@ -297,39 +350,15 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int j = (r * MB + mb) * 4 + v;
-          float s = acc[r][mb][v] + red[0][j][lane];
-          s = s + red[1][j][lane];
-          s = s + red[2][j][lane];
+          float sum = acc[r][mb][v] + red[0][j][lane];
+          sum = sum + red[1][j][lane];
+          sum = sum + red[2][j][lane];
           // D layout of 16x16 MFMA: lane holds column (token) lane%16, rows 4*(lane/16)+v
-          tileT[mb * 16 + lr][r * 16 + 4 * g + v] = s;
+          tileT[mb * 16 + lr][r * 16 + 4 * g + v] = sum;
         }
   }
   __syncthreads();
-
-  // ---- split-K: the last work-group of this row block sums all partials
-  if (a.splits > 1) {
-    float* mine = a.ws + ((size_t)rb * a.splits + sp) * TS;
-    for (int e = tid; e < TS; e += 256) mine[e] = tileT[e / ROWS][e % ROWS];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&a.ctr[rb], 1);
-      s_last = (prev == a.splits - 1);
-      if (s_last) a.ctr[rb] = 0;      // every split has arrived: reset for the next launch
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* base = a.ws + (size_t)rb * a.splits * TS;
-    for (int e = tid; e < TS; e += 256) {
-      float v = 0.f;
-      for (int s2 = 0; s2 < a.splits; ++s2)
-        v += (s2 == sp) ? tileT[e / ROWS][e % ROWS] : __builtin_nontemporal_load(base + (size_t)s2 * TS + e);
-      // written back after every thread has read its own elements (same e only)
-      tileT[e / ROWS][e % ROWS] = v;
-    }
-    __syncthreads();
-  }
+  (void)live;
 
   // ---- epilogues
   const int n0 = rt0 * 16;
@@ -349,7 +378,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
         const float xo = load_act(a.out, o, a.otype);
         const float nv = act_round(a.otype, xo + act_round(a.otype, y));
         store_act(a.out, o, a.otype, nv);
-        if (a.side) store_act(a.side, (size_t)t * a.ld_side + n, a.side_type, nv);
+        if (a.side)
+          store_act(a.side, act_index(t, a.side_col0 + n, a.ld_side, a.side_type == T_F32 ? 0 : a.ld_side),
+                    a.side_type, nv);
       }
     }
   } else if (a.epi == EPI_SILU) {
@@ -364,7 +395,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
       const float gv = act_round(rnd, tileT[t][gl] * scale_of(n0 + gl));
       const float uv = act_round(rnd, tileT[t][ul] * scale_of(n0 + ul));
       const float sv = gv / (1.0f + expf(-gv));
-      store_act(a.out, (size_t)t * a.ldo + n_out, a.otype, sv * uv);
+      store_act(a.out, act_index(t, n_out, a.ldo, a.otype == T_F32 ? 0 : a.n / 2), a.otype, sv * uv);
     }
   } else {  // EPI_ARGMAX
     if (a.logits) {
@@ -384,8 +415,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
         const float y = tileT[t][nl] * scale_of(n);
         if (y > best) { best = y; bi = n; }   // ascending n: first (lowest) index kept on ties
       }
-      a.am_val[(size_t)rb * 64 + t] = best;
-      a.am_idx[(size_t)rb * 64 + t] = bi;
+      a.am_val[(size_t)blockIdx.x * 64 + t] = best;
+      a.am_idx[(size_t)blockIdx.x * 64 + t] = bi;
     }
   }
 }
@@ -396,7 +427,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ W, const float* __restrict__ X,
                                                        int ldx, int n, int k, int m, int epi, void* out,
                                                        int ldo, void* side, int ld_side, int side_type,
-                                                       float* logits, int ldl) {
+                                                       int side_col0, float* logits, int ldl) {
   const int col = blockIdx.x * blockDim.x + threadIdx.x;
   const int ncols = epi == EPI_SILU ? n / 2 : n;
   if (col >= ncols) return;
@@ -426,7 +457,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       float* o = (float*)out + (size_t)t * ldo + col;
       const float nv = *o + acc[t];
       *o = nv;
-      if (side) store_act(side, (size_t)t * ld_side + col, side_type, nv);
+      if (side)
+        store_act(side, act_index(t, side_col0 + col, ld_side, side_type == T_F32 ? 0 : ld_side), side_type, nv);
     } else if (epi == EPI_SILU) {
       const float gv = acc[t];
       ((float*)out)[(size_t)t * ldo + col] = gv / (1.0f + expf(-gv)) * acc2[t];
@@ -511,52 +543,72 @@ hipError_t launch_argmax_rows(const float* logits, int ld, int vocab, int row0, 
 }
 
 // ------------------------------------------------------------------ planning
-struct Plan { int R, MB, nrb, splits, ktiles, ntile16; };
+// R (row tiles per work-group) is the largest that still gives every CU at
+// least one work-group, bounded by the register budget R * MB <= 8 (4 for
+// int4, whose dequantisation needs the most registers);
+// gate/up launches need R even (tile pairs).
+struct Plan { int R, MB, nwg, ktiles, ntile16; };
 
-static Plan make_plan(int fmt, int n, int k, int m) {
+#ifndef DFL_GEMM_MIN_WGS
+#define DFL_GEMM_MIN_WGS 256
+#endif
+
+static Plan make_plan(int fmt, int n, int k, int m, int gate_up) {
   Plan p;
   p.MB = (m + 15) / 16;
-  p.R = p.MB <= 2 ? 4 : 2;
   p.ntile16 = n / 16;
-  p.nrb = (p.ntile16 + p.R - 1) / p.R;
   p.ktiles = k / tile_k(fmt);
-  int sp = (512 + p.nrb - 1) / p.nrb;
-  sp = sp < 1 ? 1 : sp > 8 ? 8 : sp;
-  while (sp > 1 && p.ktiles < 4 * sp) --sp;
-  p.splits = sp;
+  const int budget = fmt == W_W4 ? 4 : 8;      // int4 dequant needs the most registers
+  int R = 8;
+  while (R > 1 && (R * p.MB > budget || (p.ntile16 + R - 1) / R < DFL_GEMM_MIN_WGS)) R /= 2;
+  if (gate_up && R < 2) R = 2;
+  p.R = R;
+  p.nwg = (p.ntile16 + R - 1) / R;
   return p;
 }
 
-size_t gemm_ws_floats(int fmt, int n, int k, int m) {
-  if (fmt == W_F32) return 0;
-  Plan p = make_plan(fmt, n, k, m);
-  if (p.splits == 1) return 0;
-  return (size_t)p.nrb * p.splits * (16 * p.R) * (16 * p.MB);
-}
+size_t gemm_ws_floats(int, int, int, int) { return 0; }
 
 int gemm_am_blocks(int fmt, int n, int m) {
   if (fmt == W_F32) return 0;
-  const int MB = (m + 15) / 16, R = MB <= 2 ? 4 : 2;
-  return (n / 16 + R - 1) / R;     // same row blocking as make_plan
+  return make_plan(fmt, n, tile_k(fmt), m, 0).nwg;
+}
+
+template <int FMT, int R>
+static hipError_t dispatch_mb(int MB, dim3 grid, const GemmArgs& a, hipStream_t s) {
+  if (R * MB > (FMT == W_W4 ? 4 : 8)) return hipErrorInvalidValue;
+  if (FMT == W_W4 && R == 8) return hipErrorInvalidValue;
+  switch (MB) {
+    case 1: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 4 ? 2 : 1)>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 2 ? 3 : 1)>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 2 ? 4 : 1)>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
 }
 
 template <int FMT>
 static hipError_t dispatch_mfma(const Plan& p, const GemmArgs& a, hipStream_t s) {
-  dim3 grid(p.nrb * p.splits), block(256);
-  if (p.R == 4 && p.MB == 1) hipLaunchKernelGGL((gemm_mfma_kernel<FMT, 4, 1>), grid, block, 0, s, a);
-  else if (p.R == 4 && p.MB == 2) hipLaunchKernelGGL((gemm_mfma_kernel<FMT, 4, 2>), grid, block, 0, s, a);
-  else if (p.R == 2 && p.MB == 3) hipLaunchKernelGGL((gemm_mfma_kernel<FMT, 2, 3>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemm_mfma_kernel<FMT, 2, 4>), grid, block, 0, s, a);
-  return hipGetLastError();
+  dim3 grid(p.nwg);
+  switch (p.R) {
+    case 8: return dispatch_mb<FMT, (FMT == W_W4 ? 4 : 8)>(p.MB, grid, a, s);
+    case 4: return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
+    case 2: return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+    default: return dispatch_mb<FMT, 1>(p.MB, grid, a, s);
+  }
 }
 
 static const char* variant_name(int fmt, const Plan& p) {
-  static const char* names[4][4] = {
-      {"gemm_f32", "gemm_f32", "gemm_f32", "gemm_f32"},
-      {"gemm_bf16_r4m1", "gemm_bf16_r4m2", "gemm_bf16_r2m3", "gemm_bf16_r2m4"},
-      {"gemm_w8_r4m1", "gemm_w8_r4m2", "gemm_w8_r2m3", "gemm_w8_r2m4"},
-      {"gemm_w4_r4m1", "gemm_w4_r4m2", "gemm_w4_r2m3", "gemm_w4_r2m4"}};
-  return names[fmt][p.MB - 1];
+  static char names[4][4][9][24];
+  static bool init = false;
+  if (!init) {
+    const char* f[4] = {"f32", "bf16", "w8", "w4"};
+    for (int i = 0; i < 4; ++i)
+      for (int mb = 1; mb <= 4; ++mb)
+        for (int r = 1; r <= 8; ++r) snprintf(names[i][mb - 1][r], 24, "gemm_%s_r%dm%d", f[i], r, mb);
+    init = true;
+  }
+  return names[fmt][p.MB - 1][p.R];
 }
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
@@ -571,26 +623,27 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
     float* lg = c.epi == EPI_ARGMAX ? w.logits_tmp : nullptr;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((ncols + 255) / 256), dim3(256), 0, s, (const float*)W.w,
                        (const float*)c.x, c.ldx, W.n, W.k, c.m, c.epi, c.out, c.ldo, c.side, c.ld_side,
-                       c.side_type, lg, W.n);
+                       c.side_type, c.side_col0, lg, W.n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
     return launch_argmax_rows(w.logits_tmp, W.n, W.n, c.row0, c.m - c.row0, c.am_out, c.logits, c.ldl, s);
   }
-  Plan p = make_plan(W.fmt, W.n, W.k, c.m);
+  Plan p = make_plan(W.fmt, W.n, W.k, c.m, W.gate_up);
   if (variant) *variant = variant_name(W.fmt, p);
   GemmArgs a;
   a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x; a.ldx = c.ldx;
-  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16; a.nrb = p.nrb; a.splits = p.splits;
+  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16;
   a.m = c.m; a.epi = c.epi; a.out = c.out; a.ldo = c.ldo; a.otype = c.otype;
-  a.side = c.side; a.ld_side = c.ld_side; a.side_type = c.side_type;
+  a.side = c.side; a.ld_side = c.ld_side; a.side_type = c.side_type; a.side_col0 = c.side_col0;
   a.logits = c.logits; a.ldl = c.ldl; a.row0 = c.row0;
-  a.am_val = w.am_val; a.am_idx = w.am_idx; a.ws = w.ws; a.ctr = w.counters;
+  a.am_val = w.am_val; a.am_idx = w.am_idx;
+  a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   hipError_t e;
   if (W.fmt == W_BF16) e = dispatch_mfma<W_BF16>(p, a, s);
   else if (W.fmt == W_W8) e = dispatch_mfma<W_W8>(p, a, s);
   else e = dispatch_mfma<W_W4>(p, a, s);
   if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
-  return launch_argmax_final(w.am_val, w.am_idx, p.nrb, c.row0, c.m - c.row0, c.am_out, s);
+  return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
 }
 
 }  // namespace dfl

@@ -7,7 +7,7 @@ namespace dfl {
 // RMSNorm(z) = z * (mean(z^2) + eps)^-1/2 * g, one work-group per row.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, int xtype, int ldx, void* out,
                                                       int otype, int ldo, const float* __restrict__ gain, int h,
-                                                      float eps) {
+                                                      float eps, int fmK) {
   const int row = blockIdx.x;
   const size_t xb = (size_t)row * ldx, ob = (size_t)row * ldo;
   float ss = 0.f;
@@ -22,13 +22,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float r = 1.0f / sqrtf(tot / (float)h + eps);
   for (int j = threadIdx.x; j < h; j += 256)
-    store_act(out, ob + j, otype, load_act(x, xb + j, xtype) * r * gain[j]);
+    store_act(out, fmK ? fm_index(row, j, fmK) : ob + j, otype, load_act(x, xb + j, xtype) * r * gain[j]);
 }
 
 hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo, const float* gain,
-                          int rows, int h, float eps, hipStream_t s) {
+                          int rows, int h, float eps, hipStream_t s, int tiled) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, xtype, ldx, out, otype, ldo, gain, h, eps);
+  const int fmK = (tiled && otype != T_F32) ? h : 0;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, xtype, ldx, out, otype, ldo, gain, h, eps, fmK);
   return hipGetLastError();
 }
 

@@ -22,6 +22,23 @@ def stream_handle() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def tile_activations(x: torch.Tensor) -> torch.Tensor:
+    """Row-major [m, k] -> the library's tiled GEMM-input layout (16-bit
+    formats): 16-row blocks, each 32-column step one 512-element fragment in
+    lane order (lane = row%16 + 16*((col%32)//8), 8 columns per lane)."""
+    m, k = x.shape
+    mb = (m + 15) // 16
+    xp = torch.zeros(mb * 16, k, dtype=x.dtype, device=x.device)
+    xp[:m] = x
+    return xp.view(mb, 16, k // 32, 4, 8).permute(0, 2, 3, 1, 4).contiguous().view(-1)
+
+
+def untile_activations(flat: torch.Tensor, m: int, k: int) -> torch.Tensor:
+    """Inverse of tile_activations (first m rows)."""
+    mb = (m + 15) // 16
+    return flat[: mb * 16 * k].view(mb, k // 32, 4, 16, 8).permute(0, 3, 1, 2, 4).reshape(mb * 16, k)[:m]
+
+
 def _dev(a, dtype, device):
     if isinstance(a, torch.Tensor):
         return a.to(device=device, dtype=dtype).contiguous()
@@ -173,7 +190,8 @@ class Pair:
         if self.cfg.drafter.fmt == FMT_F32:
             return self._arena_slice(self.view.side, 4 * self.B * w, torch.float32).view(self.B, w)
         dt = torch.bfloat16 if self.cfg.drafter.fmt == FMT_BF16 else torch.float16
-        return self._arena_slice(self.view.side, 2 * self.B * w, dt).view(self.B, w).float()
+        flat = self._arena_slice(self.view.side, 2 * self.B * w, dt)
+        return untile_activations(flat, self.B, w).float()
 
     # ------------------------------------------------------------- calls
     def prefill(self, prompt) -> int:

@@ -93,9 +93,14 @@ int dflash_pack_weight(int fmt, int n, int k, int gate_up, const void *d_src_cod
 
 /* Apply one packed linear layer on its own: Y = X W^T, the GEMM behind every
  * projection of the step (same kernels, same split plan).
- *   d_x      [m][k] activations in the GEMM-input encoding of the format:
- *            fp32 (F32), bf16 (BF16), or fp16 codes of bf16 values
- *            (W8A16 / W4A16); 1 <= m <= 64.
+ *   d_x      activations X[m][k], 1 <= m <= 64, in the GEMM-input encoding
+ *            of the format: fp32 row-major [m][ldx] (F32, ldx >= k); for the
+ *            16-bit formats (bf16 for BF16, fp16 codes of bf16 values for
+ *            W8A16 / W4A16) the tiled layout the library's own producers
+ *            write: ceil(m/16) blocks of 16 rows, element (t, j) at
+ *              ((t/16)*(k/32) + j/32)*512 + ((t%16) + 16*((j%32)/8))*8 + j%8
+ *            (every 32-column step of a block is one contiguous 1 KiB MFMA
+ *            operand); ldx is ignored there.
  *   epilogue 0: d_out = Y as fp32 [m][n] (not rounded);
  *            1: d_argmax[i] = argmax_j Y[i][j] (lowest index on ties) and, if
  *               d_out is not NULL, the fp32 logits Y [m][n].
@@ -105,8 +110,8 @@ int dflash_pack_weight(int fmt, int n, int k, int gate_up, const void *d_src_cod
  * Errors: SHAPE for unsupported dims, INVALID for null pointers or an
  * undersized workspace. */
 size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m);
-int dflash_linear(int fmt, int n, int k, const void *d_w, const void *d_s, const void *d_x, int m,
-                  int epilogue, float *d_out, int32_t *d_argmax, void *d_ws, size_t ws_bytes,
+int dflash_linear(int fmt, int n, int k, const void *d_w, const void *d_s, const void *d_x, int ldx,
+                  int m, int epilogue, float *d_out, int32_t *d_argmax, void *d_ws, size_t ws_bytes,
                   void *stream);
 
 /* ------------------------------------------------------------- models */

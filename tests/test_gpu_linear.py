@@ -13,7 +13,7 @@ from ctypes import c_size_t, byref
 from dflash_block_diffusion_amd import binding as bn
 from dflash_block_diffusion_amd import configs as C
 from dflash_block_diffusion_amd import synth
-from dflash_block_diffusion_amd.runtime import pack_weight, stream_handle
+from dflash_block_diffusion_amd.runtime import pack_weight, stream_handle, tile_activations
 from oracle.model import top2_margin
 from oracle.numerics import linear
 
@@ -27,27 +27,27 @@ def x_values(rng, m, k, fmt):
     return x
 
 
-def x_device(x, fmt):
-    t = torch.from_numpy(x).cuda()
+def x_device(x, fmt, pad=0):
+    """fp32: row-major [m][k + pad]; 16-bit formats: the tiled GEMM-input layout."""
     if fmt == C.FMT_F32:
-        return t.contiguous()
-    if fmt == C.FMT_BF16:
-        return t.to(torch.bfloat16).contiguous()
-    return t.to(torch.float16).contiguous()       # fp16 codes of bf16 values (exact here)
+        return torch.from_numpy(np.pad(x, ((0, 0), (0, pad)))).cuda().contiguous()
+    t = torch.from_numpy(x).cuda()
+    t = t.to(torch.bfloat16) if fmt == C.FMT_BF16 else t.to(torch.float16)   # fp16: exact for bf16 values
+    return tile_activations(t)
 
 
-def run_linear(w, x, fmt, epilogue=0, want_logits=True):
+def run_linear(w, x, fmt, epilogue=0, want_logits=True, pad=64):
     L = bn.lib()
     m = x.shape[0]
     dst, dsts = pack_weight(w)
     ws_bytes = L.dflash_linear_workspace_bytes(fmt, w.n, w.k, m)
     assert ws_bytes > 0
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
-    xd = x_device(x, fmt)
+    xd = x_device(x, fmt, pad)
     out = torch.full((m, w.n), float("nan"), device="cuda") if (epilogue == 0 or want_logits) else None
     am = torch.full((m,), -1, dtype=torch.int32, device="cuda")
     bn.check(L.dflash_linear(fmt, w.n, w.k, dst.data_ptr(), None if dsts is None else dsts.data_ptr(),
-                             xd.data_ptr(), m, epilogue, None if out is None else out.data_ptr(),
+                             xd.data_ptr(), w.k + pad, m, epilogue, None if out is None else out.data_ptr(),
                              am.data_ptr(), ws.data_ptr(), ws_bytes, stream_handle()))
     torch.cuda.synchronize()
     return (None if out is None else out.cpu().numpy().astype(np.float64)), am.cpu().numpy(), ws
@@ -78,6 +78,16 @@ def test_linear_parity_small(fmt, n, k, m):
     ref = linear(x, w)
     assert np.all(np.isfinite(y))
     assert np.all(np.abs(y - ref) <= bound(x, w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_linear_unpadded_rows(fmt):
+    # fp32 inputs take a row stride; exact k works too
+    g = synth.HostSynth(5)
+    w = g.weight("unpad", 272, 512, fmt)
+    x = x_values(np.random.default_rng(6), 20, 512, fmt)
+    y, _, _ = run_linear(w, x, fmt, pad=0)
+    assert np.all(np.abs(y - linear(x, w)) <= bound(x, w))
 
 
 @pytest.mark.parametrize("fmt", [C.FMT_BF16, C.FMT_W4A16])
