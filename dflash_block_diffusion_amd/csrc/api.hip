@@ -382,6 +382,7 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   s->pages = (need + PAGE - 1) / PAGE;
   s->capacity = s->pages * PAGE;
   s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
   return DFLASH_OK;
 }
 

@@ -480,7 +480,19 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restri
   const int t = row0 + blockIdx.x;
   float v = -INFINITY;
   int i = 0x7fffffff;
-  for (int b = threadIdx.x; b < nblocks; b += 256) am_merge(v, i, val[(size_t)b * 64 + t], idx[(size_t)b * 64 + t]);
+  // candidates loaded 8 at a time before merging (independent loads)
+  for (int b0 = threadIdx.x; b0 < nblocks; b0 += 256 * 8) {
+    float cv[8];
+    int ci[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + 256 * u;
+      cv[u] = b < nblocks ? val[(size_t)b * 64 + t] : -INFINITY;
+      ci[u] = b < nblocks ? idx[(size_t)b * 64 + t] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) am_merge(v, i, cv[u], ci[u]);
+  }
   __shared__ float sv[256];
   __shared__ int si[256];
   sv[threadIdx.x] = v;

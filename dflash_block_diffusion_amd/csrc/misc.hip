@@ -5,15 +5,37 @@
 namespace dfl {
 
 // RMSNorm(z) = z * (mean(z^2) + eps)^-1/2 * g, one work-group per row.
+// Each thread owns whole 8-column chunks: one 16-byte load (bf16) or two
+// (fp32) per chunk, kept in registers between the reduction and the output,
+// and one 16-byte store per chunk (8 consecutive columns are contiguous in the
+// tiled layout as well as in a row-major one).  h % 8 == 0, h <= 8192.
+constexpr int NORM_CHUNKS = 4;
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, int xtype, int ldx, void* out,
                                                       int otype, int ldo, const float* __restrict__ gain, int h,
                                                       float eps, int fmK) {
   const int row = blockIdx.x;
-  const size_t xb = (size_t)row * ldx, ob = (size_t)row * ldo;
+  const int nch = h >> 3;
+  float v[NORM_CHUNKS][8];
   float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 256) {
-    const float v = load_act(x, xb + j, xtype);
-    ss += v * v;
+#pragma unroll
+  for (int c = 0; c < NORM_CHUNKS; ++c) {
+    const int ch = threadIdx.x + 256 * c;
+    if (ch < nch) {
+      if (xtype == T_F32) {
+        const float4* p = (const float4*)((const float*)x + (size_t)row * ldx + ch * 8);
+        const float4 a = p[0], b = p[1];
+        v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
+        v[c][4] = b.x; v[c][5] = b.y; v[c][6] = b.z; v[c][7] = b.w;
+      } else {
+        const uint4 q = *(const uint4*)((const uint16_t*)x + (size_t)row * ldx + ch * 8);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
+    }
   }
   ss = wave_sum(ss);
   __shared__ float part[4];
@@ -21,13 +43,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float r = 1.0f / sqrtf(tot / (float)h + eps);
-  for (int j = threadIdx.x; j < h; j += 256)
-    store_act(out, fmK ? fm_index(row, j, fmK) : ob + j, otype, load_act(x, xb + j, xtype) * r * gain[j]);
+#pragma unroll
+  for (int c = 0; c < NORM_CHUNKS; ++c) {
+    const int ch = threadIdx.x + 256 * c;
+    if (ch >= nch) continue;
+    const int j0 = ch * 8;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = v[c][e] * r * gain[j0 + e];
+    const size_t o = fmK ? fm_index(row, j0, fmK) : (size_t)row * ldo + j0;
+    if (otype == T_F32) {
+      float4* p = (float4*)((float*)out + o);
+      p[0] = float4{y[0], y[1], y[2], y[3]};
+      p[1] = float4{y[4], y[5], y[6], y[7]};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
+        if (otype == T_F16) {
+          lo = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(lo));
+          hi = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(hi));
+        }
+        w[e] = lo | (hi << 16);
+      }
+      *(uint4*)((uint16_t*)out + o) = uint4{w[0], w[1], w[2], w[3]};
+    }
+  }
 }
 
 hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo, const float* gain,
                           int rows, int h, float eps, hipStream_t s, int tiled) {
   if (rows <= 0) return hipSuccess;
+  if (h % 8 || h > 8 * 256 * NORM_CHUNKS) return hipErrorInvalidValue;
   const int fmK = (tiled && otype != T_F32) ? h : 0;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, xtype, ldx, out, otype, ldo, gain, h, eps, fmK);
   return hipGetLastError();
