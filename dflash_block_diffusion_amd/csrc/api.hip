@@ -253,7 +253,7 @@ extern "C" int dflash_drafter_bind(dflash_model* drafter, const dflash_model* ta
 }
 
 // ------------------------------------------------------------------ state
-struct ProfRec { const char* name; double bytes; hipEvent_t a, b; };
+struct ProfRec { const char* name; double bytes; hipEvent_t a, b; GemmCall call; };
 
 struct dflash_state {
   const dflash_model* t = nullptr;
@@ -466,7 +466,7 @@ static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, 
   hipEvent_t ea = nullptr, eb = nullptr;
   if (s->prof) { ea = take_event(s); eb = take_event(s); hipEventRecord(ea, st); }
   hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes);
-  if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, ea, eb}); }
+  if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, ea, eb, c}); }
   if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm: ") + hipGetErrorString(e));
   return DFLASH_OK;
 }
@@ -696,7 +696,40 @@ extern "C" int dflash_state_buffers(dflash_state* s, dflash_state_view* v) {
 
 extern "C" int dflash_prof_enable(dflash_state* s, int on) {
   if (!s) return fail(DFLASH_E_INVALID, "null state");
+  if (on && !s->prof) {
+    for (auto& r : s->prof_recs) { s->ev_pool.push_back(r.a); s->ev_pool.push_back(r.b); }
+    s->prof_recs.clear();
+  }
   s->prof = on != 0;
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_prof_replay(dflash_state* s, const char* variant, int reps, void* stream, double* h_ms,
+                                  int64_t* h_launches) {
+  if (!s || !variant || !h_ms || !h_launches || reps < 1) return fail(DFLASH_E_INVALID, "bad argument");
+  std::vector<const GemmCall*> calls;
+  for (auto& r : s->prof_recs)
+    if (std::strcmp(r.name, variant) == 0) calls.push_back(&r.call);
+  *h_ms = 0;
+  *h_launches = 0;
+  if (calls.empty()) return DFLASH_OK;
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t ea = take_event(s), eb = take_event(s);
+  HIPCHK(hipEventRecord(ea, st));
+  for (int r = 0; r < reps; ++r)
+    for (const GemmCall* c : calls) {
+      const char* nm = nullptr;
+      hipError_t e = launch_gemm(*c, s->ws, st, &nm, nullptr);
+      if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm replay: ") + hipGetErrorString(e));
+    }
+  HIPCHK(hipEventRecord(eb, st));
+  HIPCHK(hipEventSynchronize(eb));
+  float e = 0.f;
+  HIPCHK(hipEventElapsedTime(&e, ea, eb));
+  s->ev_pool.push_back(ea);
+  s->ev_pool.push_back(eb);
+  *h_ms = e;
+  *h_launches = (int64_t)calls.size() * reps;
   return DFLASH_OK;
 }
 
@@ -716,10 +749,7 @@ extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* la
     cnt[i] += 1;
     tms[i] += e;
     tb[i] += r.bytes;
-    s->ev_pool.push_back(r.a);
-    s->ev_pool.push_back(r.b);
   }
-  s->prof_recs.clear();
   *h_n = (int)nm.size();
   for (int i = 0; i < (int)nm.size() && i < cap; ++i) {
     if (names) names[i] = nm[i];

@@ -259,6 +259,13 @@ class Pair:
         return [{"kernel": names[i].decode(), "launches": launches[i], "ms": ms[i], "bytes": by[i]}
                 for i in range(min(n.value, cap))]
 
+    def prof_replay(self, variant: str, reps: int = 1):
+        """Kernel-only time of one GEMM variant's recorded launches, replayed
+        back to back: (total ms, launches).  Clobbers the per-step buffers."""
+        ms, n = c_double(), c_int64()
+        check(lib().dflash_prof_replay(self.st, variant.encode(), reps, stream_handle(), byref(ms), byref(n)))
+        return ms.value, n.value
+
     def __del__(self):
         try:
             if getattr(self, "st", None):

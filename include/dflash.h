@@ -265,6 +265,7 @@ int dflash_state_buffers(dflash_state *st, dflash_state_view *out);
 
 /* Optional per-launch timing of the GEMM kernels with hipEvents on the
  * launch stream (eager mode only; never while a graph is being captured).
+ * Turning profiling on discards the previous records.
  * dflash_prof_read synchronises and returns per-kernel-variant totals:
  * names[i] (static strings), launches, total milliseconds and algorithmic
  * bytes (packed weights + scales) summed over launches, for up to cap
@@ -272,6 +273,20 @@ int dflash_state_buffers(dflash_state *st, dflash_state_view *out);
 int dflash_prof_enable(dflash_state *st, int on);
 int dflash_prof_read(dflash_state *st, const char **names, int64_t *launches,
                      double *ms, double *bytes, int cap, int *h_n);
+
+/* Kernel-only timing of one GEMM variant: re-launches, back to back on
+ * `stream`, every launch of that variant recorded since profiling was
+ * enabled (same weights, shapes and epilogues, in recorded order), the
+ * whole series `reps` times, between two events; *h_ms receives the total
+ * milliseconds and *h_launches the launch count (0 if the variant was not
+ * recorded).  Unlike dflash_prof_read it has no marker between launches,
+ * so total / launches is the kernel's average duration.  It rewrites the
+ * step's per-step activations and the pending drafter context, so the
+ * sequence state is not to be stepped again afterwards; it does not touch
+ * the KV caches, the token log or the committed length.  Errors: DFLASH_E_INVALID
+ * for a null argument or reps < 1, DFLASH_E_DEVICE if a launch fails. */
+int dflash_prof_replay(dflash_state *st, const char *variant, int reps,
+                       void *stream, double *h_ms, int64_t *h_launches);
 
 #ifdef __cplusplus
 }
