@@ -83,15 +83,17 @@ static GemmW mkw(int fmt, int n, int k, int gu, const void* w, const void* s);
 
 // ------------------------------------------------------------------ one linear
 struct LinearWs {
-  size_t ws_off, ctr_off, amv_off, ami_off, lg_off, total;
+  size_t part_off, amv_off, ami_off, lg_off, total;
+  size_t part_floats;
 };
 
 static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
   LinearWs L;
   size_t off = 0;
   auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
-  L.ws_off = take(std::max<size_t>(gemm_ws_floats(fmt, n, k, m), 1) * 4);
-  L.ctr_off = take((size_t)(n / 16 + 1) * 4);
+  const Plan p = make_plan(fmt, n, k, m, EPI_PARTIAL);
+  L.part_floats = (size_t)p.S * m * n;
+  L.part_off = take(L.part_floats * 4);
   const int am = std::max(1, gemm_am_blocks(fmt, n, m));
   L.amv_off = take((size_t)am * 64 * 4);
   L.ami_off = take((size_t)am * 64 * 4);
@@ -120,19 +122,19 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   if (ws_bytes < L.total) return fail(DFLASH_E_INVALID, "workspace too small");
   char* b = (char*)ws;
   Workspace W;
-  W.ws = (float*)(b + L.ws_off); W.ws_floats = gemm_ws_floats(fmt, n, k, m);
-  W.counters = (int*)(b + L.ctr_off); W.n_counters = n / 16 + 1;
+  W.part = (float*)(b + L.part_off); W.part_floats = L.part_floats;
   W.am_val = (float*)(b + L.amv_off); W.am_idx = (int*)(b + L.ami_off);
   W.am_cap = std::max(1, gemm_am_blocks(fmt, n, m));
   W.logits_tmp = (float*)(b + L.lg_off);
   GemmW g = mkw(fmt, n, k, 0, w, sc);
-  GemmCall c;
+  GemmCall c{};
   c.W = &g; c.x = x; c.ldx = ldx; c.m = m;
-  c.epi = epilogue == 0 ? EPI_STORE : EPI_ARGMAX;
-  c.out = out; c.ldo = n; c.otype = T_F32;
-  c.side = nullptr; c.ld_side = 0; c.side_type = 0;
+  c.epi = epilogue == 0 ? EPI_PARTIAL : EPI_ARGMAX;
+  c.part = W.part; c.out = nullptr; c.otype = T_F32;
   c.logits = epilogue == 1 ? out : nullptr; c.ldl = n; c.row0 = 0; c.am_out = am;
-  HIPCHK(launch_gemm(c, W, (hipStream_t)stream, nullptr, nullptr));
+  int S = 1;
+  HIPCHK(launch_gemm(c, W, (hipStream_t)stream, nullptr, nullptr, &S));
+  if (epilogue == 0) HIPCHK(launch_sum_parts(W.part, S, (size_t)m * n, out, (hipStream_t)stream));
   return DFLASH_OK;
 }
 
@@ -255,6 +257,13 @@ extern "C" int dflash_drafter_bind(dflash_model* drafter, const dflash_model* ta
 // ------------------------------------------------------------------ state
 struct ProfRec { const char* name; double bytes; hipEvent_t a, b; GemmCall call; };
 
+// Partial sums a GEMM left for the next residual/norm kernel, and where the
+// new residual is to be copied (conditioning layers feed the drafter).
+struct Pending {
+  Parts in{nullptr, 0, 0, 0};
+  void* side = nullptr; int side_type = 0; int ld_side = 0; int side_col0 = 0;
+};
+
 struct dflash_state {
   const dflash_model* t = nullptr;
   const dflash_model* dr = nullptr;
@@ -275,7 +284,6 @@ struct dflash_state {
   void* bf = nullptr;     // SiLU*mul output [64][F] gin
   void* bqkv = nullptr;   // QKV / GDN projection [64][Nqkv] act
   void* bq = nullptr;     // q after norm+rope [B][hq][d] act
-  void* fco = nullptr;    // fc output [64][H] act
   void* side = nullptr;   // drafter context input [64][n_sel*H] drafter gin
   float* o_part = nullptr;
   float* ml_part = nullptr;
@@ -339,27 +347,23 @@ static void carve(dflash_state* s, Carver& c) {
   s->bf = c.take<char>((size_t)MAX_ROWS * F * 4);
   s->bqkv = c.take<char>((size_t)MAX_ROWS * qkv_n * 4);
   s->bq = c.take<char>((size_t)B * t->d.n_q_heads * t->d.head_dim * 4 + (size_t)B * d->d.n_q_heads * d->d.head_dim * 4);
-  s->fco = c.take<char>((size_t)MAX_ROWS * H * 4);
   s->side = c.take<char>((size_t)MAX_ROWS * d->d.n_sel * H * 4);
   const int hq = std::max(t->d.n_q_heads, d->d.n_q_heads), hd = std::max(t->d.head_dim, d->d.head_dim);
   s->o_part = c.take<float>((size_t)s->max_splits * B * hq * hd);
   s->ml_part = c.take<float>((size_t)s->max_splits * B * hq * 2);
   // GEMM workspaces: the largest need over every weight of both stacks
-  size_t wsf = 0;
-  int am = 0, ctr = 1;
+  size_t pf = 1;
+  int am = 0;
   auto need = [&](const GemmW& g, int m) {
-    wsf = std::max(wsf, gemm_ws_floats(g.fmt, g.n, g.k, m));
-    ctr = std::max(ctr, g.n / 16);
+    const Plan p = make_plan(g.fmt, g.n, g.k, m, EPI_PARTIAL);
+    pf = std::max(pf, (size_t)p.S * m * g.n);
   };
-  for (const Layer& L : t->layers) { need(L.qkv, B); need(L.o, B); need(L.gu, B); need(L.down, B); }
-  for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.gu, B); need(L.down, B); }
+  for (const Layer& L : t->layers) { need(L.qkv, B); need(L.o, B); need(L.down, B); }
+  for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.down, B); }
   need(d->fc, B);
-  need(t->lm, B);
   am = std::max(1, gemm_am_blocks(t->lm.fmt, t->lm.n, B));
-  s->ws.ws = c.take<float>(std::max<size_t>(wsf, 64));
-  s->ws.ws_floats = wsf;
-  s->ws.counters = c.take<int>(ctr);
-  s->ws.n_counters = ctr;
+  s->ws.part = c.take<float>(pf);
+  s->ws.part_floats = pf;
   s->ws.am_val = c.take<float>((size_t)am * 64);
   s->ws.am_idx = c.take<int>((size_t)am * 64);
   s->ws.am_cap = am;
@@ -453,33 +457,53 @@ static hipEvent_t take_event(dflash_state* s) {
   return e;
 }
 
-static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, void* out, int ldo,
-                int otype, hipStream_t st, void* side = nullptr, int ld_side = 0, int side_type = 0,
-                float* logits = nullptr, int ldl = 0, int row0 = 0, int32_t* am_out = nullptr,
-                int side_col0 = 0) {
-  GemmCall c;
-  c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi; c.out = out; c.ldo = ldo; c.otype = otype;
-  c.side = side; c.ld_side = ld_side; c.side_type = side_type; c.side_col0 = side_col0;
+// Enqueue one GEMM.  PARTIAL launches return (in *parts) the partial sums
+// the consuming kernel adds up.
+static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, hipStream_t st,
+                Parts* parts = nullptr, void* out = nullptr, int otype = 0, float* logits = nullptr,
+                int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
+  GemmCall c{};
+  c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi;
+  c.part = s->ws.part; c.out = out; c.otype = otype;
   c.logits = logits; c.ldl = ldl; c.row0 = row0; c.am_out = am_out;
   const char* name = nullptr;
   double bytes = 0;
+  int S = 1;
   hipEvent_t ea = nullptr, eb = nullptr;
   if (s->prof) { ea = take_event(s); eb = take_event(s); hipEventRecord(ea, st); }
-  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes);
+  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes, &S);
   if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, ea, eb, c}); }
   if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm: ") + hipGetErrorString(e));
+  if (parts) *parts = Parts{s->ws.part, S, (size_t)m * W.n, W.n};
   return DFLASH_OK;
 }
 
 #define RC(x) do { int rc_ = (x); if (rc_) return rc_; } while (0)
 
-static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer& L, bool draft, hipStream_t st) {
+// Residual update with the pending partials (if any), then RMSNorm into out.
+static int norm(dflash_state* s, const dflash_model* m, Pending& pend, const float* gain, void* out, int otype,
+                int rows, hipStream_t st) {
+  NormCall c{};
+  c.mode = pend.in.p ? NORM_RESID : NORM_ONLY;
+  c.in = pend.in;
+  c.x = s->x; c.xtype = m->act; c.ldx = m->d.hidden;
+  c.side = pend.side; c.side_type = pend.side_type; c.ld_side = pend.ld_side; c.side_col0 = pend.side_col0;
+  c.gain = gain; c.eps = m->d.eps; c.h = m->d.hidden; c.rows = rows;
+  c.out = out; c.otype = otype; c.ldo = m->d.hidden; c.tiled = 1;
+  HIPCHK(launch_norm(c, st));
+  pend = Pending{};
+  return DFLASH_OK;
+}
+
+static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer& L, bool draft, Pending& pend,
+                      hipStream_t st) {
   const int H = m->d.hidden, B = s->B, hq = m->d.n_q_heads, hkv = m->d.n_kv_heads, hd = m->d.head_dim;
   const int rows = draft ? 2 * B : B;
-  HIPCHK(launch_rmsnorm(s->x, m->act, H, s->bu, m->gin, H, L.in_norm, B, H, m->d.eps, st));
-  RC(gemm(s, L.qkv, s->bu, H, rows, EPI_STORE, s->bqkv, L.qkv.n, m->act, st));
+  RC(norm(s, m, pend, L.in_norm, s->bu, m->gin, B, st));
+  Parts qkv;
+  RC(gemm(s, L.qkv, s->bu, H, rows, EPI_PARTIAL, st, &qkv));
   RopeCall rc;
-  rc.qkv = s->bqkv; rc.ldqkv = L.qkv.n; rc.atype = m->act;
+  rc.qkv = qkv; rc.atype = m->act;
   rc.block_rows = B; rc.ctx_rows = draft ? B : 0;
   rc.dev_n = s->scal + SC_N; rc.dev_p = draft ? s->scal + SC_P : nullptr;
   rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = m->d.eps;
@@ -490,20 +514,22 @@ static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer
   AttnCall ac;
   ac.q = s->bq; ac.atype = m->act; ac.kc = rc.kc; ac.vc = rc.vc; ac.page_table = s->pt;
   ac.dev_n = s->scal + SC_N; ac.block_rows = B; ac.causal = draft ? 0 : 1;
-  ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits;
+  ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits; ac.npages = s->pages;
   ac.o_part = s->o_part; ac.ml_part = s->ml_part; ac.out = s->ba; ac.otype = m->gin; ac.ldo = hq * hd;
   HIPCHK(launch_attention(ac, st));
-  RC(gemm(s, L.o, s->ba, hq * hd, B, EPI_RESID, s->x, H, m->act, st));
+  RC(gemm(s, L.o, s->ba, hq * hd, B, EPI_PARTIAL, st, &pend.in));
   return DFLASH_OK;
 }
 
-static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, hipStream_t st, void* side, int ld_side,
-               int side_type, int side_col0) {
+// FFN block; the down projection's partials stay pending (with the side copy
+// of the new residual for a conditioning layer) for the next norm.
+static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& pend, hipStream_t st,
+               void* side, int ld_side, int side_type, int side_col0) {
   const int H = m->d.hidden, F = m->d.ffn, B = s->B;
-  HIPCHK(launch_rmsnorm(s->x, m->act, H, s->bu, m->gin, H, L.post_norm, B, H, m->d.eps, st));
-  RC(gemm(s, L.gu, s->bu, H, B, EPI_SILU, s->bf, F, m->gin, st));
-  RC(gemm(s, L.down, s->bf, F, B, EPI_RESID, s->x, H, m->act, st, side, ld_side, side_type, nullptr, 0, 0,
-          nullptr, side_col0));
+  RC(norm(s, m, pend, L.post_norm, s->bu, m->gin, B, st));
+  RC(gemm(s, L.gu, s->bu, H, B, EPI_SILU, st, nullptr, s->bf, m->gin));
+  RC(gemm(s, L.down, s->bf, F, B, EPI_PARTIAL, st, &pend.in));
+  pend.side = side; pend.ld_side = ld_side; pend.side_type = side_type; pend.side_col0 = side_col0;
   return DFLASH_OK;
 }
 
@@ -511,17 +537,25 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
   const dflash_model *t = s->t, *d = s->dr;
   const int H = d->d.hidden, B = s->B;
   // context projection of the rows the last verify committed -> QKV input rows B..2B-1
-  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_STORE, s->fco, H, d->act, st));
-  HIPCHK(launch_rmsnorm(s->fco, d->act, H, (char*)s->bu + (size_t)B * H * elem_bytes(d->gin), d->gin, H,
-                        d->d.hidden_norm, B, H, d->d.eps, st));
+  Parts fc;
+  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
+  {
+    NormCall c{};
+    c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
+    c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = B;
+    // rows B..2B-1 of the tiled QKV input: whole 16-row blocks after the block rows
+    c.out = (char*)s->bu + (size_t)B * H * elem_bytes(d->gin); c.otype = d->gin; c.ldo = H; c.tiled = 1;
+    HIPCHK(launch_norm(c, st));
+  }
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 1, d->d.mask_token, B, s->x, H,
                       s->scal + SC_STATUS, st));
+  Pending pend;
   for (int l = 0; l < d->d.n_layers; ++l) {
-    RC(attn_layer(s, d, l, d->layers[l], true, st));
-    RC(ffn(s, d, d->layers[l], st, nullptr, 0, 0, 0));
+    RC(attn_layer(s, d, l, d->layers[l], true, pend, st));
+    RC(ffn(s, d, d->layers[l], pend, st, nullptr, 0, 0, 0));
   }
-  HIPCHK(launch_rmsnorm(s->x, d->act, H, s->bu, t->gin, H, d->d.final_norm, B, H, d->d.eps, st));
-  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 1, block + 1));
+  RC(norm(s, d, pend, d->d.final_norm, s->bu, t->gin, B, st));
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 1, block + 1));
   return DFLASH_OK;
 }
 
@@ -529,22 +563,23 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
   const dflash_model *t = s->t, *d = s->dr;
   const int H = t->d.hidden, B = s->B;
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 0, 0, B, s->x, H, s->scal + SC_STATUS, st));
+  Pending pend;
   int sel = 0, g = 0;
   for (int l = 0; l < t->d.n_layers; ++l) {
     const Layer& L = t->layers[l];
     if (L.kind == DFLASH_LAYER_ATTN) {
-      RC(attn_layer(s, t, l, L, false, st));
+      RC(attn_layer(s, t, l, L, false, pend, st));
     } else {
       const int gh = t->d.gdn_heads, dkk = t->d.gdn_dk, dvv = t->d.gdn_dv;
-      HIPCHK(launch_rmsnorm(s->x, t->act, H, s->bu, t->gin, H, L.in_norm, B, H, t->d.eps, st));
-      RC(gemm(s, L.qkv, s->bu, H, B, EPI_STORE, s->bqkv, L.qkv.n, t->act, st));
+      RC(norm(s, t, pend, L.in_norm, s->bu, t->gin, B, st));
       GdnCall gc;
-      gc.proj = s->bqkv; gc.ldp = L.qkv.n; gc.atype = t->act; gc.rows = B; gc.gh = gh; gc.dk = dkk; gc.dv = dvv;
+      RC(gemm(s, L.qkv, s->bu, H, B, EPI_PARTIAL, st, &gc.proj));
+      gc.atype = t->act; gc.rows = B; gc.gh = gh; gc.dk = dkk; gc.dv = dvv;
       gc.S = s->gdn_S + (size_t)g * gh * dvv * dkk;
       gc.tape = s->gdn_tape + (size_t)g * B * gh * gdn_rec(t);
       gc.out = s->ba; gc.otype = t->gin; gc.ldo = gh * dvv;
       HIPCHK(launch_gdn_verify(gc, st));
-      RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_RESID, s->x, H, t->act, st));
+      RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_PARTIAL, st, &pend.in));
       ++g;
     }
     void* side = nullptr;
@@ -554,10 +589,10 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       col0 = sel * H;
       ++sel;
     }
-    RC(ffn(s, t, L, st, side, d->d.n_sel * H, d->gin, col0));
+    RC(ffn(s, t, L, pend, st, side, d->d.n_sel * H, d->gin, col0));
   }
-  HIPCHK(launch_rmsnorm(s->x, t->act, H, s->bu, t->gin, H, t->d.final_norm, B, H, t->d.eps, st));
-  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, nullptr, 0, 0, st, nullptr, 0, 0, logits, t->d.vocab, 0, argmax));
+  RC(norm(s, t, pend, t->d.final_norm, s->bu, t->gin, B, st));
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 0, argmax));
   return DFLASH_OK;
 }
 
@@ -719,7 +754,7 @@ extern "C" int dflash_prof_replay(dflash_state* s, const char* variant, int reps
   for (int r = 0; r < reps; ++r)
     for (const GemmCall* c : calls) {
       const char* nm = nullptr;
-      hipError_t e = launch_gemm(*c, s->ws, st, &nm, nullptr);
+      hipError_t e = launch_gemm(*c, s->ws, st, &nm, nullptr, nullptr);
       if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm replay: ") + hipGetErrorString(e));
     }
   HIPCHK(hipEventRecord(eb, st));

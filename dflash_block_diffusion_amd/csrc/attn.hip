@@ -5,7 +5,10 @@
 // cosine ~0.5), then neox split-half RoPE (pairs (i, i+d/2), the convention of
 // mx.fast.rope(traditional=False) named there), one rounding to the
 // activation format, then q goes to the query buffer and k/v to the paged KV
-// cache at slot(pos) = page_table[pos/64]*64 + pos%64.
+// cache at slot(pos) = page_table[pos/64]*64 + pos%64.  A K page of one KV
+// head is [64 keys][d] (row-major); a V page is stored transposed, [d][64
+// keys], so that both MFMA operands of the attention (K for q.k, V^T for
+// p.v) are contiguous 16-byte runs along their reduction dimension.
 //
 // attn_*_kernel: softmax(q k^T / sqrt(d)) v of the B block rows over the
 // cache positions 0..n+B-1.  Verify (causal=1): row i (position n+i) sees
@@ -41,11 +44,11 @@ __global__ __launch_bounds__(64) void qk_rope_kernel(RopeCall c) {
   const int d = c.d, half = d >> 1;
   const bool act = lane < half;
   const int i = act ? lane : 0;
-  const size_t rbase = (size_t)row * c.ldqkv;
-  const size_t src = rbase + (size_t)head * d;          // q heads, then k heads
+  const int src = head * d;                 // q heads, then k heads, then v heads
   const float* gain = head < c.hq ? c.q_norm : c.k_norm;
-  float x1 = act ? load_act(c.qkv, src + i, c.atype) : 0.f;
-  float x2 = act ? load_act(c.qkv, src + i + half, c.atype) : 0.f;
+  // the QKV projection is materialised in the activation format
+  const float x1 = act ? act_round(c.atype, parts_sum(c.qkv, row, src + i)) : 0.f;
+  const float x2 = act ? act_round(c.atype, parts_sum(c.qkv, row, src + i + half)) : 0.f;
   const float ss = wave_sum(x1 * x1 + x2 * x2);
   const float r = 1.0f / sqrtf(ss / (float)d + c.eps);
   const float a = x1 * r * gain[i];
@@ -65,9 +68,10 @@ __global__ __launch_bounds__(64) void qk_rope_kernel(RopeCall c) {
     const size_t slot = (((size_t)page * c.hkv + kh) * PAGE + (pos % PAGE)) * d;
     store_act(c.kc, slot + i, c.atype, o1);
     store_act(c.kc, slot + i + half, c.atype, o2);
-    const size_t vs = rbase + (size_t)(c.hq + c.hkv + kh) * d;
-    store_act(c.vc, slot + i, c.atype, load_act(c.qkv, vs + i, c.atype));
-    store_act(c.vc, slot + i + half, c.atype, load_act(c.qkv, vs + i + half, c.atype));
+    const int vs = (c.hq + c.hkv + kh) * d;
+    const size_t vt = ((size_t)page * c.hkv + kh) * PAGE * d + (pos % PAGE);   // V^T page: [d][64]
+    store_act(c.vc, vt + (size_t)i * PAGE, c.atype, parts_sum(c.qkv, row, vs + i));
+    store_act(c.vc, vt + (size_t)(i + half) * PAGE, c.atype, parts_sum(c.qkv, row, vs + i + half));
   }
 }
 
@@ -81,174 +85,192 @@ hipError_t launch_qk_rope(const RopeCall& c, hipStream_t s) {
 struct AttnArgs {
   const uint16_t* q; const uint16_t* kc; const uint16_t* vc; const int* pt;
   const int* dev_n; int B; int causal; int hq, hkv; float scale2;   // scale * log2(e)
+  int npages;
   float* o_part; float* ml_part;
 };
 
-constexpr int KS_LD = 128 + 8;   // padded LDS row of the K page (bf16)
-constexpr int VT_LD = 64 + 8;    // padded LDS row of the transposed V page
+constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
+constexpr int ATTN_LDS = ATTN_PAGES * 2 * 16384;    // K and V^T of every page (128 KiB)
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// round-to-nearest-even to bf16 of a finite value (softmax weights), branch-free
+__device__ __forceinline__ uint32_t bf16_bits_finite(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float round_bf16_finite(float f) { return __uint_as_float(bf16_bits_finite(f) << 16); }
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return bf16_bits_finite(lo) | (bf16_bits_finite(hi) << 16);
 }
 
 // head_dim 128, bf16 q/k/v.  Work-group = (split of 256 keys, KV head, group
-// of 4 query row blocks); wave w handles row block 4*group + w (16 rows,
-// row r = token r/G, query head h*G + r%G).  S^T = K Q^T so that a lane holds
-// 4 keys of one query row; P^T then feeds O^T = V^T P^T directly as the B
-// operand.  The next page's K/V are fetched into registers while the current
-// page is multiplied.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
+// of 4 row blocks), one wave per 16-row block of the head's G*B query rows
+// (row r = token r/G, query head h*G + r%G).
+//  1. Every wave issues its share of the 4 K pages and 4 V^T pages as
+//     direct global->LDS 16-byte loads (128 KiB in flight per work-group, no
+//     registers held).  16-byte granules are XOR-swizzled inside each row so
+//     that the fragment reads below hit 16 different bank groups:
+//       K page  granule (key, c = d/8)    at key*16 + (c ^ (key & 15))
+//       V^T page granule (d, c = key/8)   at d*8 + (c ^ ((d >> 1) & 7))
+//  2. S^T = K Q^T over the whole split (a lane holds 4 keys of one row per
+//     16-key tile), row max and exp2 in one pass, P^T fed to O^T = V^T P^T
+//     as the B operand.  Softmax weights stay fp32: each p enters the MFMA as
+//     p_hi + p_lo, two bf16 values whose sum carries 16 significant bits.
+//  3. Unnormalised partial (o, max, sum) per row; attn_combine merges the
+//     splits.
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
-  __shared__ uint16_t Ks[PAGE * KS_LD];
-  __shared__ uint16_t Vt[D * VT_LD];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, sidx = blockIdx.x;
   const int n = *a.dev_n;
   const int kv_len = n + a.B;
   const int key0 = sidx * ATTN_SPLIT;
-  if (key0 >= kv_len) return;
-  const int key1 = min(key0 + ATTN_SPLIT, kv_len);
+  if (key0 >= kv_len) return;                 // uniform over the work-group
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
-  const int rbi = blockIdx.z * 4 + wave;
-  const bool live = rbi < nrb;           // wave-uniform
-  const int rbc = live ? rbi : nrb - 1;  // dead waves mirror a live block (results dropped)
 
-  bf16x8 qf[4];
-  floatx4 o[8];
-  float mrow = -INFINITY, lrow = 0.f;
+  // 1. stage K / V^T of the split (pages past the table re-read the last one;
+  //    their keys are masked below, and the arena holds finite values).  The
+  //    page indices are read first so that no load waits on another.
+  size_t pbase[ATTN_PAGES];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < ATTN_PAGES; ++p)
+    pbase[p] = ((size_t)a.pt[min(key0 / PAGE + p, a.npages - 1)] * a.hkv + h) * PAGE * D;
+#pragma unroll
+  for (int p = 0; p < ATTN_PAGES; ++p) {
+    for (int jj = wave; jj < 32; jj += nw) {
+      const int blk = jj & 15;
+      const int q = blk * 64 + lane;           // 16-byte granule of the 16 KiB region
+      const uint16_t* src;
+      if (jj < 16) {
+        const int key = q >> 4, c = (q & 15) ^ (key & 15);
+        src = a.kc + pbase[p] + key * D + c * 8;
+      } else {
+        const int d = q >> 3, c = (q & 7) ^ ((d >> 1) & 7);
+        src = a.vc + pbase[p] + d * PAGE + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (lds_ptr)(lds + (size_t)(p * 2 + (jj >> 4)) * 16384 + blk * 1024), 16, 0, 0);
+    }
+  }
+
+  const int rbi = blockIdx.z * 4 + wave;      // this wave's 16-row block
+  const bool live = rbi < nrb;                 // wave-uniform
+  const int rb = live ? rbi : nrb - 1;
+  const int r = rb * 16 + lr;
+  const int tok = r / G, qh = h * G + r % G;
+  bf16x8 qf[4];
   {
-    const int r = rbc * 16 + lr;
-    const int tok = r / G, qh = h * G + r % G;
     const uint16_t* qp = a.q + ((size_t)tok * a.hq + qh) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
   }
-  const int tok = (rbc * 16 + lr) / G;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (!live) return;
 
-  const int pg0 = key0 / PAGE, pg1 = (key1 + PAGE - 1) / PAGE;
-  // K/V of one page: 1024 chunks of 8 bf16 each, 4 per thread
-  // named registers, not arrays: an array indexed inside the page loop is
-  // left in private memory by the compiler
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  const int fkey = tid >> 4, fdc = (tid & 15) * 8;   // chunk j: key fkey + 16 j
-#define DFL_FETCH_PAGE(PG)                                                  \
-  {                                                                         \
-    const int page_ = a.pt[(PG)];                                           \
-    const uint16_t* kp_ = a.kc + ((size_t)page_ * a.hkv + h) * PAGE * D + fkey * D + fdc; \
-    const uint16_t* vp_ = a.vc + ((size_t)page_ * a.hkv + h) * PAGE * D + fkey * D + fdc; \
-    k0 = *(const uint4*)(kp_);          v0 = *(const uint4*)(vp_);          \
-    k1 = *(const uint4*)(kp_ + 16 * D); v1 = *(const uint4*)(vp_ + 16 * D); \
-    k2 = *(const uint4*)(kp_ + 32 * D); v2 = *(const uint4*)(vp_ + 32 * D); \
-    k3 = *(const uint4*)(kp_ + 48 * D); v3 = *(const uint4*)(vp_ + 48 * D); \
-  }
-#define DFL_STAGE(J, KR, VR)                                                \
-  {                                                                         \
-    const int key_ = fkey + 16 * (J);                                       \
-    *(uint4*)(Ks + key_ * KS_LD + fdc) = (KR);                              \
-    uint16_t* vt_ = Vt + fdc * VT_LD + key_;                                \
-    vt_[0 * VT_LD] = (uint16_t)(VR).x; vt_[1 * VT_LD] = (uint16_t)((VR).x >> 16); \
-    vt_[2 * VT_LD] = (uint16_t)(VR).y; vt_[3 * VT_LD] = (uint16_t)((VR).y >> 16); \
-    vt_[4 * VT_LD] = (uint16_t)(VR).z; vt_[5 * VT_LD] = (uint16_t)((VR).z >> 16); \
-    vt_[6 * VT_LD] = (uint16_t)(VR).w; vt_[7 * VT_LD] = (uint16_t)((VR).w >> 16); \
-  }
-  DFL_FETCH_PAGE(pg0)
-  for (int pg = pg0; pg < pg1; ++pg) {
-    __syncthreads();                             // previous page fully consumed
-    DFL_STAGE(0, k0, v0)
-    DFL_STAGE(1, k1, v1)
-    DFL_STAGE(2, k2, v2)
-    DFL_STAGE(3, k3, v3)
-    __syncthreads();
-    // next page (the last iteration re-reads its own page: unconditional
-    // loads keep the registers out of memory) in flight during the MFMAs
-    DFL_FETCH_PAGE(pg + 1 < pg1 ? pg + 1 : pg)
-
-    float sv[4][4];
+  // 2. two halves of 128 keys with an online max: tile kt holds keys
+  //    16kt + 4g + v of row lr
+  constexpr int NT = 8;                      // 16-key tiles per half
+  float mrow = -INFINITY, lsum = 0.f;
+  floatx4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int hf = 0; hf < 2; ++hf) {
+    float sv[NT][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int t = 0; t < NT; ++t) {
+      if ((t & 1) == 0) __builtin_amdgcn_sched_barrier(0);   // bound the K-fragment reads in flight
+      const int kt = hf * NT + t;
+      const int p = kt >> 2, key = (kt & 3) * 16 + lr;
+      const uint8_t* kpage = lds + (size_t)(p * 2) * 16384 + (size_t)key * 256;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kt * 16 + lr) * KS_LD + 32 * ks + 8 * g));
+        const int c = (4 * ks + g) ^ (key & 15);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kpos = pg * PAGE + kt * 16 + 4 * g + v;
+        const int kpos = key0 + kt * 16 + 4 * g + v;
         const bool vis = kpos < kv_len && (!a.causal || kpos <= n + tok);
-        sv[kt][v] = vis ? acc[v] * a.scale2 : -INFINITY;
-        mx = fmaxf(mx, sv[kt][v]);
+        sv[t][v] = vis ? acc[v] * a.scale2 : -INFINITY;
+        mx = fmaxf(mx, sv[t][v]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // No per-row branching below: the MFMAs are wave-wide, so a row whose
-    // keys are all masked so far (dead) runs them too, with p = 0, alpha = 1.
+    // No per-row branching: the MFMAs are wave-wide, so a row whose keys are
+    // all masked so far (dead) runs them too, with p = 0 and alpha = 1.
     const float mnew = fmaxf(mrow, mx);
     const bool dead = mnew == -INFINITY;
     const float alpha = dead ? 1.f : (mrow == -INFINITY ? 0.f : exp2f(mrow - mnew));
     mrow = mnew;
-    // softmax weights stay fp32: each p is fed to the MFMA as p_hi + p_lo,
-    // two bf16 values whose sum carries 16 significant bits
-    float psum = 0.f;
-    uint32_t ph[4][2], pl[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float hv[4], lv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float pe = (dead || sv[kt][v] == -INFINITY) ? 0.f : exp2f(sv[kt][v] - mnew);
-        hv[v] = round_bf16(pe);
-        lv[v] = round_bf16(pe - hv[v]);
-        psum += pe;
-      }
-      ph[kt][0] = bf16_pair(hv[0], hv[1]);
-      ph[kt][1] = bf16_pair(hv[2], hv[3]);
-      pl[kt][0] = bf16_pair(lv[0], lv[1]);
-      pl[kt][1] = bf16_pair(lv[2], lv[3]);
-    }
-    lrow = lrow * alpha + psum;
+    // masked scores are -inf, so exp2(x - mref) is 0 for them; a dead row
+    // subtracts 0 instead of -inf (no NaN)
+    const float mref = dead ? 0.f : mnew;
+    lsum *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      // B operand: key slots e = hh*4+v <-> key (2*ks2+hh)*16 + 4g + v
-      const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[2 * ks2][0], ph[2 * ks2][1], ph[2 * ks2 + 1][0], ph[2 * ks2 + 1][1]});
-      const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[2 * ks2][0], pl[2 * ks2][1], pl[2 * ks2 + 1][0], pl[2 * ks2 + 1][1]});
+    for (int k2 = 0; k2 < NT / 2; ++k2) {
+      // one 32-key step at a time: keeps the scheduler from hoisting every
+      // V fragment read (and its registers) to the top of the loop
+      __builtin_amdgcn_sched_barrier(0);
+      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float hv[4], lv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float pe = exp2f(sv[2 * k2 + hh][v] - mref);
+          hv[v] = round_bf16_finite(pe);
+          lv[v] = round_bf16_finite(pe - hv[v]);
+          lsum += pe;
+        }
+        ph[2 * hh] = bf16_pair(hv[0], hv[1]);
+        ph[2 * hh + 1] = bf16_pair(hv[2], hv[3]);
+        pl[2 * hh] = bf16_pair(lv[0], lv[1]);
+        pl[2 * hh + 1] = bf16_pair(lv[2], lv[3]);
+      }
+      const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+      const int ks2 = hf * (NT / 2) + k2;
+      const int p = ks2 >> 1;
+      const uint8_t* vpage = lds + (size_t)(p * 2 + 1) * 16384;
+      const int c0 = 4 * (ks2 & 1) + (g >> 1), half = (g & 1) * 8;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* vrow = Vt + (dt * 16 + lr) * VT_LD + (2 * ks2) * 16 + 4 * g;
-        const uint2 lo = *(const uint2*)vrow;
-        const uint2 hi = *(const uint2*)(vrow + 16);
+        const int d = dt * 16 + lr, sw = (d >> 1) & 7;
+        const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + half);
+        const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + half);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
       }
     }
   }
+  const float mx = mrow;
 
-#undef DFL_FETCH_PAGE
-#undef DFL_STAGE
-  // partials: o (unnormalised), m (log2 domain) and l per query row
-  if (!live) return;
-  float l = lrow;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  const int r = rbi * 16 + lr;
-  const int qh = h * G + r % G;
+  // 3. partials: o (unnormalised), m (log2 domain) and l per query row
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
   const size_t row = ((size_t)sidx * a.B + tok) * a.hq + qh;
   float* op = a.o_part + row * D;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
     *(floatx4*)(op + dt * 16 + 4 * g) = o[dt];    // O^T: lane holds d = dt*16+4g+v of row lr
   if (g == 0) {
-    a.ml_part[row * 2] = mrow;
-    a.ml_part[row * 2 + 1] = l;
+    a.ml_part[row * 2] = mx;
+    a.ml_part[row * 2 + 1] = lsum;
   }
 }
 
@@ -282,7 +304,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     const float al = m == -INFINITY ? 0.f : exp2f(m - mn);
     const float p = exp2f(s - mn);
     l = l * al + p;
-    for (int e = 0; e < D; ++e) ov[e] = ov[e] * al + p * vc[slot + e];
+    const size_t vt = ((size_t)pt[key / PAGE] * hkv + h) * PAGE * D + key % PAGE;   // V^T page
+    for (int e = 0; e < D; ++e) ov[e] = ov[e] * al + p * vc[vt + (size_t)e * PAGE];
     m = mn;
   }
   const size_t row = ((size_t)sidx * B + tok) * hq + qh;
@@ -355,9 +378,17 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     a.q = (const uint16_t*)c.q; a.kc = (const uint16_t*)c.kc; a.vc = (const uint16_t*)c.vc;
     a.pt = c.page_table; a.dev_n = c.dev_n; a.B = c.block_rows; a.causal = c.causal;
     a.hq = c.hq; a.hkv = c.hkv; a.scale2 = scale2; a.o_part = c.o_part; a.ml_part = c.ml_part;
+    a.npages = c.npages;
     const int nrb = (c.hq / c.hkv) * c.block_rows / 16;
-    dim3 g3(c.max_splits, c.hkv, (nrb + 3) / 4);
-    hipLaunchKernelGGL(attn_mfma_kernel, g3, dim3(256), 0, s, a);
+    if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         ATTN_LDS);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), ATTN_LDS, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -94,7 +94,11 @@ struct GemmW {
   const void* s;      // packed scales (W8/W4) or null
 };
 
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+// EPI_PARTIAL: fp32 partial sums [S][m][n] of S K ranges (one range for fp32
+//              models), added up by the consuming kernel (see Parts);
+// EPI_SILU:    fused gate/up -> silu(gate) * up, 16-bit tiled output (K = n/2);
+// EPI_ARGMAX:  per-row argmax over n (lowest index on ties), optional logits.
+enum Epi { EPI_PARTIAL = 0, EPI_SILU = 2, EPI_ARGMAX = 3 };
 
 struct GemmCall {
   const GemmW* W;
@@ -102,34 +106,56 @@ struct GemmCall {
                                  // (fm_index with K) BF16 for W_BF16, F16 for W8/W4
   int m;                         // valid rows (<= 64); kernels compute ceil(m/16)*16 rows
   int epi;
-  void* out; int ldo; int otype; // STORE/SILU output, RESID residual stream (in place)
-  void* side; int ld_side; int side_type;   // RESID: optional copy of the new residual
-  int side_col0;                            // at columns side_col0.. of the side buffer (K = ld_side)
+  float* part;                   // PARTIAL: [S][m][n]
+  void* out; int otype;          // SILU output
   // ARGMAX
   float* logits; int ldl; int row0;         // optional fp32 logits of rows row0..m-1
   int32_t* am_out;                          // argmax of rows row0..m-1 -> am_out[0..]
 };
 
 struct Workspace {
-  float* ws; size_t ws_floats;   // split-K partial tiles
-  int* counters; int n_counters; // split-K arrival counters (zero between launches)
+  float* part; size_t part_floats;          // split-K partials
   float* am_val; int* am_idx; int am_cap;   // argmax partials [am_cap][64]
-  float* logits_tmp;             // F32 path: [64][V] logits scratch
+  float* logits_tmp;                        // F32 path: [64][V] logits scratch
 };
 
-struct ProfHook;  // per-launch timing (host side)
+struct Plan { int RT, MB, S, ngroups, nwg, ktiles, ntile16; };
+Plan make_plan(int fmt, int n, int k, int m, int epi);
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
-                       double* bytes);
+                       double* bytes, int* splits);
 hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, const void* src_scales,
                        void* dst, void* dst_scales, hipStream_t s);
+hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, hipStream_t s);
 void packed_bytes(int fmt, int n, int k, size_t* wb, size_t* sb);
-size_t gemm_ws_floats(int fmt, int n, int k, int m);
 int gemm_am_blocks(int fmt, int n, int m);
+
+// The S fp32 partials of one PARTIAL launch as seen by a consumer: element
+// (t, n) is the sum over s of p[s*stride + t*ld + n], added in split order.
+struct Parts {
+  const float* p;
+  int S;
+  size_t stride;   // floats between splits (m * n of the launch)
+  int ld;          // row stride (n of the launch)
+};
+constexpr int MAX_SPLITS = 8;
+// All S loads are issued before the first add (S <= MAX_SPLITS), so the
+// partials cost one memory round trip, not S.
+__device__ __forceinline__ float parts_sum(const Parts& P, int t, int n) {
+  const float* q = P.p + (size_t)t * P.ld + n;
+  float x[MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) x[s] = s < P.S ? q[(size_t)s * P.stride] : 0.f;
+  float v = x[0];
+#pragma unroll
+  for (int s = 1; s < MAX_SPLITS; ++s)
+    if (s < P.S) v = v + x[s];
+  return v;
+}
 
 // ------------------------------------------------------------ other kernels
 struct RopeCall {
-  const void* qkv; int ldqkv; int atype;   // GEMM output [rows][ldqkv] (act type)
+  Parts qkv; int atype;                     // QKV GEMM partials [rows][n_qkv]; rounded to atype
   int block_rows;                           // B: rows 0..B-1 at positions n+i
   int ctx_rows;                             // drafter: rows B..B+ctx_rows-1 are context rows
   const int* dev_n; const int* dev_p;       // committed length, pending context rows
@@ -145,15 +171,28 @@ struct AttnCall {
   const void* q; int atype;                  // [B][hq][d] act (bf16 or f32)
   const void* kc; const void* vc; const int* page_table;
   const int* dev_n; int block_rows; int causal;
-  int hq, hkv, d; int max_splits;
+  int hq, hkv, d; int max_splits; int npages;  // splits of ATTN_SPLIT keys; pages in the table
   float* o_part; float* ml_part;              // [max_splits][B*hq][d], [max_splits][B*hq][2]
   void* out; int otype; int ldo;              // [B][hq*d]
 };
 hipError_t launch_attention(const AttnCall& c, hipStream_t s);
 
-// out: tiled with K = h when otype is 16-bit and tiled != 0, else row-major [rows][ldo]
-hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo,
-                          const float* gain, int rows, int h, float eps, hipStream_t s, int tiled = 1);
+// Residual update + RMSNorm of `rows` rows of width h, one work-group per row:
+//   NORM_ONLY  v = x
+//   NORM_RESID v = round(x + round(sum of in)); x <- v; side copy of v (optional)
+//   NORM_PROJ  v = round(sum of in)            (x untouched)
+// then out = round(v * (mean(v^2) + eps)^-1/2 * gain).  out is tiled (K = h)
+// when otype is 16-bit and tiled != 0, else row-major [rows][ldo].
+enum NormMode { NORM_ONLY = 0, NORM_RESID = 1, NORM_PROJ = 2 };
+struct NormCall {
+  int mode;
+  Parts in;
+  void* x; int xtype; int ldx;              // residual stream (row-major)
+  void* side; int side_type; int ld_side; int side_col0;   // tiled (K = ld_side) when 16-bit
+  const float* gain; float eps; int h; int rows;
+  void* out; int otype; int ldo; int tiled;
+};
+hipError_t launch_norm(const NormCall& c, hipStream_t s);
 hipError_t launch_embed(const void* table, int ttype, int h, int vocab, const int32_t* tokens,
                         int mask_mode, int mask_token, int rows, void* out, int ldo,
                         int32_t* status, hipStream_t s);
@@ -178,7 +217,7 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t count, hipStream
 
 // GatedDeltaNet
 struct GdnCall {
-  const void* proj; int ldp; int atype;     // [B][gh*(2dk+dv)+2gh] GEMM output (act)
+  Parts proj; int atype;                    // [B][gh*(2dk+dv)+2gh] GEMM partials, rounded to atype
   int rows; int gh, dk, dv;
   const float* S;                            // committed state [gh][dv][dk]
   float* tape;                               // [B][gh][dk+dv+2]

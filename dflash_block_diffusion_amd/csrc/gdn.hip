@@ -72,11 +72,12 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
 
   // per-token preprocessing: one wave per token
   for (int t = wave; t < c.rows; t += NT / 64) {
-    const size_t rb = (size_t)t * c.ldp;
+    // the projection is materialised in the activation format
+    auto proj = [&](size_t col) { return act_round(c.atype, parts_sum(c.proj, t, (int)col)); };
     float qs = 0.f, ks = 0.f;
     for (int e = lane; e < DK; e += 64) {
-      const float qv = load_act(c.proj, rb + qo + e, c.atype);
-      const float kv = load_act(c.proj, rb + ko + e, c.atype);
+      const float qv = proj(qo + e);
+      const float kv = proj(ko + e);
       qs += qv * qv;
       ks += kv * kv;
     }
@@ -86,19 +87,19 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
     const float kn = 1.0f / sqrtf(ks + 1e-6f);
     float* tape = c.tape + ((size_t)t * gh + h) * REC;
     for (int e = lane; e < DK; e += 64) {
-      const float kh = load_act(c.proj, rb + ko + e, c.atype) * kn;
+      const float kh = proj(ko + e) * kn;
       kq[t][e] = kh;
-      kq[t][DK + e] = load_act(c.proj, rb + qo + e, c.atype) * qn;
+      kq[t][DK + e] = proj(qo + e) * qn;
       tape[e] = kh;
     }
     for (int e = lane; e < DV; e += 64) {
-      const float vv = load_act(c.proj, rb + vo + e, c.atype);
+      const float vv = proj(vo + e);
       kq[t][2 * DK + e] = vv;
       tape[DK + e] = vv;
     }
     if (lane == 0) {
-      const float av = load_act(c.proj, rb + ao, c.atype);
-      const float bv = load_act(c.proj, rb + bo, c.atype);
+      const float av = proj(ao);
+      const float bv = proj(bo);
       const float alpha = 1.0f / (1.0f + expf(av));
       const float beta = 1.0f / (1.0f + expf(-bv));
       kq[t][2 * DK + DV] = alpha;

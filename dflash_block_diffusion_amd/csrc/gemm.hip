@@ -16,22 +16,32 @@
 // Packed layout: per tile of 16 weight rows x KT columns (KT = 32/64/128 for
 // BF16/W8/W4) one contiguous 1 KiB block; lane l of a wave loads bytes
 // [16l, 16l+16), which hold row (l % 16) and, for each 32-wide MFMA sub-step
-// ss of the tile, the 8 columns KT*t + 32*ss + 8*(l/16) + e, e = 0..7 --
-// exactly the A-operand of v_mfma_f32_16x16x32 for that lane.  So every wave
-// load is one fully coalesced 1 KiB read and needs no shuffling.  The
-// activations come in the matching tiled layout (fm_index in common.h), so
-// their operand fragments are contiguous 1 KiB reads as well: with row-major
-// activations each fragment is a 16-row gather, and those gathers saturated
-// the texture addresser long before HBM.
+// ss of the tile, the 8 columns KT*t + 32*ss + 8*(l/16) + e, e = 0..7 -- one
+// lane's share of a 16x32 MFMA operand.  So every wave load is one fully
+// coalesced 1 KiB read and needs no shuffling.  W4 scales are packed per
+// (row tile, K tile) as 16 dwords, dword r = the two group scales of row r, so
+// that lane l reads its row's pair with one 4-byte load.  The activations come
+// in the matching tiled layout (fm_index in common.h): every operand fragment
+// is a contiguous 1 KiB read as well.
 //
-// Work split: a work-group (4 waves) owns R row tiles (16R rows) over the full
-// K; wave w takes the w-th quarter of the K tiles and prefetches the next tile
-// while it multiplies the current one.  The 4 wave partials are summed in LDS
-// in a fixed order, so results are bit-reproducible.  R is chosen per shape
-// so that even the narrow projections (N = 4096) launch one work-group per
-// CU.  (No cross-work-group split-K: a release/acquire handoff between
-// work-groups writes back the L2 and costs far more than it saves here.)
+// MFMA orientation: A = activation fragment (16 tokens x 32 K), B = weight
+// fragment (32 K x 16 weight rows), so lane l accumulates weight row l % 16
+// for tokens 4*(l/16)..+3 and the per-row W4 scale is one value per lane.
+//
+// Work split (memory-level parallelism first):
+//   * a work-group (4 waves) owns RT row tiles (16*RT weight rows) and one of
+//     S contiguous K ranges; wave w takes the w-th quarter of that range;
+//   * each wave streams its K tiles through a ring of U register stages (U K
+//     tiles of all RT row tiles in flight); every activation fragment loaded
+//     feeds RT MFMAs, so activation reads are 2x (int4), 1x (int8) or 1/4x
+//     (bf16) the weight bytes rather than 8x with one row tile per wave;
+//   * the 4 wave partials are summed in LDS in a fixed order; with S > 1 the
+//     work-group writes an fp32 partial [m][n] of its K range and the consumer
+//     kernel (residual + RMSNorm, QK-norm + RoPE, GatedDeltaNet) adds the S
+//     partials in a fixed order.  All sums are bit-reproducible.
+//   Non-linear epilogues (fused gate/up SiLU*mul, lm-head argmax) use S = 1.
 #include <cstdio>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -84,18 +94,18 @@ __global__ void pack_kernel(int n, int k, int gate_up, const void* __restrict__ 
   *(uint4*)(dst + tile * 1024 + (size_t)lane * 16) = v;
 }
 
-// W4 scales: per (row tile, K tile) 32 halves; lane quarter q reads 8 halves
-// [group 0: rows 4q..4q+3][group 1: rows 4q..4q+3] with one 16-byte load.
+// W4 scales: per (row tile, K tile) 16 dwords; dword r holds the scales of
+// groups 2t (low half) and 2t+1 (high half) of packed row 16*rt + r.
 __global__ void pack_scales_w4(int n, int k, int gate_up, const uint16_t* __restrict__ src,
                                uint16_t* __restrict__ dst) {
   const int ktiles = k / 128;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)(n / 16) * ktiles * 32;
   if (idx >= total) return;
-  const int v = idx & 3, gg = (idx >> 2) & 1, q = (idx >> 3) & 3;
+  const int gg = idx & 1, r = (idx >> 1) & 15;
   const size_t tile = idx >> 5;
   const int t = (int)(tile % ktiles), rt = (int)(tile / ktiles);
-  const int row = canon_row(rt, 4 * q + v, n, gate_up);
+  const int row = canon_row(rt, r, n, gate_up);
   dst[idx] = src[(size_t)row * (k / 64) + 2 * t + gg];
 }
 
@@ -147,7 +157,6 @@ hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, cons
 
 // --------------------------------------------------------------- dequant
 __device__ __forceinline__ half2v h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
-__device__ __forceinline__ uint32_t u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // 8 int4 codes (one dword, offset binary, nibble slots as packed) -> 8 halves
 // 0x6400 | u is the fp16 value 1024 + u; (0x6400 | 16u) scaled by 1/16 is 64 + u.
@@ -179,53 +188,66 @@ __device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi, uint32_t magic
 
 // ------------------------------------------------------------------ kernel
 struct GemmArgs {
-  const uint8_t* w; const uint16_t* s; const uint16_t* x; int ldx;
-  int n, k, ktiles, ntile16, m;
-  int epi; void* out; int ldo; int otype;
-  void* side; int ld_side; int side_type; int side_col0;
-  float* logits; int ldl; int row0;
+  const uint8_t* w; const uint16_t* s; const uint16_t* x;
+  int n, k, ktiles, ntile16, m, splits;
+  int epi;
+  float* part;                               // EPI_PARTIAL: [splits][m][n] fp32
+  void* out; int otype;                      // EPI_SILU: tiled [m][n/2] (K = n/2)
+  float* logits; int ldl; int row0;          // EPI_ARGMAX
   float* am_val; int* am_idx;
   // dequant bit masks, passed as arguments so that they live in registers
   // (gfx9 VOP3 encodings take no literal constants)
   uint32_t mlo, mhi, magic;
 };
 
-template <int FMT, int R, int MB>
-struct Frag {          // one K tile's operands for one wave
-  uint4 w[R];
-  uint4 s[R];
+// registers of one ring stage (one K tile of all RT row tiles + its
+// activation fragments) and the ring depth that fits ~170 VGPRs
+__host__ __device__ constexpr int stage_regs(int fmt, int rt, int mb) {
+  return 4 * rt + (fmt == W_W4 ? rt : 0) + 4 * mb * (tile_k(fmt) / 32);
+}
+__host__ __device__ constexpr int ring_depth(int fmt, int rt, int mb) {
+  return 170 / stage_regs(fmt, rt, mb) < 2 ? 2 : (170 / stage_regs(fmt, rt, mb) > 8 ? 8 : 170 / stage_regs(fmt, rt, mb));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// streamed weights are read once: non-temporal, so they do not evict the
+// activations every work-group re-reads from L2
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+template <int FMT, int RT, int MB>
+struct Stage {
+  uint4 w[RT];
+  uint32_t s[RT];                 // W4: the two group scales of this lane's row
   uint4 x[MB][tile_k(FMT) / 32];
 };
 
-// Work-group = 4 waves on R row tiles (16R weight rows) over the full K; wave
-// w takes the w-th quarter of the K tiles; the quarters are summed in LDS in a
-// fixed order (bit-reproducible).  Loads of the next K tile are issued before
-// the current one is consumed (register double buffering).
-template <int FMT, int R, int MB>
+template <int FMT, int RT, int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void gemm_mfma_kernel(GemmArgs a) {
+void gemm_stream_kernel(GemmArgs a) {
   constexpr int KT = tile_k(FMT);
   constexpr int SS = KT / 32;
-  // ring depth (K tiles in flight per wave): as many stages as fit ~128 VGPRs
-  constexpr int STAGE = 4 * R * (FMT == W_W4 ? 2 : 1) + 4 * MB * SS;
-  constexpr int U = 4 * STAGE <= 128 ? 4 : (3 * STAGE <= 128 ? 3 : 2);
-  constexpr int ROWS = 16 * R;          // weight rows of this work-group
-  constexpr int TOK = 16 * MB;          // token rows computed
-  constexpr int TS = ROWS * TOK;        // tile floats
-  __shared__ float red[3][R * MB * 4][64];
-  __shared__ float tileT[TOK][ROWS + 1];
+  constexpr int U = ring_depth(FMT, RT, MB);
+  constexpr int NE = RT * MB * 4;            // accumulator floats per lane
+  __shared__ float red[4][NE][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int rt0 = blockIdx.x * R;
-  const int t0 = (int)((long long)a.ktiles * wave / 4);
-  const int t1 = (int)((long long)a.ktiles * (wave + 1) / 4);
+  const int S = a.splits;
+  const int sidx = blockIdx.x % S, rg = blockIdx.x / S;
+  const int kt0 = (int)((long long)a.ktiles * sidx / S);
+  const int kt1 = (int)((long long)a.ktiles * (sidx + 1) / S);
+  const int nk = kt1 - kt0;
+  const int t0 = kt0 + nk * wave / 4, t1 = kt0 + nk * (wave + 1) / 4;
+  const int rt0 = rg * RT;
   const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
 
-  floatx4 acc[R][MB];
+  floatx4 acc[RT][MB];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[r][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -234,23 +256,21 @@ void gemm_mfma_kernel(GemmArgs a) {
   const uint16_t* xrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) xrow[mb] = a.x + (size_t)mb * (a.k >> 5) * 512 + lane * 8;
-  const uint8_t* wbase[R];
-  const uint16_t* sbase[R];
-  bool live[R];
+  const uint8_t* wbase[RT];
+  const uint32_t* sbase[RT];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < RT; ++r) {
     const int rt = rt0 + r;
-    live[r] = rt < a.ntile16;
-    const int rtc = live[r] ? rt : a.ntile16 - 1;     // clamped: dead tiles re-read a valid one
+    const int rtc = rt < a.ntile16 ? rt : a.ntile16 - 1;   // dead tiles re-read a valid one
     wbase[r] = a.w + (size_t)rtc * a.ktiles * 1024 + lane * 16;
-    sbase[r] = (FMT == W_W4) ? a.s + (size_t)rtc * a.ktiles * 32 + g * 8 : nullptr;
+    sbase[r] = (FMT == W_W4) ? (const uint32_t*)a.s + (size_t)rtc * a.ktiles * 16 + lr : nullptr;
   }
 
-  auto load = [&](int t, Frag<FMT, R, MB>& f) {
+  auto load = [&](int t, Stage<FMT, RT, MB>& f) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      f.w[r] = *(const uint4*)(wbase[r] + (size_t)t * 1024);
-      if (FMT == W_W4) f.s[r] = *(const uint4*)(sbase[r] + (size_t)t * 32);
+    for (int r = 0; r < RT; ++r) {
+      f.w[r] = load_stream(wbase[r] + (size_t)t * 1024);
+      if (FMT == W_W4) f.s[r] = sbase[r][(size_t)t * 16];
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -258,165 +278,158 @@ void gemm_mfma_kernel(GemmArgs a) {
       for (int ss = 0; ss < SS; ++ss) f.x[mb][ss] = *(const uint4*)(xrow[mb] + ((size_t)t * SS + ss) * 512);
   };
 
-  auto compute = [&](const Frag<FMT, R, MB>& f) {
-    const uint4 (&xf)[MB][SS] = f.x;
+  auto compute = [&](const Stage<FMT, RT, MB>& f) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RT; ++r) {
       if (FMT == W_BF16) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, f.w[r]);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, f.w[r]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              av, __builtin_bit_cast(bf16x8, xf[mb][0]), acc[r][mb], 0, 0, 0);
+          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.x[mb][0]), bv,
+                                                               acc[r][mb], 0, 0, 0);
       } else if (FMT == W_W8) {
-        const half8 a0 = deq_w8(f.w[r].x, f.w[r].y, magic);
-        const half8 a1 = deq_w8(f.w[r].z, f.w[r].w, magic);
+        const half8 b0 = deq_w8(f.w[r].x, f.w[r].y, magic);
+        const half8 b1 = deq_w8(f.w[r].z, f.w[r].w, magic);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              a0, __builtin_bit_cast(half8, xf[mb][0]), acc[r][mb], 0, 0, 0);
-          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              a1, __builtin_bit_cast(half8, xf[mb][1]), acc[r][mb], 0, 0, 0);
+          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][0]), b0,
+                                                              acc[r][mb], 0, 0, 0);
+          acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][1]), b1,
+                                                              acc[r][mb], 0, 0, 0);
         }
       } else {  // W4: two 64-wide groups per tile, sub-steps (0,1) and (2,3)
         const uint32_t wd[4] = {f.w[r].x, f.w[r].y, f.w[r].z, f.w[r].w};
-        const uint32_t sd[4] = {f.s[r].x, f.s[r].y, f.s[r].z, f.s[r].w};
+        const half2v sc = h2(f.s[r]);
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
-          const half8 a0 = deq_w4(wd[2 * gg], mlo, mhi, magic);
-          const half8 a1 = deq_w4(wd[2 * gg + 1], mlo, mhi, magic);
-          const half2v s01 = __builtin_bit_cast(half2v, sd[2 * gg]);
-          const half2v s23 = __builtin_bit_cast(half2v, sd[2 * gg + 1]);
+          const half8 b0 = deq_w4(wd[2 * gg], mlo, mhi, magic);
+          const half8 b1 = deq_w4(wd[2 * gg + 1], mlo, mhi, magic);
+          const float sg = (float)sc[gg];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                a0, __builtin_bit_cast(half8, xf[mb][2 * gg]), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                a1, __builtin_bit_cast(half8, xf[mb][2 * gg + 1]), tmp, 0, 0, 0);
-            acc[r][mb][0] += (float)s01[0] * tmp[0];
-            acc[r][mb][1] += (float)s01[1] * tmp[1];
-            acc[r][mb][2] += (float)s23[0] * tmp[2];
-            acc[r][mb][3] += (float)s23[1] * tmp[3];
+            floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), b0,
+                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]), b1, tmp,
+                                                         0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[r][mb][v] += sg * tmp[v];
           }
         }
       }
     }
   };
 
-  // Operands stream through a ring of U register stages: each stage holds one
-  // K tile's weights (HBM), scales and activations (L2), so U tiles of loads
-  // are in flight per wave while the oldest is multiplied.  The main loop is
-  // branch-free (every load unconditional, the last round re-reads a clamped
-  // valid tile) so the compiler can wait for one stage at a time instead of
-  // draining all outstanding loads; leftover tiles run in a short tail loop.
-  const int full = (t1 - t0) / U;
-  if (full > 0) {
-    Frag<FMT, R, MB> ring[U];
+  const int nt = t1 - t0;
+  if (nt > 0 && nt <= U) {
+    // the wave's whole K range fits the ring: issue every load, then multiply
+    Stage<FMT, RT, MB> ring[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < nt) load(t0 + u, ring[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < nt) compute(ring[u]);
+  } else if (nt > U) {
+    // Operands stream through a ring of U register stages: U K tiles of loads
+    // are in flight per wave while the oldest is multiplied.  Loads are
+    // unconditional (the last round re-reads a clamped valid tile) so the
+    // compiler waits for one stage at a time instead of draining the ring.
+    Stage<FMT, RT, MB> ring[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(t0 + u, ring[u]);
     // keep the scheduler from sinking loads next to their uses (it would
     // trade the in-flight depth for registers)
     __builtin_amdgcn_sched_barrier(0);
-    for (int rd = 0; rd < full; ++rd) {
+    for (int base = t0; base < t1; base += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        compute(ring[u]);
-        load(min(t0 + (rd + 1) * U + u, t1 - 1), ring[u]);
+        if (base + u < t1) compute(ring[u]);
+        load(min(base + U + u, t1 - 1), ring[u]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-  for (int t = t0 + full * U; t < t1; ++t) {
-    Frag<FMT, R, MB> f;
-    load(t, f);
-    compute(f);
-  }
 
-  // ---- fixed-order reduction of the 4 wave partials
-  if (wave > 0) {
+  // ---- fixed-order reduction of the 4 wave partials: ((w0 + w1) + w2) + w3
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave - 1][(r * MB + mb) * 4 + v][lane] = acc[r][mb][v];
-  }
+      for (int v = 0; v < 4; ++v) red[wave][(r * MB + mb) * 4 + v][lane] = acc[r][mb][v];
   __syncthreads();
-  if (wave == 0) {
+  // thread (wave w, lane) finishes accumulator slot v = w of every (r, mb):
+  // token mb*16 + 4g + w, weight row (rt0 + r)*16 + lr
+  float val[RT][MB];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = (r * MB + mb) * 4 + v;
-          float sum = acc[r][mb][v] + red[0][j][lane];
-          sum = sum + red[1][j][lane];
-          sum = sum + red[2][j][lane];
-          // D layout of 16x16 MFMA: lane holds column (token) lane%16, rows 4*(lane/16)+v
-          tileT[mb * 16 + lr][r * 16 + 4 * g + v] = sum;
-        }
-  }
-  __syncthreads();
-  (void)live;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int j = (r * MB + mb) * 4 + wave;
+      val[r][mb] = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+    }
 
-  // ---- epilogues
-  const int n0 = rt0 * 16;
   const uint16_t* sc8 = (FMT == W_W8) ? a.s : nullptr;
   auto scale_of = [&](int n) -> float {
     return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : 1.0f;
   };
-  if (a.epi == EPI_STORE || a.epi == EPI_RESID) {
-    for (int e = tid; e < TS; e += 256) {
-      const int t = e / ROWS, nl = e % ROWS, n = n0 + nl;
-      if (t >= a.m || n >= a.n) continue;
-      const float y = tileT[t][nl] * scale_of(n);
-      const size_t o = (size_t)t * a.ldo + n;
-      if (a.epi == EPI_STORE) {
-        store_act(a.out, o, a.otype, y);
-      } else {
-        const float xo = load_act(a.out, o, a.otype);
-        const float nv = act_round(a.otype, xo + act_round(a.otype, y));
-        store_act(a.out, o, a.otype, nv);
-        if (a.side)
-          store_act(a.side, act_index(t, a.side_col0 + n, a.ld_side, a.side_type == T_F32 ? 0 : a.ld_side),
-                    a.side_type, nv);
+  if (a.epi == EPI_PARTIAL) {
+    float* part = a.part + (size_t)sidx * a.m * a.n;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      if (rt0 + r >= a.ntile16) continue;
+      const int n = (rt0 + r) * 16 + lr;
+      const float sc = scale_of(n);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int t = mb * 16 + 4 * g + wave;
+        if (t < a.m) part[(size_t)t * a.n + n] = val[r][mb] * sc;
       }
     }
   } else if (a.epi == EPI_SILU) {
-    constexpr int HALF = ROWS / 2;
-    for (int e = tid; e < TOK * HALF; e += 256) {
-      const int t = e / HALF, j = e % HALF;
-      const int pr = j / 16, w = j % 16;
-      const int gl = (2 * pr) * 16 + w, ul = (2 * pr + 1) * 16 + w;
-      const int n_out = (rt0 / 2 + pr) * 16 + w;
-      if (t >= a.m || n_out >= a.n / 2) continue;
-      const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
-      const float gv = act_round(rnd, tileT[t][gl] * scale_of(n0 + gl));
-      const float uv = act_round(rnd, tileT[t][ul] * scale_of(n0 + ul));
-      const float sv = gv / (1.0f + expf(-gv));
-      store_act(a.out, act_index(t, n_out, a.ldo, a.otype == T_F32 ? 0 : a.n / 2), a.otype, sv * uv);
+    const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
+    const int half_n = a.n >> 1;
+#pragma unroll
+    for (int p = 0; p < RT / 2; ++p) {
+      if (rt0 + 2 * p + 1 >= a.ntile16) continue;
+      const int ng = (rt0 + 2 * p) * 16 + lr, nu = ng + 16;
+      const int n_out = ((rt0 >> 1) + p) * 16 + lr;
+      const float sg = scale_of(ng), su = scale_of(nu);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int t = mb * 16 + 4 * g + wave;
+        if (t >= a.m) continue;
+        const float gv = act_round(rnd, val[2 * p][mb] * sg);
+        const float uv = act_round(rnd, val[2 * p + 1][mb] * su);
+        const float sv = gv / (1.0f + expf(-gv));
+        store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
+      }
     }
   } else {  // EPI_ARGMAX
-    if (a.logits) {
-      for (int e = tid; e < TS; e += 256) {
-        const int t = e / ROWS, nl = e % ROWS, n = n0 + nl;
-        if (t < a.row0 || t >= a.m || n >= a.n) continue;
-        a.logits[(size_t)(t - a.row0) * a.ldl + n] = tileT[t][nl] * scale_of(n);
-      }
-    }
-    if (tid < TOK) {
-      const int t = tid;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int t = mb * 16 + 4 * g + wave;
       float best = -INFINITY;
       int bi = 0x7fffffff;
-      for (int nl = 0; nl < ROWS; ++nl) {
-        const int n = n0 + nl;
-        if (n >= a.n) break;
-        const float y = tileT[t][nl] * scale_of(n);
-        if (y > best) { best = y; bi = n; }   // ascending n: first (lowest) index kept on ties
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        if (rt0 + r >= a.ntile16) continue;
+        const int n = (rt0 + r) * 16 + lr;
+        const float y = val[r][mb] * scale_of(n);
+        if (a.logits && t >= a.row0 && t < a.m) a.logits[(size_t)(t - a.row0) * a.ldl + n] = y;
+        if (y > best) { best = y; bi = n; }   // ascending n within the lane
       }
-      a.am_val[(size_t)blockIdx.x * 64 + t] = best;
-      a.am_idx[(size_t)blockIdx.x * 64 + t] = bi;
+      // across the 16 lanes of this token (rows differ by lane): lowest index on ties
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+      }
+      if (lr == 0) {
+        a.am_val[(size_t)blockIdx.x * 64 + t] = best;
+        a.am_idx[(size_t)blockIdx.x * 64 + t] = bi;
+      }
     }
   }
 }
@@ -424,10 +437,10 @@ void gemm_mfma_kernel(GemmArgs a) {
 // ------------------------------------------------------------------ fp32 path
 // Plain fp32 GEMM for fp32 models (the small sanity configuration): one
 // thread per output column, all token rows; weights in canonical [N][K].
+// EPI_PARTIAL writes the unrounded sums to out (one split).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ W, const float* __restrict__ X,
                                                        int ldx, int n, int k, int m, int epi, void* out,
-                                                       int ldo, void* side, int ld_side, int side_type,
-                                                       int side_col0, float* logits, int ldl) {
+                                                       int ldo, float* logits, int ldl) {
   const int col = blockIdx.x * blockDim.x + threadIdx.x;
   const int ncols = epi == EPI_SILU ? n / 2 : n;
   if (col >= ncols) return;
@@ -451,14 +464,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #pragma unroll
   for (int t = 0; t < MAX_ROWS; ++t) {
     if (t >= m) continue;
-    if (epi == EPI_STORE) {
+    if (epi == EPI_PARTIAL) {
       ((float*)out)[(size_t)t * ldo + col] = acc[t];
-    } else if (epi == EPI_RESID) {
-      float* o = (float*)out + (size_t)t * ldo + col;
-      const float nv = *o + acc[t];
-      *o = nv;
-      if (side)
-        store_act(side, act_index(t, side_col0 + col, ld_side, side_type == T_F32 ? 0 : ld_side), side_type, nv);
     } else if (epi == EPI_SILU) {
       const float gv = acc[t];
       ((float*)out)[(size_t)t * ldo + col] = gv / (1.0f + expf(-gv)) * acc2[t];
@@ -554,106 +561,127 @@ hipError_t launch_argmax_rows(const float* logits, int ld, int vocab, int row0, 
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ planning
-// R (row tiles per work-group) is the largest that still gives every CU at
-// least one work-group, bounded by the register budget R * MB <= 8 (4 for
-// int4, whose dequantisation needs the most registers);
-// gate/up launches need R even (tile pairs).
-struct Plan { int R, MB, nwg, ktiles, ntile16; };
+// Sum of the S fp32 partials of a PARTIAL launch into one fp32 matrix
+// (dflash_linear's plain output); fixed split order.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int S, size_t count,
+                                                        float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v = v + part[(size_t)s * count + i];
+    out[i] = v;
+  }
+}
 
-#ifndef DFL_GEMM_MIN_WGS
-#define DFL_GEMM_MIN_WGS 256
+hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((count + 255) / 256, 2048);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks), dim3(256), 0, s, part, S, count, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ planning
+// RT (row tiles per work-group) is 4, or 2 when 64 token rows make the
+// accumulators and activation fragments twice as large.  S (K splits) raises
+// the work-group count of narrow projections towards two per CU, keeping at
+// least one K tile per wave; non-linear epilogues take S = 1.
+#ifndef DFL_GEMM_TARGET_WGS
+#define DFL_GEMM_TARGET_WGS 512
+#endif
+#ifndef DFL_GEMM_MAX_SPLITS
+#define DFL_GEMM_MAX_SPLITS 8
 #endif
 
-static Plan make_plan(int fmt, int n, int k, int m, int gate_up) {
+Plan make_plan(int fmt, int n, int k, int m, int epi) {
   Plan p;
   p.MB = (m + 15) / 16;
   p.ntile16 = n / 16;
-  p.ktiles = k / tile_k(fmt);
-  const int budget = fmt == W_W4 ? 4 : 8;      // int4 dequant needs the most registers
-  int R = 8;
-  while (R > 1 && (R * p.MB > budget || (p.ntile16 + R - 1) / R < DFL_GEMM_MIN_WGS)) R /= 2;
-  if (gate_up && R < 2) R = 2;
-  p.R = R;
-  p.nwg = (p.ntile16 + R - 1) / R;
+  p.ktiles = fmt == W_F32 ? 0 : k / tile_k(fmt);
+  p.RT = p.MB >= 3 ? 2 : 4;
+  p.ngroups = (p.ntile16 + p.RT - 1) / p.RT;
+  p.S = 1;
+  if (fmt != W_F32 && epi == EPI_PARTIAL) {
+    int S = (DFL_GEMM_TARGET_WGS + p.ngroups - 1) / p.ngroups;
+    S = std::min(S, DFL_GEMM_MAX_SPLITS);
+    S = std::min(S, std::max(1, p.ktiles / 4));
+    p.S = std::max(S, 1);
+  }
+  p.nwg = p.ngroups * p.S;
   return p;
 }
 
-size_t gemm_ws_floats(int, int, int, int) { return 0; }
-
 int gemm_am_blocks(int fmt, int n, int m) {
   if (fmt == W_F32) return 0;
-  return make_plan(fmt, n, tile_k(fmt), m, 0).nwg;
+  return make_plan(fmt, n, tile_k(fmt), m, EPI_ARGMAX).nwg;
 }
 
-template <int FMT, int R>
+template <int FMT, int RT>
 static hipError_t dispatch_mb(int MB, dim3 grid, const GemmArgs& a, hipStream_t s) {
-  if (R * MB > (FMT == W_W4 ? 4 : 8)) return hipErrorInvalidValue;
-  if (FMT == W_W4 && R == 8) return hipErrorInvalidValue;
   switch (MB) {
-    case 1: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 4 ? 2 : 1)>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 2 ? 3 : 1)>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_mfma_kernel<FMT, R, (R <= 2 ? 4 : 1)>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 3>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 4>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <int FMT>
-static hipError_t dispatch_mfma(const Plan& p, const GemmArgs& a, hipStream_t s) {
+static hipError_t dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
   dim3 grid(p.nwg);
-  switch (p.R) {
-    case 8: return dispatch_mb<FMT, (FMT == W_W4 ? 4 : 8)>(p.MB, grid, a, s);
-    case 4: return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
-    case 2: return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
-    default: return dispatch_mb<FMT, 1>(p.MB, grid, a, s);
-  }
+  if (p.RT == 4) return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
+  return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
 }
 
 static const char* variant_name(int fmt, const Plan& p) {
-  static char names[4][4][9][24];
+  static char names[4][5][5][9][32];
   static bool init = false;
   if (!init) {
     const char* f[4] = {"f32", "bf16", "w8", "w4"};
     for (int i = 0; i < 4; ++i)
       for (int mb = 1; mb <= 4; ++mb)
-        for (int r = 1; r <= 8; ++r) snprintf(names[i][mb - 1][r], 24, "gemm_%s_r%dm%d", f[i], r, mb);
+        for (int rt = 1; rt <= 4; ++rt)
+          for (int sp = 1; sp <= 8; ++sp)
+            snprintf(names[i][mb][rt][sp], 32, "gemm_%s_t%dm%ds%d", f[i], rt, mb, sp);
     init = true;
   }
-  return names[fmt][p.MB - 1][p.R];
+  return names[fmt][p.MB][p.RT][p.S];
 }
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
-                       double* bytes) {
+                       double* bytes, int* splits) {
   const GemmW& W = *c.W;
   size_t wb, sb;
   packed_bytes(W.fmt, W.n, W.k, &wb, &sb);
   if (bytes) *bytes = (double)(wb + sb);
   if (W.fmt == W_F32) {
     if (variant) *variant = "gemm_f32";
+    if (splits) *splits = 1;
     const int ncols = c.epi == EPI_SILU ? W.n / 2 : W.n;
     float* lg = c.epi == EPI_ARGMAX ? w.logits_tmp : nullptr;
+    void* out = c.epi == EPI_PARTIAL ? (void*)c.part : c.out;
+    const int ldo = c.epi == EPI_PARTIAL ? W.n : W.n / 2;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((ncols + 255) / 256), dim3(256), 0, s, (const float*)W.w,
-                       (const float*)c.x, c.ldx, W.n, W.k, c.m, c.epi, c.out, c.ldo, c.side, c.ld_side,
-                       c.side_type, c.side_col0, lg, W.n);
+                       (const float*)c.x, c.ldx, W.n, W.k, c.m, c.epi, out, ldo, lg, W.n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
     return launch_argmax_rows(w.logits_tmp, W.n, W.n, c.row0, c.m - c.row0, c.am_out, c.logits, c.ldl, s);
   }
-  Plan p = make_plan(W.fmt, W.n, W.k, c.m, W.gate_up);
+  Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);
   if (variant) *variant = variant_name(W.fmt, p);
+  if (splits) *splits = p.S;
+  if (c.epi == EPI_PARTIAL && (size_t)p.S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
+  if (c.epi == EPI_ARGMAX && p.nwg > w.am_cap) return hipErrorInvalidValue;
   GemmArgs a;
-  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x; a.ldx = c.ldx;
-  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16;
-  a.m = c.m; a.epi = c.epi; a.out = c.out; a.ldo = c.ldo; a.otype = c.otype;
-  a.side = c.side; a.ld_side = c.ld_side; a.side_type = c.side_type; a.side_col0 = c.side_col0;
+  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
+  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16; a.m = c.m; a.splits = p.S;
+  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.logits = c.logits; a.ldl = c.ldl; a.row0 = c.row0;
   a.am_val = w.am_val; a.am_idx = w.am_idx;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   hipError_t e;
-  if (W.fmt == W_BF16) e = dispatch_mfma<W_BF16>(p, a, s);
-  else if (W.fmt == W_W8) e = dispatch_mfma<W_W8>(p, a, s);
-  else e = dispatch_mfma<W_W4>(p, a, s);
+  if (W.fmt == W_BF16) e = dispatch<W_BF16>(p, a, s);
+  else if (W.fmt == W_W8) e = dispatch<W_W8>(p, a, s);
+  else e = dispatch<W_W4>(p, a, s);
   if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
   return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
 }

@@ -4,80 +4,120 @@
 
 namespace dfl {
 
-// RMSNorm(z) = z * (mean(z^2) + eps)^-1/2 * g, one work-group per row.
-// Each thread owns whole 8-column chunks: one 16-byte load (bf16) or two
-// (fp32) per chunk, kept in registers between the reduction and the output,
-// and one 16-byte store per chunk (8 consecutive columns are contiguous in the
+// Residual update + RMSNorm(z) = z * (mean(z^2) + eps)^-1/2 * g, one
+// work-group per row.  The producing GEMM left fp32 partial sums of S K
+// ranges; they are added here in split order, rounded to the activation
+// format (the GEMM output's materialisation point), added to the residual
+// stream and rounded again, then normalised.  Each thread owns whole 8-column
+// chunks, kept in registers between the reduction and the output, and writes
+// one 16-byte store per chunk (8 consecutive columns are contiguous in the
 // tiled layout as well as in a row-major one).  h % 8 == 0, h <= 8192.
-constexpr int NORM_CHUNKS = 4;
-
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, int xtype, int ldx, void* out,
-                                                      int otype, int ldo, const float* __restrict__ gain, int h,
-                                                      float eps, int fmK) {
-  const int row = blockIdx.x;
-  const int nch = h >> 3;
-  float v[NORM_CHUNKS][8];
-  float ss = 0.f;
+__device__ __forceinline__ void load8_act(const void* p, size_t i, int t, float (&v)[8]) {
+  if (t == T_F32) {
+    const float4 a = *(const float4*)((const float*)p + i), b = *(const float4*)((const float*)p + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 q = *(const uint4*)((const uint16_t*)p + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int c = 0; c < NORM_CHUNKS; ++c) {
-    const int ch = threadIdx.x + 256 * c;
-    if (ch < nch) {
-      if (xtype == T_F32) {
-        const float4* p = (const float4*)((const float*)x + (size_t)row * ldx + ch * 8);
-        const float4 a = p[0], b = p[1];
-        v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
-        v[c][4] = b.x; v[c][5] = b.y; v[c][6] = b.z; v[c][7] = b.w;
-      } else {
-        const uint4 q = *(const uint4*)((const uint16_t*)x + (size_t)row * ldx + ch * 8);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
-    }
-  }
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float r = 1.0f / sqrtf(tot / (float)h + eps);
-#pragma unroll
-  for (int c = 0; c < NORM_CHUNKS; ++c) {
-    const int ch = threadIdx.x + 256 * c;
-    if (ch >= nch) continue;
-    const int j0 = ch * 8;
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = v[c][e] * r * gain[j0 + e];
-    const size_t o = fmK ? fm_index(row, j0, fmK) : (size_t)row * ldo + j0;
-    if (otype == T_F32) {
-      float4* p = (float4*)((float*)out + o);
-      p[0] = float4{y[0], y[1], y[2], y[3]};
-      p[1] = float4{y[4], y[5], y[6], y[7]};
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
-        if (otype == T_F16) {
-          lo = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(lo));
-          hi = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(hi));
-        }
-        w[e] = lo | (hi << 16);
-      }
-      *(uint4*)((uint16_t*)out + o) = uint4{w[0], w[1], w[2], w[3]};
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      v[e] = t == T_BF16 ? bf16_bits_to_f32(h) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
     }
   }
 }
 
-hipError_t launch_rmsnorm(const void* x, int xtype, int ldx, void* out, int otype, int ldo, const float* gain,
-                          int rows, int h, float eps, hipStream_t s, int tiled) {
-  if (rows <= 0) return hipSuccess;
-  if (h % 8 || h > 8 * 256 * NORM_CHUNKS) return hipErrorInvalidValue;
-  const int fmK = (tiled && otype != T_F32) ? h : 0;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, xtype, ldx, out, otype, ldo, gain, h, eps, fmK);
+__device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float (&y)[8]) {
+  if (t == T_F32) {
+    float4* q = (float4*)((float*)p + i);
+    q[0] = float4{y[0], y[1], y[2], y[3]};
+    q[1] = float4{y[4], y[5], y[6], y[7]};
+    return;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
+    if (t == T_F16) {
+      lo = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(lo));
+      hi = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(hi));
+    }
+    w[e] = lo | (hi << 16);
+  }
+  *(uint4*)((uint16_t*)p + i) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+// one thread per 8-column chunk (blockDim = h/8 rounded up to a wave, <= 1024)
+__global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
+  const int row = blockIdx.x;
+  const int nch = c.h >> 3;
+  const int ch = threadIdx.x;
+  const bool live = ch < nch;
+  const int j0 = live ? ch * 8 : 0;
+  const int rt = c.xtype;                       // activation (rounding) type of the stack
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  if (live) {
+    if (c.mode != NORM_PROJ) load8_act(c.x, (size_t)row * c.ldx + j0, c.xtype, v);
+    if (c.mode != NORM_ONLY) {
+      // every split's 8 values are loaded before any is added
+      float4 pa[MAX_SPLITS], pb[MAX_SPLITS];
+      const float* q = c.in.p + (size_t)row * c.in.ld + j0;
+#pragma unroll
+      for (int s = 0; s < MAX_SPLITS; ++s) {
+        if (s < c.in.S) {
+          pa[s] = *(const float4*)(q + (size_t)s * c.in.stride);
+          pb[s] = *(const float4*)(q + (size_t)s * c.in.stride + 4);
+        }
+      }
+      float y[8] = {pa[0].x, pa[0].y, pa[0].z, pa[0].w, pb[0].x, pb[0].y, pb[0].z, pb[0].w};
+#pragma unroll
+      for (int s = 1; s < MAX_SPLITS; ++s) {
+        if (s < c.in.S) {
+          y[0] = y[0] + pa[s].x; y[1] = y[1] + pa[s].y; y[2] = y[2] + pa[s].z; y[3] = y[3] + pa[s].w;
+          y[4] = y[4] + pb[s].x; y[5] = y[5] + pb[s].y; y[6] = y[6] + pb[s].z; y[7] = y[7] + pb[s].w;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = c.mode == NORM_RESID ? act_round(rt, v[e] + act_round(rt, y[e])) : act_round(rt, y[e]);
+      if (c.mode == NORM_RESID) {
+        store8_act(c.x, (size_t)row * c.ldx + j0, c.xtype, v);
+        if (c.side) {
+          const int col = c.side_col0 + j0;
+          const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
+          store8_act(c.side, o, c.side_type, v);
+        }
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  ss = wave_sum(ss);
+  __shared__ float part[16];
+  const int nw = (blockDim.x + 63) >> 6;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  // fixed-order sum of the wave partials
+  float tot = part[0];
+  for (int w = 1; w < nw; ++w) tot = tot + part[w];
+  const float r = 1.0f / sqrtf(tot / (float)c.h + c.eps);
+  if (!live) return;
+  const int fmK = (c.tiled && c.otype != T_F32) ? c.h : 0;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = v[e] * r * c.gain[j0 + e];
+  const size_t o = fmK ? fm_index(row, j0, fmK) : (size_t)row * c.ldo + j0;
+  store8_act(c.out, o, c.otype, y);
+}
+
+hipError_t launch_norm(const NormCall& c, hipStream_t s) {
+  if (c.rows <= 0) return hipSuccess;
+  if (c.h % 8 || c.h > 8 * 1024 || c.in.S > MAX_SPLITS) return hipErrorInvalidValue;
+  const int threads = ((c.h / 8 + 63) / 64) * 64;
+  hipLaunchKernelGGL(norm_kernel, dim3(c.rows), dim3(threads), 0, s, c);
   return hipGetLastError();
 }
 
