@@ -173,92 +173,87 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   if (!live) return;
 
-  // 2. two halves of 128 keys with an online max: tile kt holds keys
-  //    16kt + 4g + v of row lr
-  constexpr int NT = 8;                      // 16-key tiles per half
-  float mrow = -INFINITY, lsum = 0.f;
+  // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr),
+  //    row max, then exp2 and P*V in one pass.  Splits that end at or before
+  //    n are visible to every row (the whole committed context), so only the
+  //    split holding the block needs the mask.
+  constexpr int NT = ATTN_SPLIT / 16;
+  const bool full = key0 + ATTN_SPLIT <= n;    // uniform
+  float sv[NT][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    const int p = kt >> 2, key = (kt & 3) * 16 + lr;
+    const uint8_t* kpage = lds + (size_t)(p * 2) * 16384 + (size_t)key * 256;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = (4 * ks + g) ^ (key & 15);
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[kt][v] = acc[v] * a.scale2;
+  }
+  if (!full) {
+    const int kmax = a.causal ? n + tok : kv_len - 1;       // last key this row sees
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (key0 + kt * 16 + 4 * g + v > kmax) sv[kt][v] = -INFINITY;
+  }
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(sv[kt][0], sv[kt][1]), fmaxf(sv[kt][2], sv[kt][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // masked scores are -inf, so exp2(x - mref) is 0 for them; a row with no
+  // visible key in this split subtracts 0 instead of -inf (no NaN) and runs
+  // the wave-wide MFMAs with p = 0
+  const float mref = mx == -INFINITY ? 0.f : mx;
+  float lsum = 0.f;
   floatx4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int hf = 0; hf < 2; ++hf) {
-    float sv[NT][4];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if ((t & 1) == 0) __builtin_amdgcn_sched_barrier(0);   // bound the K-fragment reads in flight
-      const int kt = hf * NT + t;
-      const int p = kt >> 2, key = (kt & 3) * 16 + lr;
-      const uint8_t* kpage = lds + (size_t)(p * 2) * 16384 + (size_t)key * 256;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
+    // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v.
+    // p = hi + lo: hi keeps the top 16 bits of p (a bf16 by truncation),
+    // lo = p - hi (exact) rounded to bf16, so hi + lo carries 16 bits of p.
+    uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c = (4 * ks + g) ^ (key & 15);
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
-      }
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t hb[4], lb[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kpos = key0 + kt * 16 + 4 * g + v;
-        const bool vis = kpos < kv_len && (!a.causal || kpos <= n + tok);
-        sv[t][v] = vis ? acc[v] * a.scale2 : -INFINITY;
-        mx = fmaxf(mx, sv[t][v]);
+        const float pe = __builtin_amdgcn_exp2f(sv[2 * ks2 + hh][v] - mref);
+        lsum += pe;
+        const uint32_t u = __float_as_uint(pe);
+        const float hv = __uint_as_float(u & 0xffff0000u);
+        const uint32_t lu = __float_as_uint(pe - hv);
+        hb[v] = u;
+        lb[v] = lu + 0x7fffu + ((lu >> 16) & 1u);
       }
+      ph[2 * hh] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+      ph[2 * hh + 1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
+      pl[2 * hh] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
+      pl[2 * hh + 1] = __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // No per-row branching: the MFMAs are wave-wide, so a row whose keys are
-    // all masked so far (dead) runs them too, with p = 0 and alpha = 1.
-    const float mnew = fmaxf(mrow, mx);
-    const bool dead = mnew == -INFINITY;
-    const float alpha = dead ? 1.f : (mrow == -INFINITY ? 0.f : exp2f(mrow - mnew));
-    mrow = mnew;
-    // masked scores are -inf, so exp2(x - mref) is 0 for them; a dead row
-    // subtracts 0 instead of -inf (no NaN)
-    const float mref = dead ? 0.f : mnew;
-    lsum *= alpha;
+    const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+    const int p = ks2 >> 1;
+    const uint8_t* vpage = lds + (size_t)(p * 2 + 1) * 16384;
+    const int c0 = 4 * (ks2 & 1) + (g >> 1), half = (g & 1) * 8;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-#pragma unroll
-    for (int k2 = 0; k2 < NT / 2; ++k2) {
-      // one 32-key step at a time: keeps the scheduler from hoisting every
-      // V fragment read (and its registers) to the top of the loop
-      __builtin_amdgcn_sched_barrier(0);
-      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float hv[4], lv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float pe = exp2f(sv[2 * k2 + hh][v] - mref);
-          hv[v] = round_bf16_finite(pe);
-          lv[v] = round_bf16_finite(pe - hv[v]);
-          lsum += pe;
-        }
-        ph[2 * hh] = bf16_pair(hv[0], hv[1]);
-        ph[2 * hh + 1] = bf16_pair(hv[2], hv[3]);
-        pl[2 * hh] = bf16_pair(lv[0], lv[1]);
-        pl[2 * hh + 1] = bf16_pair(lv[2], lv[3]);
-      }
-      const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
-      const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
-      const int ks2 = hf * (NT / 2) + k2;
-      const int p = ks2 >> 1;
-      const uint8_t* vpage = lds + (size_t)(p * 2 + 1) * 16384;
-      const int c0 = 4 * (ks2 & 1) + (g >> 1), half = (g & 1) * 8;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d = dt * 16 + lr, sw = (d >> 1) & 7;
-        const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + half);
-        const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + half);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = dt * 16 + lr, sw = (d >> 1) & 7;
+      const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + half);
+      const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + half);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
     }
   }
-  const float mx = mrow;
 
   // 3. partials: o (unnormalised), m (log2 domain) and l per query row
   lsum += __shfl_xor(lsum, 16, 64);

@@ -119,11 +119,15 @@ struct Workspace {
   float* logits_tmp;                        // F32 path: [64][V] logits scratch
 };
 
-struct Plan { int RT, MB, S, ngroups, nwg, ktiles, ntile16; };
+// RT row tiles per chunk, MB 16-token blocks, S K splits, PR work-groups per
+// split (nwg = PR * S), align = row tiles per balancing unit (2 for gate/up)
+struct Plan { int RT, MB, S, PR, ngroups, nwg, ktiles, ntile16, align; };
 Plan make_plan(int fmt, int n, int k, int m, int epi);
+struct Workspace;
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
                        double* bytes, int* splits);
+hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p);
 hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, const void* src_scales,
                        void* dst, void* dst_scales, hipStream_t s);
 hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, hipStream_t s);

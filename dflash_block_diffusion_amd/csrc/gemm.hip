@@ -189,24 +189,24 @@ __device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi, uint32_t magic
 // ------------------------------------------------------------------ kernel
 struct GemmArgs {
   const uint8_t* w; const uint16_t* s; const uint16_t* x;
-  int n, k, ktiles, ntile16, m, splits;
+  int n, k, ktiles, ntile16, m, splits, align;
   int epi;
   float* part;                               // EPI_PARTIAL: [splits][m][n] fp32
   void* out; int otype;                      // EPI_SILU: tiled [m][n/2] (K = n/2)
   float* logits; int ldl; int row0;          // EPI_ARGMAX
-  float* am_val; int* am_idx;
+  float* am_val; int* am_idx;                // EPI_ARGMAX: one (value, index) per work-group and token
   // dequant bit masks, passed as arguments so that they live in registers
   // (gfx9 VOP3 encodings take no literal constants)
   uint32_t mlo, mhi, magic;
 };
 
 // registers of one ring stage (one K tile of all RT row tiles + its
-// activation fragments) and the ring depth that fits ~170 VGPRs
+// activation fragments) and the ring depth that fits ~140 VGPRs
 __host__ __device__ constexpr int stage_regs(int fmt, int rt, int mb) {
   return 4 * rt + (fmt == W_W4 ? rt : 0) + 4 * mb * (tile_k(fmt) / 32);
 }
 __host__ __device__ constexpr int ring_depth(int fmt, int rt, int mb) {
-  return 170 / stage_regs(fmt, rt, mb) < 2 ? 2 : (170 / stage_regs(fmt, rt, mb) > 8 ? 8 : 170 / stage_regs(fmt, rt, mb));
+  return 140 / stage_regs(fmt, rt, mb) < 2 ? 2 : (140 / stage_regs(fmt, rt, mb) > 8 ? 8 : 140 / stage_regs(fmt, rt, mb));
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -224,6 +224,13 @@ struct Stage {
   uint4 x[MB][tile_k(FMT) / 32];
 };
 
+// Persistent streaming GEMM.  Work-group w serves K split s = w % S and a
+// contiguous, balanced range of row tiles (in units of `align` tiles, 2 for
+// fused gate/up); it walks that range in chunks of RT row tiles.  Each wave
+// takes a quarter of the split's K tiles and streams the flattened sequence
+// (chunk, K tile) through a ring of U register stages: loads of the next
+// chunk are in flight while the previous chunk's four wave partials are
+// added in LDS (fixed order) and written out.
 template <int FMT, int RT, int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_stream_kernel(GemmArgs a) {
@@ -237,12 +244,18 @@ void gemm_stream_kernel(GemmArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int S = a.splits;
-  const int sidx = blockIdx.x % S, rg = blockIdx.x / S;
+  const int sidx = blockIdx.x % S, wr = blockIdx.x / S, PR = gridDim.x / S;
+  // row tiles [rtb, rte) of this work-group
+  const int units = a.ntile16 / a.align;
+  const int rtb = (int)((long long)units * wr / PR) * a.align;
+  const int rte = (int)((long long)units * (wr + 1) / PR) * a.align;
+  const int nch = (rte - rtb + RT - 1) / RT;
+  // K tiles [t0, t1) of this wave
   const int kt0 = (int)((long long)a.ktiles * sidx / S);
   const int kt1 = (int)((long long)a.ktiles * (sidx + 1) / S);
   const int nk = kt1 - kt0;
   const int t0 = kt0 + nk * wave / 4, t1 = kt0 + nk * (wave + 1) / 4;
-  const int rt0 = rg * RT;
+  const int nt = t1 - t0;
   const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
 
   floatx4 acc[RT][MB];
@@ -256,21 +269,16 @@ void gemm_stream_kernel(GemmArgs a) {
   const uint16_t* xrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) xrow[mb] = a.x + (size_t)mb * (a.k >> 5) * 512 + lane * 8;
-  const uint8_t* wbase[RT];
-  const uint32_t* sbase[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int rt = rt0 + r;
-    const int rtc = rt < a.ntile16 ? rt : a.ntile16 - 1;   // dead tiles re-read a valid one
-    wbase[r] = a.w + (size_t)rtc * a.ktiles * 1024 + lane * 16;
-    sbase[r] = (FMT == W_W4) ? (const uint32_t*)a.s + (size_t)rtc * a.ktiles * 16 + lr : nullptr;
-  }
+  const uint8_t* wlane = a.w + lane * 16;
+  const uint32_t* slane = (FMT == W_W4) ? (const uint32_t*)a.s + lr : nullptr;
 
-  auto load = [&](int t, Stage<FMT, RT, MB>& f) {
+  // stage (chunk c, K tile t); row tiles past the range re-read the last one
+  auto load = [&](int c, int t, Stage<FMT, RT, MB>& f) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      f.w[r] = load_stream(wbase[r] + (size_t)t * 1024);
-      if (FMT == W_W4) f.s[r] = sbase[r][(size_t)t * 16];
+      const int rt = min(rtb + c * RT + r, rte - 1);
+      f.w[r] = load_stream(wlane + ((size_t)rt * a.ktiles + t) * 1024);
+      if (FMT == W_W4) f.s[r] = slane[((size_t)rt * a.ktiles + t) * 16];
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -319,115 +327,138 @@ void gemm_stream_kernel(GemmArgs a) {
     }
   };
 
-  const int nt = t1 - t0;
-  if (nt > 0 && nt <= U) {
-    // the wave's whole K range fits the ring: issue every load, then multiply
-    Stage<FMT, RT, MB> ring[U];
+  // running argmax of this thread's tokens over every chunk
+  float best[MB];
+  int bidx[MB];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (u < nt) load(t0 + u, ring[u]);
+  for (int mb = 0; mb < MB; ++mb) { best[mb] = -INFINITY; bidx[mb] = 0x7fffffff; }
+  const uint16_t* sc8 = (FMT == W_W8) ? a.s : nullptr;
+  auto scale_of = [&](int n) -> float {
+    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : 1.0f;
+  };
+
+  // Chunk epilogue: fixed-order reduction of the 4 wave partials,
+  // ((w0 + w1) + w2) + w3; thread (wave w, lane) finishes accumulator slot
+  // v = w of every (r, mb): token mb*16 + 4g + w, weight row (rt0 + r)*16 + lr.
+  auto epilogue = [&](int c) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (u < nt) compute(ring[u]);
-  } else if (nt > U) {
-    // Operands stream through a ring of U register stages: U K tiles of loads
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          red[wave][(r * MB + mb) * 4 + v][lane] = acc[r][mb][v];
+          acc[r][mb][v] = 0.f;
+        }
+    __syncthreads();
+    const int rt0 = rtb + c * RT;
+    float val[RT][MB];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int j = (r * MB + mb) * 4 + wave;
+        val[r][mb] = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+      }
+    __syncthreads();      // red is rewritten by the next chunk
+    if (a.epi == EPI_PARTIAL) {
+      float* part = a.part + (size_t)sidx * a.m * a.n;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        if (rt0 + r >= rte) continue;
+        const int n = (rt0 + r) * 16 + lr;
+        const float sc = scale_of(n);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int t = mb * 16 + 4 * g + wave;
+          if (t < a.m) part[(size_t)t * a.n + n] = val[r][mb] * sc;
+        }
+      }
+    } else if (a.epi == EPI_SILU) {
+      const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
+      const int half_n = a.n >> 1;
+#pragma unroll
+      for (int p = 0; p < RT / 2; ++p) {
+        if (rt0 + 2 * p + 1 >= rte) continue;
+        const int ng = (rt0 + 2 * p) * 16 + lr, nu = ng + 16;
+        const int n_out = ((rt0 >> 1) + p) * 16 + lr;
+        const float sg = scale_of(ng), su = scale_of(nu);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int t = mb * 16 + 4 * g + wave;
+          if (t >= a.m) continue;
+          const float gv = act_round(rnd, val[2 * p][mb] * sg);
+          const float uv = act_round(rnd, val[2 * p + 1][mb] * su);
+          const float sv = gv / (1.0f + expf(-gv));
+          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
+        }
+      }
+    } else {  // EPI_ARGMAX: ascending n within the lane keeps the lowest index on ties
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int t = mb * 16 + 4 * g + wave;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          if (rt0 + r >= rte) continue;
+          const int n = (rt0 + r) * 16 + lr;
+          const float y = val[r][mb] * scale_of(n);
+          if (a.logits && t >= a.row0 && t < a.m) a.logits[(size_t)(t - a.row0) * a.ldl + n] = y;
+          if (y > best[mb]) { best[mb] = y; bidx[mb] = n; }
+        }
+      }
+    }
+  };
+
+  if (nt == 0) {
+    // fewer K tiles than waves: this wave only joins the reductions
+    for (int c = 0; c < nch; ++c) epilogue(c);
+  } else {
+    // Operands stream through a ring of U register stages: U stages of loads
     // are in flight per wave while the oldest is multiplied.  Loads are
-    // unconditional (the last round re-reads a clamped valid tile) so the
+    // unconditional (past the end they re-read the last stage) so the
     // compiler waits for one stage at a time instead of draining the ring.
+    const int Q = nch * nt;
     Stage<FMT, RT, MB> ring[U];
+    int pc = 0, pt = t0;                       // next stage to load
+    auto advance = [&](int& c, int& t) {
+      if (t + 1 < t1) { ++t; } else if (c + 1 < nch) { ++c; t = t0; }
+    };
 #pragma unroll
-    for (int u = 0; u < U; ++u) load(t0 + u, ring[u]);
+    for (int u = 0; u < U; ++u) { load(pc, pt, ring[u]); advance(pc, pt); }
     // keep the scheduler from sinking loads next to their uses (it would
     // trade the in-flight depth for registers)
     __builtin_amdgcn_sched_barrier(0);
-    for (int base = t0; base < t1; base += U) {
+    int cc = 0, ct = t0;                       // stage being multiplied
+    for (int q = 0; q < Q; q += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (base + u < t1) compute(ring[u]);
-        load(min(base + U + u, t1 - 1), ring[u]);
+        if (q + u < Q) {
+          compute(ring[u]);
+          if (ct == t1 - 1) epilogue(cc);
+          advance(cc, ct);
+        }
+        load(pc, pt, ring[u]);
+        advance(pc, pt);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // ---- fixed-order reduction of the 4 wave partials: ((w0 + w1) + w2) + w3
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][(r * MB + mb) * 4 + v][lane] = acc[r][mb][v];
-  __syncthreads();
-  // thread (wave w, lane) finishes accumulator slot v = w of every (r, mb):
-  // token mb*16 + 4g + w, weight row (rt0 + r)*16 + lr
-  float val[RT][MB];
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
+  if (a.epi == EPI_ARGMAX) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int j = (r * MB + mb) * 4 + wave;
-      val[r][mb] = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
-    }
-
-  const uint16_t* sc8 = (FMT == W_W8) ? a.s : nullptr;
-  auto scale_of = [&](int n) -> float {
-    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : 1.0f;
-  };
-  if (a.epi == EPI_PARTIAL) {
-    float* part = a.part + (size_t)sidx * a.m * a.n;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (rt0 + r >= a.ntile16) continue;
-      const int n = (rt0 + r) * 16 + lr;
-      const float sc = scale_of(n);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int t = mb * 16 + 4 * g + wave;
-        if (t < a.m) part[(size_t)t * a.n + n] = val[r][mb] * sc;
-      }
-    }
-  } else if (a.epi == EPI_SILU) {
-    const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
-    const int half_n = a.n >> 1;
-#pragma unroll
-    for (int p = 0; p < RT / 2; ++p) {
-      if (rt0 + 2 * p + 1 >= a.ntile16) continue;
-      const int ng = (rt0 + 2 * p) * 16 + lr, nu = ng + 16;
-      const int n_out = ((rt0 >> 1) + p) * 16 + lr;
-      const float sg = scale_of(ng), su = scale_of(nu);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int t = mb * 16 + 4 * g + wave;
-        if (t >= a.m) continue;
-        const float gv = act_round(rnd, val[2 * p][mb] * sg);
-        const float uv = act_round(rnd, val[2 * p + 1][mb] * su);
-        const float sv = gv / (1.0f + expf(-gv));
-        store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
-      }
-    }
-  } else {  // EPI_ARGMAX
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int t = mb * 16 + 4 * g + wave;
-      float best = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        if (rt0 + r >= a.ntile16) continue;
-        const int n = (rt0 + r) * 16 + lr;
-        const float y = val[r][mb] * scale_of(n);
-        if (a.logits && t >= a.row0 && t < a.m) a.logits[(size_t)(t - a.row0) * a.ldl + n] = y;
-        if (y > best) { best = y; bi = n; }   // ascending n within the lane
-      }
+      float bv = best[mb];
+      int bi = bidx[mb];
       // across the 16 lanes of this token (rows differ by lane): lowest index on ties
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(best, o, 64);
+        const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
+      const int t = mb * 16 + 4 * g + wave;
       if (lr == 0) {
-        a.am_val[(size_t)blockIdx.x * 64 + t] = best;
+        a.am_val[(size_t)blockIdx.x * 64 + t] = bv;
         a.am_idx[(size_t)blockIdx.x * 64 + t] = bi;
       }
     }
@@ -580,32 +611,40 @@ hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, 
 }
 
 // ------------------------------------------------------------------ planning
-// RT (row tiles per work-group) is 4, or 2 when 64 token rows make the
-// accumulators and activation fragments twice as large.  S (K splits) raises
-// the work-group count of narrow projections towards two per CU, keeping at
-// least one K tile per wave; non-linear epilogues take S = 1.
-#ifndef DFL_GEMM_TARGET_WGS
-#define DFL_GEMM_TARGET_WGS 512
-#endif
-#ifndef DFL_GEMM_MAX_SPLITS
-#define DFL_GEMM_MAX_SPLITS 8
-#endif
-
+// RT (row tiles per chunk) is 4, or 2 when 64 token rows make the
+// accumulators and activation fragments twice as large.  The launch has
+// nwg = PR * S work-groups: S K splits (PARTIAL epilogue only) times PR
+// work-groups per split, each owning a balanced range of row tiles.  Chosen
+// from a sweep of (PR, S) on MI355X over the 8B-class shapes (weights
+// rotated through more than the 256 MiB last-level cache):
+//   * narrow projections (partial sums): one work-group per CU, S = 256 /
+//     chunks rounded down, at most 4 and at most one K tile per wave;
+//   * wide gate/up and lm-head launches: two work-groups per CU (one for
+//     int8 gate/up, whose dequantisation is cheap and activation reads
+//     dominate).
 Plan make_plan(int fmt, int n, int k, int m, int epi) {
   Plan p;
   p.MB = (m + 15) / 16;
   p.ntile16 = n / 16;
   p.ktiles = fmt == W_F32 ? 0 : k / tile_k(fmt);
   p.RT = p.MB >= 3 ? 2 : 4;
-  p.ngroups = (p.ntile16 + p.RT - 1) / p.RT;
+  p.align = epi == EPI_SILU ? 2 : 1;
+  const int units = std::max(1, p.ntile16 / p.align);
   p.S = 1;
-  if (fmt != W_F32 && epi == EPI_PARTIAL) {
-    int S = (DFL_GEMM_TARGET_WGS + p.ngroups - 1) / p.ngroups;
-    S = std::min(S, DFL_GEMM_MAX_SPLITS);
+  if (epi == EPI_PARTIAL) {
+    const int chunks = std::max(1, p.ntile16 / p.RT);
+    int S = std::max(1, 256 / chunks);
+    S = std::min(S, 4);
     S = std::min(S, std::max(1, p.ktiles / 4));
-    p.S = std::max(S, 1);
+    p.S = S;
+    p.PR = std::min(units, (256 + S - 1) / S);
+  } else if (epi == EPI_SILU) {
+    p.PR = std::min(units, fmt == W_W8 ? 256 : 512);
+  } else {
+    p.PR = std::min(units, 512);
   }
-  p.nwg = p.ngroups * p.S;
+  p.nwg = p.PR * p.S;
+  p.ngroups = p.PR;
   return p;
 }
 
@@ -647,6 +686,27 @@ static const char* variant_name(int fmt, const Plan& p) {
   return names[fmt][p.MB][p.RT][p.S];
 }
 
+hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p) {
+  const GemmW& W = *c.W;
+  if (p.S < 1 || p.S > MAX_SPLITS || p.PR < 1 || p.nwg != p.PR * p.S) return hipErrorInvalidValue;
+  if (c.epi == EPI_PARTIAL && (size_t)p.S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
+  if (c.epi != EPI_PARTIAL && p.S != 1) return hipErrorInvalidValue;
+  if (c.epi == EPI_ARGMAX && p.nwg > w.am_cap) return hipErrorInvalidValue;
+  GemmArgs a;
+  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
+  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16; a.m = c.m; a.splits = p.S; a.align = p.align;
+  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
+  a.logits = c.logits; a.ldl = c.ldl; a.row0 = c.row0;
+  a.am_val = w.am_val; a.am_idx = w.am_idx;
+  a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
+  hipError_t e;
+  if (W.fmt == W_BF16) e = dispatch<W_BF16>(p, a, s);
+  else if (W.fmt == W_W8) e = dispatch<W_W8>(p, a, s);
+  else e = dispatch<W_W4>(p, a, s);
+  if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
+  return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
+}
+
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
                        double* bytes, int* splits) {
   const GemmW& W = *c.W;
@@ -666,24 +726,10 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
     if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
     return launch_argmax_rows(w.logits_tmp, W.n, W.n, c.row0, c.m - c.row0, c.am_out, c.logits, c.ldl, s);
   }
-  Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);
+  const Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);
   if (variant) *variant = variant_name(W.fmt, p);
   if (splits) *splits = p.S;
-  if (c.epi == EPI_PARTIAL && (size_t)p.S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
-  if (c.epi == EPI_ARGMAX && p.nwg > w.am_cap) return hipErrorInvalidValue;
-  GemmArgs a;
-  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
-  a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16; a.m = c.m; a.splits = p.S;
-  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
-  a.logits = c.logits; a.ldl = c.ldl; a.row0 = c.row0;
-  a.am_val = w.am_val; a.am_idx = w.am_idx;
-  a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
-  hipError_t e;
-  if (W.fmt == W_BF16) e = dispatch<W_BF16>(p, a, s);
-  else if (W.fmt == W_W8) e = dispatch<W_W8>(p, a, s);
-  else e = dispatch<W_W4>(p, a, s);
-  if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
-  return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
+  return launch_gemm_plan(c, w, s, p);
 }
 
 }  // namespace dfl
