@@ -158,6 +158,13 @@ hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, cons
 // --------------------------------------------------------------- dequant
 __device__ __forceinline__ half2v h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
+// (a & m) | c in one VALU op (the compiler splits it into two)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
 // 8 int4 codes (one dword, offset binary, nibble slots as packed) -> 8 halves
 // 0x6400 | u is the fp16 value 1024 + u; (0x6400 | 16u) scaled by 1/16 is 64 + u.
 // mlo = 0x000F000F, mhi = 0x00F000F0, magic = 0x64006400 (register operands).
@@ -166,10 +173,10 @@ __device__ __forceinline__ half8 deq_w4(uint32_t w, uint32_t mlo, uint32_t mhi, 
   const half2v s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2v c1 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t w2 = w >> 8;
-  half2v a = h2((w & mlo) | magic) + c0;
-  half2v b = h2((w & mhi) | magic) * s16 + c1;
-  half2v c = h2((w2 & mlo) | magic) + c0;
-  half2v d = h2((w2 & mhi) | magic) * s16 + c1;
+  half2v a = h2(and_or(w, mlo, magic)) + c0;
+  half2v b = h2(and_or(w, mhi, magic)) * s16 + c1;
+  half2v c = h2(and_or(w2, mlo, magic)) + c0;
+  half2v d = h2(and_or(w2, mhi, magic)) * s16 + c1;
   half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   return r;
 }
@@ -241,7 +248,10 @@ void gemm_stream_kernel(GemmArgs a) {
   __shared__ float red[4][NE][64];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave index as a scalar: every per-wave index and stage address below is
+  // then computed on the scalar unit, and loads take an SGPR base plus the
+  // lane's offset
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
   const int S = a.splits;
   const int sidx = blockIdx.x % S, wr = blockIdx.x / S, PR = gridDim.x / S;
