@@ -621,35 +621,46 @@ hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, 
 }
 
 // ------------------------------------------------------------------ planning
-// RT (row tiles per chunk) is 4, or 2 when 64 token rows make the
-// accumulators and activation fragments twice as large.  The launch has
-// nwg = PR * S work-groups: S K splits (PARTIAL epilogue only) times PR
-// work-groups per split, each owning a balanced range of row tiles.  Chosen
-// from a sweep of (PR, S) on MI355X over the 8B-class shapes (weights
-// rotated through more than the 256 MiB last-level cache):
-//   * narrow projections (partial sums): one work-group per CU, S = 256 /
-//     chunks rounded down, at most 4 and at most one K tile per wave;
-//   * wide gate/up and lm-head launches: two work-groups per CU (one for
-//     int8 gate/up, whose dequantisation is cheap and activation reads
-//     dominate).
+// The launch has nwg = PR * S work-groups: S K splits (partial-sum epilogue
+// only) times PR work-groups per split, each owning a balanced range of row
+// tiles that it walks in chunks of RT.  The rule below was fitted to a sweep
+// of (RT, S, PR) on MI355X over the 4B/8B/27B-class shapes (weights rotated
+// through more than the 256 MiB last-level cache) and lands within 2 % of the
+// per-shape optimum summed over the shapes:
+//   * RT = 2 for 64 token rows (register budget) and for bf16 partial sums,
+//     6 for the fused gate/up (SiLU), 4 otherwise;
+//   * gate/up: one work-group per CU, two when a CU would get more than one
+//     chunk; lm-head: two per CU;
+//   * partial sums: at most one work-group per CU; S in 1..4 minimises the
+//     streamed tile slots per work-group (whole chunks, including the dead
+//     row tiles of a partial chunk, times K tiles per wave) plus a small cost
+//     per split for writing and re-reading the partials.
 Plan make_plan(int fmt, int n, int k, int m, int epi) {
   Plan p;
   p.MB = (m + 15) / 16;
   p.ntile16 = n / 16;
   p.ktiles = fmt == W_F32 ? 0 : k / tile_k(fmt);
-  p.RT = p.MB >= 3 ? 2 : 4;
+  if (p.MB >= 3) p.RT = 2;
+  else if (epi == EPI_SILU) p.RT = 6;
+  else if (epi == EPI_ARGMAX) p.RT = 4;
+  else p.RT = fmt == W_BF16 ? 2 : 4;
   p.align = epi == EPI_SILU ? 2 : 1;
   const int units = std::max(1, p.ntile16 / p.align);
   p.S = 1;
   if (epi == EPI_PARTIAL) {
-    const int chunks = std::max(1, p.ntile16 / p.RT);
-    int S = std::max(1, 256 / chunks);
-    S = std::min(S, 4);
-    S = std::min(S, std::max(1, p.ktiles / 4));
-    p.S = S;
-    p.PR = std::min(units, (256 + S - 1) / S);
+    double best = 1e30;
+    for (int S = 1; S <= 4; ++S) {
+      if (S > 1 && p.ktiles / S < 4) continue;
+      const int PR = std::max(1, std::min(units, 256 / S));
+      const int tiles = (p.ntile16 + PR - 1) / PR;
+      const int chunks = (tiles + p.RT - 1) / p.RT;
+      const int kw = (p.ktiles + 4 * S - 1) / (4 * S);
+      const double cost = (double)chunks * p.RT * kw + 0.15 * S * p.RT;
+      if (cost < best - 1e-9) { best = cost; p.S = S; p.PR = PR; }
+    }
   } else if (epi == EPI_SILU) {
-    p.PR = std::min(units, fmt == W_W8 ? 256 : 512);
+    const int tiles256 = (p.ntile16 + 255) / 256;
+    p.PR = std::min(units, tiles256 > p.RT ? 512 : 256);
   } else {
     p.PR = std::min(units, 512);
   }
@@ -677,18 +688,23 @@ static hipError_t dispatch_mb(int MB, dim3 grid, const GemmArgs& a, hipStream_t 
 template <int FMT>
 static hipError_t dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
   dim3 grid(p.nwg);
-  if (p.RT == 4) return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
-  return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+  if (p.MB >= 3) return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+  switch (p.RT) {
+    case 8: return dispatch_mb<FMT, 8>(p.MB, grid, a, s);
+    case 6: return dispatch_mb<FMT, 6>(p.MB, grid, a, s);
+    case 4: return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
+    default: return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+  }
 }
 
 static const char* variant_name(int fmt, const Plan& p) {
-  static char names[4][5][5][9][32];
+  static char names[4][5][9][9][32];
   static bool init = false;
   if (!init) {
     const char* f[4] = {"f32", "bf16", "w8", "w4"};
     for (int i = 0; i < 4; ++i)
       for (int mb = 1; mb <= 4; ++mb)
-        for (int rt = 1; rt <= 4; ++rt)
+        for (int rt = 1; rt <= 8; ++rt)
           for (int sp = 1; sp <= 8; ++sp)
             snprintf(names[i][mb][rt][sp], 32, "gemm_%s_t%dm%ds%d", f[i], rt, mb, sp);
     init = true;
@@ -699,6 +715,9 @@ static const char* variant_name(int fmt, const Plan& p) {
 hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p) {
   const GemmW& W = *c.W;
   if (p.S < 1 || p.S > MAX_SPLITS || p.PR < 1 || p.nwg != p.PR * p.S) return hipErrorInvalidValue;
+  if (p.RT != 2 && p.RT != 4 && p.RT != 6 && p.RT != 8) return hipErrorInvalidValue;
+  if (p.MB >= 3 && p.RT != 2) return hipErrorInvalidValue;
+  if (c.epi == EPI_SILU && p.RT % 2) return hipErrorInvalidValue;
   if (c.epi == EPI_PARTIAL && (size_t)p.S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
   if (c.epi != EPI_PARTIAL && p.S != 1) return hipErrorInvalidValue;
   if (c.epi == EPI_ARGMAX && p.nwg > w.am_cap) return hipErrorInvalidValue;
