@@ -90,7 +90,6 @@ struct AttnArgs {
 };
 
 constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
-constexpr int ATTN_LDS = ATTN_PAGES * 2 * 16384;    // K and V^T of every page (128 KiB)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -121,9 +120,11 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 //     splits.
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // K and V^T staging as two LDS objects, so that waiting for the K loads
+  // does not also wait for the V^T loads
+  __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsV[ATTN_PAGES * 16384];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nw = blockDim.x >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, sidx = blockIdx.x;
   const int n = *a.dev_n;
@@ -140,24 +141,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int p = 0; p < ATTN_PAGES; ++p)
     pbase[p] = ((size_t)a.pt[min(key0 / PAGE + p, a.npages - 1)] * a.hkv + h) * PAGE * D;
-#pragma unroll
-  for (int p = 0; p < ATTN_PAGES; ++p) {
-    for (int jj = wave; jj < 32; jj += nw) {
-      const int blk = jj & 15;
-      const int q = blk * 64 + lane;           // 16-byte granule of the 16 KiB region
-      const uint16_t* src;
-      if (jj < 16) {
-        const int key = q >> 4, c = (q & 15) ^ (key & 15);
-        src = a.kc + pbase[p] + key * D + c * 8;
-      } else {
-        const int d = q >> 3, c = (q & 7) ^ ((d >> 1) & 7);
-        src = a.vc + pbase[p] + d * PAGE + c * 8;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (lds_ptr)(lds + (size_t)(p * 2 + (jj >> 4)) * 16384 + blk * 1024), 16, 0, 0);
-    }
-  }
-
   const int rbi = blockIdx.z * 4 + wave;      // this wave's 16-row block
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
@@ -169,86 +152,119 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (!live) return;
+  // K pages first, then V^T pages: the scores and the softmax run while the
+  // V^T loads are still in flight.  Each of the 4 waves issues 16 K and then
+  // 16 V^T 1 KiB blocks.
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int p = 0; p < ATTN_PAGES; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = wave + 4 * j;
+        const int q = blk * 64 + lane;         // 16-byte granule of the 16 KiB region
+        const uint16_t* src;
+        if (half == 0) {
+          const int key = q >> 4, c = (q & 15) ^ (key & 15);
+          src = a.kc + pbase[p] + key * D + c * 8;
+        } else {
+          const int d = q >> 3, c = (q & 7) ^ ((d >> 1) & 7);
+          src = a.vc + pbase[p] + d * PAGE + c * 8;
+        }
+        uint8_t* dst = (half == 0 ? ldsK : ldsV) + (size_t)p * 16384 + blk * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+      }
+    }
+  }
+  // this wave's q and K loads are done once at most its 16 V^T loads are
+  // outstanding (vmcnt 16 = 0x4000 | 0; expcnt and lgkmcnt not waited on)
+  __builtin_amdgcn_s_waitcnt(0x4F70);
+  __builtin_amdgcn_s_barrier();
 
   // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr),
-  //    row max, then exp2 and P*V in one pass.  Splits that end at or before
-  //    n are visible to every row (the whole committed context), so only the
-  //    split holding the block needs the mask.
+  //    row max, exp2 and the bf16 hi/lo split of p.  Splits that end at or
+  //    before n are visible to every row (the whole committed context), so
+  //    only the split holding the block needs the mask.
   constexpr int NT = ATTN_SPLIT / 16;
   const bool full = key0 + ATTN_SPLIT <= n;    // uniform
-  float sv[NT][4];
   float mx = -INFINITY;
+  float lsum = 0.f;
+  uint32_t ph[NT / 2][4], pl[NT / 2][4];
+  if (live) {
+    float sv[NT][4];
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    const int p = kt >> 2, key = (kt & 3) * 16 + lr;
-    const uint8_t* kpage = lds + (size_t)(p * 2) * 16384 + (size_t)key * 256;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < NT; ++kt) {
+      const int p = kt >> 2, key = (kt & 3) * 16 + lr;
+      const uint8_t* kpage = ldsK + (size_t)p * 16384 + (size_t)key * 256;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = (4 * ks + g) ^ (key & 15);
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = (4 * ks + g) ^ (key & 15);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[kt][v] = acc[v] * a.scale2;
+    }
+    if (!full) {
+      const int kmax = a.causal ? n + tok : kv_len - 1;     // last key this row sees
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (key0 + kt * 16 + 4 * g + v > kmax) sv[kt][v] = -INFINITY;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sv[kt][v] = acc[v] * a.scale2;
+    for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(sv[kt][0], sv[kt][1]), fmaxf(sv[kt][2], sv[kt][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // masked scores are -inf, so exp2(x - mref) is 0 for them; a row with no
+    // visible key in this split subtracts 0 instead of -inf (no NaN) and runs
+    // the wave-wide MFMAs with p = 0
+    const float mref = mx == -INFINITY ? 0.f : mx;
+#pragma unroll
+    for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
+      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v.
+      // p = hi + lo: hi keeps the top 16 bits of p (a bf16 by truncation),
+      // lo = p - hi (exact) rounded to bf16, so hi + lo carries 16 bits of p.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float pe = __builtin_amdgcn_exp2f(sv[2 * ks2 + hh][v] - mref);
+          lsum += pe;
+          const uint32_t u = __float_as_uint(pe);
+          const float hv = __uint_as_float(u & 0xffff0000u);
+          const uint32_t lu = __float_as_uint(pe - hv);
+          hb[v] = u;
+          lb[v] = lu + 0x7fffu + ((lu >> 16) & 1u);
+        }
+        ph[ks2][2 * hh] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+        ph[ks2][2 * hh + 1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
+        pl[ks2][2 * hh] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
+        pl[ks2][2 * hh + 1] = __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u);
+      }
+    }
   }
-  if (!full) {
-    const int kmax = a.causal ? n + tok : kv_len - 1;       // last key this row sees
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (key0 + kt * 16 + 4 * g + v > kmax) sv[kt][v] = -INFINITY;
-  }
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(sv[kt][0], sv[kt][1]), fmaxf(sv[kt][2], sv[kt][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // masked scores are -inf, so exp2(x - mref) is 0 for them; a row with no
-  // visible key in this split subtracts 0 instead of -inf (no NaN) and runs
-  // the wave-wide MFMAs with p = 0
-  const float mref = mx == -INFINITY ? 0.f : mx;
-  float lsum = 0.f;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();                  // every wave's V^T loads are in LDS
+  if (!live) return;
   floatx4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
-    // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v.
-    // p = hi + lo: hi keeps the top 16 bits of p (a bf16 by truncation),
-    // lo = p - hi (exact) rounded to bf16, so hi + lo carries 16 bits of p.
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint32_t hb[4], lb[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float pe = __builtin_amdgcn_exp2f(sv[2 * ks2 + hh][v] - mref);
-        lsum += pe;
-        const uint32_t u = __float_as_uint(pe);
-        const float hv = __uint_as_float(u & 0xffff0000u);
-        const uint32_t lu = __float_as_uint(pe - hv);
-        hb[v] = u;
-        lb[v] = lu + 0x7fffu + ((lu >> 16) & 1u);
-      }
-      ph[2 * hh] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
-      ph[2 * hh + 1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-      pl[2 * hh] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
-      pl[2 * hh + 1] = __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u);
-    }
-    const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+    const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[ks2][0], ph[ks2][1], ph[ks2][2], ph[ks2][3]});
+    const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[ks2][0], pl[ks2][1], pl[ks2][2], pl[ks2][3]});
     const int p = ks2 >> 1;
-    const uint8_t* vpage = lds + (size_t)(p * 2 + 1) * 16384;
-    const int c0 = 4 * (ks2 & 1) + (g >> 1), half = (g & 1) * 8;
+    const uint8_t* vpage = ldsV + (size_t)p * 16384;
+    const int c0 = 4 * (ks2 & 1) + (g >> 1), hoff = (g & 1) * 8;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = dt * 16 + lr, sw = (d >> 1) & 7;
-      const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + half);
-      const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + half);
+      const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + hoff);
+      const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + hoff);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
@@ -376,14 +392,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     a.npages = c.npages;
     const int nrb = (c.hq / c.hkv) * c.block_rows / 16;
     if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         ATTN_LDS);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), ATTN_LDS, s, a);
+    hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
