@@ -20,6 +20,10 @@ The tape of one token and head is (k_t, v_t, alpha_t, beta_t) in fp32.
 Committing a+1 tokens replays the tape of those tokens from the committed
 state; rejected tokens leave no trace.
 
+The verify runs the B tokens of a block in the chunked (UT / WY) form of the
+same rule (``recurrence_chunked``), which the tests pin against the
+sequential definition above.
+
 Bit-exact replay.  ``replay_pinned`` fixes the fp32 operation order so that
 two implementations can agree to the bit: per token, per head, per value row
 i,
@@ -81,6 +85,46 @@ def recurrence(S0, qh, kh, v, alpha, beta):
         o[t] = np.einsum("hij,hj->hi", S, qh[t])
         states[t] = S
     return o, states
+
+
+def recurrence_chunked(S0, qh, kh, v, alpha, beta):
+    """The same gated delta rule over one chunk of T tokens in its UT / WY
+    (chunked) form, in float64.  With gamma_t = alpha_1 ... alpha_t (gamma_0 = 1)
+    the recurrence unrolls to
+
+        S_t = gamma_t S0 + sum_{s<=t} (gamma_t / gamma_s) u_s k_s^T
+        u_s = beta_s v_s - beta_s gamma_s S0 k_s
+              - beta_s sum_{r<s} (gamma_s / gamma_r) (k_r . k_s) u_r
+
+    i.e. (I + A) U = diag(beta) (V - diag(gamma) K S0^T) with A strictly lower
+    triangular, A[s, r] = beta_s (gamma_s / gamma_r) k_s . k_r, solved by forward
+    substitution (the unit lower-triangular inverse is the UT transform), and
+
+        O   = diag(gamma) Q S0^T + (M o Q K^T) U,  M[t, s] = gamma_t / gamma_s (s <= t)
+        S_T = gamma_T S0 + U^T diag(gamma_T / gamma) K.
+
+    Decay ratios are exp(log gamma_t - log gamma_s), never a division by a small
+    gamma.  Returns (o [T, gh, dv], S_T [gh, dv, dk]).
+    """
+    S0 = np.asarray(S0, F64)
+    qh, kh, v = (np.asarray(a, F64) for a in (qh, kh, v))
+    alpha, beta = np.asarray(alpha, F64), np.asarray(beta, F64)
+    T, gh = kh.shape[0], kh.shape[1]
+    lg = np.cumsum(np.log(alpha), axis=0)               # log gamma_t, [T, gh]
+    o = np.empty(v.shape, F64)
+    S_end = np.empty(S0.shape, F64)
+    for h in range(gh):
+        K, Q, V, b, g = kh[:, h], qh[:, h], v[:, h], beta[:, h], lg[:, h]
+        S = S0[h]
+        ratio = np.exp(g[:, None] - g[None, :])           # gamma_t / gamma_s
+        A = np.tril(b[:, None] * ratio * (K @ K.T), -1)
+        rhs = b[:, None] * (V - np.exp(g)[:, None] * (K @ S.T))
+        U = np.empty_like(rhs)
+        for t in range(T):                                # forward substitution
+            U[t] = rhs[t] - A[t, :t] @ U[:t]
+        o[:, h] = np.exp(g)[:, None] * (Q @ S.T) + (np.tril(ratio) * (Q @ K.T)) @ U
+        S_end[h] = np.exp(g[-1]) * S + (U * np.exp(g[-1] - g)[:, None]).T @ K
+    return o, S_end
 
 
 def gdn_layer(L, x, S0, s: Shape, R):

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle.gdn import gates, halving_sum, l2norm, recurrence, replay_pinned
+from oracle.gdn import gates, halving_sum, l2norm, recurrence, recurrence_chunked, replay_pinned
 from oracle.model import sigmoid
 
 
@@ -105,3 +105,43 @@ def test_commit_state_equals_tape_replay():
     for a in (0, 3, 7):
         _, st2 = recurrence(S0, q[:a + 1], k[:a + 1], v[:a + 1], alpha[:a + 1], beta[:a + 1])
         assert np.array_equal(st2[-1], st[a])
+
+
+def test_chunked_form_equals_sequential():
+    # the UT / WY chunk form is an exact rewriting of the sequential rule
+    rng = np.random.default_rng(6)
+    q, k, v, alpha, beta = _tape(rng, 16, gh=3, dk=32, dv=32)
+    S0 = rng.standard_normal((3, 32, 32))
+    o_seq, st = recurrence(S0, q, k, v, alpha, beta)
+    o_ch, S_end = recurrence_chunked(S0, q, k, v, alpha, beta)
+    assert np.allclose(o_ch, o_seq, rtol=1e-10, atol=1e-10)
+    assert np.allclose(S_end, st[-1], rtol=1e-10, atol=1e-10)
+
+
+def test_chunked_form_special_cases():
+    rng = np.random.default_rng(7)
+    q, k, v, alpha, beta = _tape(rng, 6)
+    S0 = rng.standard_normal((2, 16, 16))
+    # beta = 0: pure decay, o_t = gamma_t S0 q_t
+    o, S_end = recurrence_chunked(S0, q, k, v, alpha, np.zeros_like(beta))
+    gam = np.cumprod(alpha, axis=0)
+    assert np.allclose(o, gam[:, :, None] * np.einsum("hij,thj->thi", S0, q), rtol=1e-12, atol=1e-13)
+    assert np.allclose(S_end, gam[-1][:, None, None] * S0, rtol=1e-12)
+    # one token: one step of the rule
+    o1, S1 = recurrence_chunked(S0, q[:1], k[:1], v[:1], alpha[:1], beta[:1])
+    r = v[0] - alpha[0][:, None] * np.einsum("hij,hj->hi", S0, k[0])
+    Sx = alpha[0][:, None, None] * S0 + (beta[0][:, None] * r)[:, :, None] * k[0][:, None, :]
+    assert np.allclose(S1, Sx, rtol=1e-13, atol=1e-13)
+    assert np.allclose(o1[0], np.einsum("hij,hj->hi", Sx, q[0]), rtol=1e-13, atol=1e-13)
+
+
+def test_chunks_chain():
+    # two chunks chained through the end state equal one chunk of both
+    rng = np.random.default_rng(8)
+    q, k, v, alpha, beta = _tape(rng, 12)
+    S0 = rng.standard_normal((2, 16, 16))
+    o, S_end = recurrence_chunked(S0, q, k, v, alpha, beta)
+    oa, Sa = recurrence_chunked(S0, q[:5], k[:5], v[:5], alpha[:5], beta[:5])
+    ob, Sb = recurrence_chunked(Sa, q[5:], k[5:], v[5:], alpha[5:], beta[5:])
+    assert np.allclose(np.concatenate([oa, ob]), o, rtol=1e-11, atol=1e-11)
+    assert np.allclose(Sb, S_end, rtol=1e-11, atol=1e-11)
