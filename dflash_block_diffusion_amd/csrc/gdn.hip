@@ -54,24 +54,36 @@ __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_l
   }
 }
 
-// Verify: one work-group per head, 4*dv threads; tokens applied in order to a
-// register copy of the committed state (which stays untouched).
+// Verify: the T = rows tokens of a block in the chunk (UT / WY) form of the
+// rule.  With gamma_t = alpha_1..alpha_t (kept as log gamma, cumulative sums
+// of log alpha = -softplus(a)), per head:
+//   KS = K S0^T, QS = Q S0^T            (one pass over the committed state)
+//   A[s][r] = beta_s gamma_s/gamma_r k_s.k_r (r < s),
+//   (I + A) U = diag(beta)(V - diag(gamma) KS)   (forward substitution)
+//   O = diag(gamma) QS + (M o Q K^T) U,  M[t][s] = gamma_t/gamma_s (s <= t).
+// The committed state is only read; the tape records (k_hat, v, alpha, beta)
+// per token for the commit's pinned replay.  One work-group per head,
+// 4*dv threads; thread (i, r) owns value row i and key columns r + 4m.
 template <int DK, int DV>
 __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   constexpr int NT = 4 * DV;
   constexpr int MAXT = 32;
   constexpr int REC = DK + DV + 2;
   __shared__ float kq[MAXT][2 * DK + DV + 2];   // k_hat, q_hat, v, alpha, beta per token
+  __shared__ float lga[MAXT];                   // log alpha, then log gamma
+  __shared__ float KS[MAXT][DV + 1], QS[MAXT][DV + 1], U[MAXT][DV + 1];
+  __shared__ float Am[MAXT][MAXT + 1], Mq[MAXT][MAXT + 1];
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid >> 2, r = tid & 3;
   const int gh = c.gh;
+  const int T = c.rows;
   const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
   const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
   const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
 
-  // per-token preprocessing: one wave per token
-  for (int t = wave; t < c.rows; t += NT / 64) {
+  // 1. per-token preprocessing, one wave per token: L2 norms, gates, tape
+  for (int t = wave; t < T; t += NT / 64) {
     // the projection is materialised in the activation format
     auto proj = [&](size_t col) { return act_round(c.atype, parts_sum(c.proj, t, (int)col)); };
     float qs = 0.f, ks = 0.f;
@@ -106,24 +118,69 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
       kq[t][2 * DK + DV + 1] = beta;
       tape[DK + DV] = alpha;
       tape[DK + DV + 1] = beta;
+      lga[t] = -(fmaxf(av, 0.f) + log1pf(expf(-fabsf(av))));   // log alpha = -softplus(a)
     }
   }
   __syncthreads();
-
-  float S[DK / 4];
-  const float* Sg = c.S + ((size_t)h * DV + i) * DK;
+  if (tid == 0)
+    for (int t = 1; t < T; ++t) lga[t] = lga[t - 1] + lga[t];   // log gamma_t
+  // 2. KS, QS: row i of S0 against every k_hat_t, q_hat_t (4 lanes per row,
+  //    partial dots over columns r + 4m, then the xor-2 / xor-1 exchanges)
+  {
+    float S[DK / 4];
+    const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
-  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
-
-  for (int t = 0; t < c.rows; ++t) {
-    apply_token<DK>(S, kq[t], kq[t][2 * DK + i], kq[t][2 * DK + DV], kq[t][2 * DK + DV + 1], r);
-    const float o = tree_dot<DK>(S, kq[t] + DK, r);
-    if (r == 0)
-      store_act(c.out, act_index(t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
+    for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+    for (int t = 0; t < T; ++t) {
+      float dk_ = 0.f, dq_ = 0.f;
+#pragma unroll
+      for (int m = 0; m < DK / 4; ++m) {
+        dk_ = dk_ + S[m] * kq[t][r + 4 * m];
+        dq_ = dq_ + S[m] * kq[t][DK + r + 4 * m];
+      }
+      dk_ = dk_ + __shfl_xor(dk_, 2, 64);
+      dk_ = dk_ + __shfl_xor(dk_, 1, 64);
+      dq_ = dq_ + __shfl_xor(dq_, 2, 64);
+      dq_ = dq_ + __shfl_xor(dq_, 1, 64);
+      if (r == 0) { KS[t][i] = dk_; QS[t][i] = dq_; }
+    }
+  }
+  __syncthreads();
+  // 3. A and M o QK^T (T x T each)
+  for (int e = tid; e < 2 * T * T; e += NT) {
+    const int which = e / (T * T), t = (e / T) % T, s2 = e % T;
+    float v = 0.f;
+    if (which == 0 ? s2 < t : s2 <= t) {
+      const float* x = which == 0 ? &kq[t][0] : &kq[t][DK];
+      float d = 0.f;
+      for (int j = 0; j < DK; ++j) d = d + x[j] * kq[s2][j];
+      const float ratio = expf(lga[t] - lga[s2]);
+      v = which == 0 ? kq[t][2 * DK + DV + 1] * ratio * d : ratio * d;
+    }
+    if (which == 0) Am[t][s2] = v; else Mq[t][s2] = v;
+  }
+  __syncthreads();
+  // 4. U by forward substitution, one thread per value column
+  if (tid < DV) {
+    const int col = tid;
+    for (int t = 0; t < T; ++t) {
+      const float beta = kq[t][2 * DK + DV + 1];
+      float u = beta * (kq[t][2 * DK + col] - expf(lga[t]) * KS[t][col]);
+      for (int s2 = 0; s2 < t; ++s2) u = u - Am[t][s2] * U[s2][col];
+      U[t][col] = u;
+    }
+  }
+  __syncthreads();
+  // 5. O = diag(gamma) QS + (M o QK^T) U; thread (i, r) takes tokens r, r+4, ...
+  for (int t = r; t < T; t += 4) {
+    float o = expf(lga[t]) * QS[t][i];
+    for (int s2 = 0; s2 <= t; ++s2) o = o + Mq[t][s2] * U[s2][i];
+    store_act(c.out, act_index(t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
   }
 }
 
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
+  if (c.rows < 1 || c.rows > 32) return hipErrorInvalidValue;    // one chunk of at most 32 tokens
   if (c.dk == 128 && c.dv == 128)
     hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c);
   else if (c.dk == 32 && c.dv == 32)

@@ -103,6 +103,13 @@ def lockstep(cfg, P, forced, gdn_exact=False):
     sched = torch.zeros(1, dtype=torch.int32, device="cuda")
     fill = torch.as_tensor(synth.filler_tokens(cfg, len(forced)), device="cuda")
     tl = tol_logits(cfg)
+    # The injection can only force an acceptance length while the committed
+    # stream still follows the reference stream.  Attention layers make each
+    # token's logits a function of its prefix alone, but the chunked GDN
+    # verify also depends on where the block starts, so at a near tie the
+    # lockstep run may leave the reference stream (the tie is then excluded
+    # by compare_tokens) and later forced lengths are no longer meaningful.
+    on_ref = True
     for s, k in enumerate(forced):
         n = op.t.n
         assert pair.query()["n"] == n
@@ -141,7 +148,8 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         a_o = accept_length(block[1:], argmax_first(fwd["logits"]))
         if np.all(vm[:max(a, a_o) + 1] >= max(TIE, 2 * vfloor)):
             assert a == a_o
-            assert a == k, "injected acceptance not realised"
+            if on_ref:
+                assert a == k, "injected acceptance not realised"
         emit = pair.emit[:a + 1].cpu().numpy()
         assert emit.tolist() == [int(t) for t in block[1:a + 1]] + [int(y[a])]
         if gdn_exact:
@@ -153,6 +161,8 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         with gemm_accumulation("f32"):
             op32.d.ctx_append(fwd32["hidden"][:a + 1], n + np.arange(a + 1))
         op32.anchor = int(y[a])
+        nn = pair.query()["n"]
+        on_ref = on_ref and torch.equal(pair.tokens(nn + 1).cpu(), ref[:nn + 1].cpu())
     q = pair.query()
     assert q["n"] == op.t.n and q["status"] == 0
     print(f"[{cfg.name}] tokens compared {stats['compared']}, excluded as undecidable {stats['excluded']}",
