@@ -121,7 +121,7 @@ struct Workspace {
 
 // RT row tiles per chunk, MB 16-token blocks, S K splits, PR work-groups per
 // split (nwg = PR * S), align = row tiles per balancing unit (2 for gate/up)
-struct Plan { int RT, MB, S, PR, ngroups, nwg, ktiles, ntile16, align; };
+struct Plan { int RT, MB, S, PR, ngroups, nwg, ktiles, ntile16, align, NW; };
 Plan make_plan(int fmt, int n, int k, int m, int epi);
 struct Workspace;
 

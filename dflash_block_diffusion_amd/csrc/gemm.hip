@@ -42,6 +42,10 @@
 //   Non-linear epilogues (fused gate/up SiLU*mul, lm-head argmax) use S = 1.
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
 
 #include "common.h"
 
@@ -217,10 +221,19 @@ __host__ __device__ constexpr int ring_depth(int fmt, int rt, int mb) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Operands are read through buffer descriptors: the base lives in SGPRs, each
+// lane adds a fixed byte offset and the per-tile offset is a scalar, so no
+// per-load address arithmetic runs on the vector unit.  Reads past
+// num_records return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
 // streamed weights are read once: non-temporal, so they do not evict the
 // activations every work-group re-reads from L2
-__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+constexpr int CPOL_NT = 2;
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, bool nt) {
+  const u32x4 v = __builtin_bit_cast(u32x4, nt ? __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CPOL_NT)
+                                                 : __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
   return uint4{v.x, v.y, v.z, v.w};
 }
 
@@ -233,19 +246,21 @@ struct Stage {
 
 // Persistent streaming GEMM.  Work-group w serves K split s = w % S and a
 // contiguous, balanced range of row tiles (in units of `align` tiles, 2 for
-// fused gate/up); it walks that range in chunks of RT row tiles.  Each wave
-// takes a quarter of the split's K tiles and streams the flattened sequence
-// (chunk, K tile) through a ring of U register stages: loads of the next
-// chunk are in flight while the previous chunk's four wave partials are
-// added in LDS (fixed order) and written out.
-template <int FMT, int RT, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// fused gate/up); it walks that range in chunks of RT row tiles.  Each of
+// its NW waves takes 1/NW of the split's K tiles and streams the flattened
+// sequence (chunk, K tile) through a ring of U register stages: loads of the
+// next chunk are in flight while the previous chunk's NW wave partials are
+// added in LDS (fixed order) and written out.  With NW = 8 (two waves per
+// SIMD) one wave's dequantisation overlaps the other's loads.
+template <int FMT, int RT, int MB, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_stream_kernel(GemmArgs a) {
   constexpr int KT = tile_k(FMT);
   constexpr int SS = KT / 32;
   constexpr int U = ring_depth(FMT, RT, MB);
   constexpr int NE = RT * MB * 4;            // accumulator floats per lane
-  __shared__ float red[4][NE][64];
+  static_assert(NW == 4 || (NW == 8 && MB == 2), "8 waves need two token blocks");
+  __shared__ float red[NW][NE][64];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every per-wave index and stage address below is
@@ -264,7 +279,7 @@ void gemm_stream_kernel(GemmArgs a) {
   const int kt0 = (int)((long long)a.ktiles * sidx / S);
   const int kt1 = (int)((long long)a.ktiles * (sidx + 1) / S);
   const int nk = kt1 - kt0;
-  const int t0 = kt0 + nk * wave / 4, t1 = kt0 + nk * (wave + 1) / 4;
+  const int t0 = kt0 + nk * wave / NW, t1 = kt0 + nk * (wave + 1) / NW;
   const int nt = t1 - t0;
   const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
 
@@ -275,25 +290,28 @@ void gemm_stream_kernel(GemmArgs a) {
     for (int mb = 0; mb < MB; ++mb) acc[r][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // activations are tiled (fm_index): the fragment of token block mb and
-  // 32-column step kb is the contiguous 1 KiB at ((mb * K/32) + kb) * 512
-  const uint16_t* xrow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) xrow[mb] = a.x + (size_t)mb * (a.k >> 5) * 512 + lane * 8;
-  const uint8_t* wlane = a.w + lane * 16;
-  const uint32_t* slane = (FMT == W_W4) ? (const uint32_t*)a.s + lr : nullptr;
+  // 32-column step kb is the contiguous 1 KiB at ((mb * K/32) + kb) * 1024 B;
+  // weight tile (rt, t) is the 1 KiB at (rt * ktiles + t) * 1024 B and its
+  // W4 scales the 64 B at (rt * ktiles + t) * 64 B
+  const uint32_t xfrag = (uint32_t)(a.k >> 5);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (uint32_t)a.ntile16 * a.ktiles * 1024u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.s, FMT == W_W4 ? (uint32_t)a.ntile16 * a.ktiles * 64u : 0u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)MB * xfrag * 1024u);
+  const uint32_t vlane = lane * 16, vrow = lr * 4;
 
   // stage (chunk c, K tile t); row tiles past the range re-read the last one
   auto load = [&](int c, int t, Stage<FMT, RT, MB>& f) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int rt = min(rtb + c * RT + r, rte - 1);
-      f.w[r] = load_stream(wlane + ((size_t)rt * a.ktiles + t) * 1024);
-      if (FMT == W_W4) f.s[r] = slane[((size_t)rt * a.ktiles + t) * 16];
+      const uint32_t tile = (uint32_t)min(rtb + c * RT + r, rte - 1) * a.ktiles + t;
+      f.w[r] = buf_load16(rw, vlane, tile * 1024u, true);
+      if (FMT == W_W4) f.s[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, vrow, tile * 64u, 0);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int ss = 0; ss < SS; ++ss) f.x[mb][ss] = *(const uint4*)(xrow[mb] + ((size_t)t * SS + ss) * 512);
+      for (int ss = 0; ss < SS; ++ss)
+        f.x[mb][ss] = buf_load16(rx, vlane, ((uint32_t)mb * xfrag + (uint32_t)t * SS + ss) * 1024u, false);
   };
 
   auto compute = [&](const Stage<FMT, RT, MB>& f) {
@@ -347,9 +365,12 @@ void gemm_stream_kernel(GemmArgs a) {
     return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : 1.0f;
   };
 
-  // Chunk epilogue: fixed-order reduction of the 4 wave partials,
-  // ((w0 + w1) + w2) + w3; thread (wave w, lane) finishes accumulator slot
-  // v = w of every (r, mb): token mb*16 + 4g + w, weight row (rt0 + r)*16 + lr.
+  // Chunk epilogue: fixed-order reduction of the NW wave partials,
+  // ((w0 + w1) + w2) + ...; thread (wave w, lane) finishes accumulator slot
+  // v = w % 4 of every (r, mb) it owns (all mb with 4 waves, mb = w / 4 with
+  // 8): token mb*16 + 4g + v, weight row (rt0 + r)*16 + lr.
+  const int vslot = wave & 3;
+  auto own = [&](int mb) { return NW == 4 || mb == (wave >> 2); };
   auto epilogue = [&](int c) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -367,10 +388,13 @@ void gemm_stream_kernel(GemmArgs a) {
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int j = (r * MB + mb) * 4 + wave;
-        val[r][mb] = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+        const int j = (r * MB + mb) * 4 + vslot;
+        float v = red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v = v + red[w][j][lane];
+        val[r][mb] = v;
       }
-    __syncthreads();      // red is rewritten by the next chunk
+    if (c + 1 < nch) __syncthreads();      // red is rewritten by the next chunk
     if (a.epi == EPI_PARTIAL) {
       float* part = a.part + (size_t)sidx * a.m * a.n;
 #pragma unroll
@@ -380,8 +404,8 @@ void gemm_stream_kernel(GemmArgs a) {
         const float sc = scale_of(n);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int t = mb * 16 + 4 * g + wave;
-          if (t < a.m) part[(size_t)t * a.n + n] = val[r][mb] * sc;
+          const int t = mb * 16 + 4 * g + vslot;
+          if (own(mb) && t < a.m) part[(size_t)t * a.n + n] = val[r][mb] * sc;
         }
       }
     } else if (a.epi == EPI_SILU) {
@@ -395,8 +419,8 @@ void gemm_stream_kernel(GemmArgs a) {
         const float sg = scale_of(ng), su = scale_of(nu);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int t = mb * 16 + 4 * g + wave;
-          if (t >= a.m) continue;
+          const int t = mb * 16 + 4 * g + vslot;
+          if (!own(mb) || t >= a.m) continue;
           const float gv = act_round(rnd, val[2 * p][mb] * sg);
           const float uv = act_round(rnd, val[2 * p + 1][mb] * su);
           const float sv = gv / (1.0f + expf(-gv));
@@ -406,7 +430,8 @@ void gemm_stream_kernel(GemmArgs a) {
     } else {  // EPI_ARGMAX: ascending n within the lane keeps the lowest index on ties
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int t = mb * 16 + 4 * g + wave;
+        const int t = mb * 16 + 4 * g + vslot;
+        if (!own(mb)) continue;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           if (rt0 + r >= rte) continue;
@@ -457,6 +482,7 @@ void gemm_stream_kernel(GemmArgs a) {
   if (a.epi == EPI_ARGMAX) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      if (!own(mb)) continue;
       float bv = best[mb];
       int bi = bidx[mb];
       // across the 16 lanes of this token (rows differ by lane): lowest index on ties
@@ -466,7 +492,7 @@ void gemm_stream_kernel(GemmArgs a) {
         const int oi = __shfl_xor(bi, o, 64);
         if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
-      const int t = mb * 16 + 4 * g + wave;
+      const int t = mb * 16 + 4 * g + vslot;
       if (lr == 0) {
         a.am_val[(size_t)blockIdx.x * 64 + t] = bv;
         a.am_idx[(size_t)blockIdx.x * 64 + t] = bi;
@@ -637,6 +663,7 @@ hipError_t launch_sum_parts(const float* part, int S, size_t count, float* out, 
 //     per split for writing and re-reading the partials.
 Plan make_plan(int fmt, int n, int k, int m, int epi) {
   Plan p;
+  p.NW = 4;
   p.MB = (m + 15) / 16;
   p.ntile16 = n / 16;
   p.ktiles = fmt == W_F32 ? 0 : k / tile_k(fmt);
@@ -675,12 +702,15 @@ int gemm_am_blocks(int fmt, int n, int m) {
 }
 
 template <int FMT, int RT>
-static hipError_t dispatch_mb(int MB, dim3 grid, const GemmArgs& a, hipStream_t s) {
+static hipError_t dispatch_mb(int MB, int NW, dim3 grid, const GemmArgs& a, hipStream_t s) {
   switch (MB) {
-    case 1: hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 3>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 1, 4>), grid, dim3(256), 0, s, a); break;
+    case 2:
+      if (NW == 8) hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 2, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gemm_stream_kernel<FMT, RT, 2, 4>), grid, dim3(256), 0, s, a);
+      break;
+    case 3: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 3, 4>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_stream_kernel<FMT, 2, 4, 4>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -688,28 +718,32 @@ static hipError_t dispatch_mb(int MB, dim3 grid, const GemmArgs& a, hipStream_t 
 template <int FMT>
 static hipError_t dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
   dim3 grid(p.nwg);
-  if (p.MB >= 3) return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+  if (p.MB >= 3) return dispatch_mb<FMT, 2>(p.MB, 4, grid, a, s);
   switch (p.RT) {
-    case 8: return dispatch_mb<FMT, 8>(p.MB, grid, a, s);
-    case 6: return dispatch_mb<FMT, 6>(p.MB, grid, a, s);
-    case 4: return dispatch_mb<FMT, 4>(p.MB, grid, a, s);
-    default: return dispatch_mb<FMT, 2>(p.MB, grid, a, s);
+    case 8: return dispatch_mb<FMT, 8>(p.MB, p.NW, grid, a, s);
+    case 6: return dispatch_mb<FMT, 6>(p.MB, p.NW, grid, a, s);
+    case 4: return dispatch_mb<FMT, 4>(p.MB, p.NW, grid, a, s);
+    default: return dispatch_mb<FMT, 2>(p.MB, p.NW, grid, a, s);
   }
 }
 
+// Name of the compiled kernel and launch shape a plan runs: the template
+// instance (format, row tile chunk, token row blocks) and the grid.  Launches
+// that differ only in their split count run the same kernel on the same grid
+// and share a name, so the name is also what a kernel trace can tell apart.
 static const char* variant_name(int fmt, const Plan& p) {
-  static char names[4][5][9][9][32];
-  static bool init = false;
-  if (!init) {
-    const char* f[4] = {"f32", "bf16", "w8", "w4"};
-    for (int i = 0; i < 4; ++i)
-      for (int mb = 1; mb <= 4; ++mb)
-        for (int rt = 1; rt <= 8; ++rt)
-          for (int sp = 1; sp <= 8; ++sp)
-            snprintf(names[i][mb][rt][sp], 32, "gemm_%s_t%dm%ds%d", f[i], rt, mb, sp);
-    init = true;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int>, std::string> names;
+  const char* f[4] = {"f32", "bf16", "w8", "w4"};
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_tuple(fmt, p.RT, p.MB, p.NW, p.nwg);
+  auto it = names.find(key);
+  if (it == names.end()) {
+    char buf[48];
+    snprintf(buf, sizeof buf, "gemm_%s_t%dm%dw%d_g%d", f[fmt], p.RT, p.MB, p.NW, p.nwg);
+    it = names.emplace(key, std::string(buf)).first;
   }
-  return names[fmt][p.MB][p.RT][p.S];
+  return it->second.c_str();
 }
 
 hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p) {
@@ -717,6 +751,7 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
   if (p.S < 1 || p.S > MAX_SPLITS || p.PR < 1 || p.nwg != p.PR * p.S) return hipErrorInvalidValue;
   if (p.RT != 2 && p.RT != 4 && p.RT != 6 && p.RT != 8) return hipErrorInvalidValue;
   if (p.MB >= 3 && p.RT != 2) return hipErrorInvalidValue;
+  if (p.NW != 4 && !(p.NW == 8 && p.MB == 2)) return hipErrorInvalidValue;
   if (c.epi == EPI_SILU && p.RT % 2) return hipErrorInvalidValue;
   if (c.epi == EPI_PARTIAL && (size_t)p.S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
   if (c.epi != EPI_PARTIAL && p.S != 1) return hipErrorInvalidValue;
@@ -741,7 +776,16 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
   const GemmW& W = *c.W;
   size_t wb, sb;
   packed_bytes(W.fmt, W.n, W.k, &wb, &sb);
-  if (bytes) *bytes = (double)(wb + sb);
+  // algorithmic bytes: packed weights and scales, the bf16 activations read
+  // once, and the product written once in its consumer's type (fp32 sums,
+  // bf16 SiLU rows, or the fp32 logits when they are kept)
+  if (bytes) {
+    double out_b = 0;
+    if (c.epi == EPI_PARTIAL) out_b = 4.0 * c.m * W.n;
+    else if (c.epi == EPI_SILU) out_b = 2.0 * c.m * (W.n / 2);
+    else if (c.logits) out_b = 4.0 * c.m * W.n;
+    *bytes = (double)(wb + sb) + 2.0 * c.m * W.k + out_b;
+  }
   if (W.fmt == W_F32) {
     if (variant) *variant = "gemm_f32";
     if (splits) *splits = 1;
