@@ -31,12 +31,13 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet); both results
+// are formed and one selected, so no divergent branch is emitted
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rn = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rn;
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
 

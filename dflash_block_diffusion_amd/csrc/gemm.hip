@@ -423,7 +423,10 @@ void gemm_stream_kernel(GemmArgs a) {
           if (!own(mb) || t >= a.m) continue;
           const float gv = act_round(rnd, val[2 * p][mb] * sg);
           const float uv = act_round(rnd, val[2 * p + 1][mb] * su);
-          const float sv = gv / (1.0f + expf(-gv));
+          // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal
+          // (about 1 ulp each in fp32, before the bf16 rounding below);
+          // e^-g = +inf for g << 0 gives g * 0 = -0
+          const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
           store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
         }
       }
@@ -464,17 +467,26 @@ void gemm_stream_kernel(GemmArgs a) {
     // trade the in-flight depth for registers)
     __builtin_amdgcn_sched_barrier(0);
     int cc = 0, ct = t0;                       // stage being multiplied
-    for (int q = 0; q < Q; q += U) {
+    int q = 0;
+    for (; q + U < Q; q += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (q + u < Q) {
-          compute(ring[u]);
-          if (ct == t1 - 1) epilogue(cc);
-          advance(cc, ct);
-        }
+        compute(ring[u]);
+        if (ct == t1 - 1) epilogue(cc);
+        advance(cc, ct);
         load(pc, pt, ring[u]);
         advance(pc, pt);
         __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // last block: the remaining 1..U stages are all in flight; no loads
+    // past the end are issued, so the wave's tail carries no dead reads
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q + u < Q) {
+        compute(ring[u]);
+        if (ct == t1 - 1) epilogue(cc);
+        advance(cc, ct);
       }
     }
   }
