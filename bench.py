@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
+    ap.add_argument("--max-draft", type=int, default=0,
+                    help="verify only the first N drafts per step (0 = the whole block)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the draft+verify step of one sequence runs on a single "
@@ -187,6 +189,10 @@ def main():
     K, W = args.steps, args.warmup
     max_ctx = ctx + (W + K + 4) * B + 64
     pair = Pair(cfg, ck, max_ctx=max_ctx)
+    n_drafts = B - 1
+    if args.max_draft:
+        pair.set_max_draft(args.max_draft)
+        n_drafts = pair.accept_block - 1
     del ck
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -244,7 +250,7 @@ def main():
     acc = pair.acc_log().cpu().numpy()
     idx = [(steps0 + i) % len(acc) for i in range(K)]
     a_run = acc[idx]
-    a_sched = sched.cpu().numpy()[[(steps0 + i) % n_sched for i in range(K)]]
+    a_sched = np.minimum(sched.cpu().numpy()[[(steps0 + i) % n_sched for i in range(K)]], n_drafts)
     if q["status"] != 0:
         log(f"WARNING: device status word {q['status']}")
     log(f"timed {K} steps: {ms:.3f} ms, n {ctx} -> {q['n']}, accepted {a_run.tolist()}, "
@@ -313,8 +319,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {fmt_name[cfg.target.fmt]} target {cfg.target.n_layers} layers "
                                 f"H{cfg.target.hidden} + {fmt_name[cfg.drafter.fmt]} drafter "
-                                f"{cfg.drafter.n_layers} layers, block {B}, ctx {ctx}, injected acceptance"),
-                   "block": B, "ctx": ctx, "global_batch": 1,
+                                f"{cfg.drafter.n_layers} layers, block {B}, ctx {ctx}, injected acceptance"
+                                + (f", draft cap {n_drafts} ({pair.vrows} verify rows)" if args.max_draft else "")),
+                   "block": B, "ctx": ctx, "global_batch": 1, "verify_rows": pair.vrows, "drafts_verified": n_drafts,
                    "target_format": fmt_name[cfg.target.fmt], "drafter_format": fmt_name[cfg.drafter.fmt]},
         "tok_per_s": round(tok_per_s, 1),
         "tokens_per_step": round(tokens / K, 3),

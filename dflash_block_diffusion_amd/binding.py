@@ -65,6 +65,7 @@ SIGNATURES = {
     "dflash_draft_block": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_verify_block": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_accept": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dflash_set_max_draft": (c_int, [c_void_p, c_int, POINTER(c_int), POINTER(c_int)]),
     "dflash_kv_commit": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_kv_rollback": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
     "dflash_gdn_snapshot": (c_int, [c_void_p, c_void_p]),

@@ -268,6 +268,8 @@ struct dflash_state {
   const dflash_model* t = nullptr;
   const dflash_model* dr = nullptr;
   int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
+  int vrows = 0;          // rows a verify runs (B, or fewer under a draft cap)
+  int max_draft = 0;      // drafts verified per step (0 = the whole block)
   char* base = nullptr;
   size_t bytes = 0;
   int32_t* scal = nullptr;
@@ -382,6 +384,7 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   if (block != 16 && block != 32) return fail(DFLASH_E_SHAPE, "block must be 16 or 32");
   if (max_ctx < 1) return fail(DFLASH_E_SHAPE, "max_ctx must be positive");
   s->t = t; s->dr = d; s->B = block; s->max_ctx = max_ctx;
+  s->vrows = block; s->max_draft = 0;
   const int need = max_ctx + 2 * block;
   s->pages = (need + PAGE - 1) / PAGE;
   s->capacity = s->pages * PAGE;
@@ -495,9 +498,11 @@ static int norm(dflash_state* s, const dflash_model* m, Pending& pend, const flo
   return DFLASH_OK;
 }
 
+// B = block rows of this pass: the whole block for a draft (plus as many
+// context rows), the verify rows for a verify.
 static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer& L, bool draft, Pending& pend,
-                      hipStream_t st) {
-  const int H = m->d.hidden, B = s->B, hq = m->d.n_q_heads, hkv = m->d.n_kv_heads, hd = m->d.head_dim;
+                      int B, hipStream_t st) {
+  const int H = m->d.hidden, hq = m->d.n_q_heads, hkv = m->d.n_kv_heads, hd = m->d.head_dim;
   const int rows = draft ? 2 * B : B;
   RC(norm(s, m, pend, L.in_norm, s->bu, m->gin, B, st));
   Parts qkv;
@@ -523,9 +528,9 @@ static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer
 
 // FFN block; the down projection's partials stay pending (with the side copy
 // of the new residual for a conditioning layer) for the next norm.
-static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& pend, hipStream_t st,
+static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& pend, int B, hipStream_t st,
                void* side, int ld_side, int side_type, int side_col0) {
-  const int H = m->d.hidden, F = m->d.ffn, B = s->B;
+  const int H = m->d.hidden, F = m->d.ffn;
   RC(norm(s, m, pend, L.post_norm, s->bu, m->gin, B, st));
   RC(gemm(s, L.gu, s->bu, H, B, EPI_SILU, st, nullptr, s->bf, m->gin));
   RC(gemm(s, L.down, s->bf, F, B, EPI_PARTIAL, st, &pend.in));
@@ -551,24 +556,26 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
                       s->scal + SC_STATUS, st));
   Pending pend;
   for (int l = 0; l < d->d.n_layers; ++l) {
-    RC(attn_layer(s, d, l, d->layers[l], true, pend, st));
-    RC(ffn(s, d, d->layers[l], pend, st, nullptr, 0, 0, 0));
+    RC(attn_layer(s, d, l, d->layers[l], true, pend, B, st));
+    RC(ffn(s, d, d->layers[l], pend, B, st, nullptr, 0, 0, 0));
   }
   RC(norm(s, d, pend, d->d.final_norm, s->bu, t->gin, B, st));
   RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 1, block + 1));
   return DFLASH_OK;
 }
 
-static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, hipStream_t st) {
+// Target forward of rows 0..B-1 of block (B = s->B for prefill chunks, the
+// verify rows otherwise).
+static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, int B, hipStream_t st) {
   const dflash_model *t = s->t, *d = s->dr;
-  const int H = t->d.hidden, B = s->B;
+  const int H = t->d.hidden;
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 0, 0, B, s->x, H, s->scal + SC_STATUS, st));
   Pending pend;
   int sel = 0, g = 0;
   for (int l = 0; l < t->d.n_layers; ++l) {
     const Layer& L = t->layers[l];
     if (L.kind == DFLASH_LAYER_ATTN) {
-      RC(attn_layer(s, t, l, L, false, pend, st));
+      RC(attn_layer(s, t, l, L, false, pend, B, st));
     } else {
       const int gh = t->d.gdn_heads, dkk = t->d.gdn_dk, dvv = t->d.gdn_dv;
       RC(norm(s, t, pend, L.in_norm, s->bu, t->gin, B, st));
@@ -576,7 +583,7 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       RC(gemm(s, L.qkv, s->bu, H, B, EPI_PARTIAL, st, &gc.proj));
       gc.atype = t->act; gc.rows = B; gc.gh = gh; gc.dk = dkk; gc.dv = dvv;
       gc.S = s->gdn_S + (size_t)g * gh * dvv * dkk;
-      gc.tape = s->gdn_tape + (size_t)g * B * gh * gdn_rec(t);
+      gc.tape = s->gdn_tape + (size_t)g * s->B * gh * gdn_rec(t);   // tape rows are laid out per B
       gc.out = s->ba; gc.otype = t->gin; gc.ldo = gh * dvv;
       HIPCHK(launch_gdn_verify(gc, st));
       RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_PARTIAL, st, &pend.in));
@@ -589,7 +596,7 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       col0 = sel * H;
       ++sel;
     }
-    RC(ffn(s, t, L, pend, st, side, d->d.n_sel * H, d->gin, col0));
+    RC(ffn(s, t, L, pend, B, st, side, d->d.n_sel * H, d->gin, col0));
   }
   RC(norm(s, t, pend, t->d.final_norm, s->bu, t->gin, B, st));
   RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 0, argmax));
@@ -623,7 +630,7 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
   int last = 0;
   for (int c0 = 0; c0 < n_tokens; c0 += s->B) {
     const int len = std::min(s->B, n_tokens - c0);
-    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, st));
+    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, s->B, st));
     RC(do_commit(s, nullptr, len, nullptr, st));
     RC(do_draft(s, s->blk, nullptr, st));          // appends the chunk's drafter context rows
     last = len;
@@ -643,7 +650,31 @@ extern "C" int dflash_draft_block(dflash_state* s, int32_t* d_block, float* d_lo
 extern "C" int dflash_verify_block(dflash_state* s, const int32_t* d_block, int32_t* d_argmax, float* d_logits,
                                    void* stream) {
   if (!s || !d_block || !d_argmax) return fail(DFLASH_E_INVALID, "null argument");
-  return do_verify(s, d_block, d_argmax, d_logits, (hipStream_t)stream);
+  return do_verify(s, d_block, d_argmax, d_logits, s->vrows, (hipStream_t)stream);
+}
+
+// Draft cap (mlx-dspark v0.0.3 "Highlights" and "API", --max-draft): verify
+// only the first N = min(max_draft, B-1) drafts (0 = the whole block).  The
+// verify then runs V >= N+1 rows, V the smallest multiple of the attention
+// row quantum (16 query rows of one KV head per MFMA block) not below N+1;
+// the caller accepts over N+1 rows.
+extern "C" int dflash_set_max_draft(dflash_state* s, int max_draft, int* h_verify_rows, int* h_accept_block) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  if (max_draft < 0) return fail(DFLASH_E_SHAPE, "max_draft must be >= 0");
+  const int N = max_draft == 0 ? s->B - 1 : std::min(max_draft, s->B - 1);
+  // the target's MFMA attention takes G*V query rows per KV head in 16-row
+  // blocks (G query heads per KV head); the fp32 attention has no quantum
+  int q = 1;
+  if (s->t->act != T_F32) {
+    const int G = s->t->d.n_q_heads / s->t->d.n_kv_heads;
+    while ((G * q) % 16) ++q;
+  }
+  const int V = std::min(s->B, (N + 1 + q - 1) / q * q);
+  s->max_draft = max_draft;
+  s->vrows = V;
+  if (h_verify_rows) *h_verify_rows = V;
+  if (h_accept_block) *h_accept_block = N + 1;
+  return DFLASH_OK;
 }
 
 extern "C" int dflash_accept(const int32_t* d_block, const int32_t* d_argmax, int block, int32_t* d_accept,

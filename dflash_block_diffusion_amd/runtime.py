@@ -159,6 +159,7 @@ class Pair:
         self.view = StateView()
         check(lib().dflash_state_buffers(self.st, byref(self.view)))
         self.prompt_len = 0
+        self.vrows, self.accept_block = self.B, self.B
 
     # ------------------------------------------------------------- views
     def _arena_slice(self, addr: int, nbytes: int, dtype) -> torch.Tensor:
@@ -208,8 +209,16 @@ class Pair:
     def verify(self, logits: Optional[torch.Tensor] = None):
         check(lib().dflash_verify_block(self.st, ptr(self.block), ptr(self.y), ptr(logits), stream_handle()))
 
+    def set_max_draft(self, max_draft: int) -> int:
+        """Verify only the first min(max_draft, B-1) drafts (0 = the whole
+        block); returns the number of rows a verify now runs."""
+        v, a = c_int(), c_int()
+        check(lib().dflash_set_max_draft(self.st, int(max_draft), byref(v), byref(a)))
+        self.vrows, self.accept_block = v.value, a.value
+        return self.vrows
+
     def accept(self):
-        check(lib().dflash_accept(ptr(self.block), ptr(self.y), self.B, ptr(self.acc), ptr(self.emit),
+        check(lib().dflash_accept(ptr(self.block), ptr(self.y), self.accept_block, ptr(self.acc), ptr(self.emit),
                                   ptr(self.block), stream_handle()))
 
     def commit(self):

@@ -196,14 +196,30 @@ int dflash_prefill(dflash_state *st, const int32_t *d_tokens, int n_tokens,
  * draft logits of rows 1..B-1 as [B-1][V]. */
 int dflash_draft_block(dflash_state *st, int32_t *d_block, float *d_logits, void *stream);
 
-/* Target verify of d_block[0..B-1] at positions n..n+B-1 (causal inside the
- * block, full committed context).  Writes y_i = argmax of row i (lowest index
- * on ties) to d_argmax[0..B-1], K/V of all B positions to the cache (the
- * rejected ones are overwritten by the next verify), the conditioning layers'
- * outputs to the drafter's context buffer, and for GatedDeltaNet layers the
- * per-token tape.  d_logits, if not NULL, receives [B][V] fp32 logits. */
+/* Target verify of d_block[0..R-1] at positions n..n+R-1 (causal inside the
+ * block, full committed context), R = B, or the verify rows set by
+ * dflash_set_max_draft.  Writes y_i = argmax of row i (lowest index on ties)
+ * to d_argmax[0..R-1], K/V of all R positions to the cache (the rejected
+ * ones are overwritten by the next verify), the conditioning layers' outputs
+ * to the drafter's context buffer, and for GatedDeltaNet layers the
+ * per-token tape.  d_logits, if not NULL, receives [R][vocab] fp32 logits. */
 int dflash_verify_block(dflash_state *st, const int32_t *d_block, int32_t *d_argmax,
                         float *d_logits, void *stream);
+
+/* Draft cap (mlx-dspark v0.0.3, "Highlights" and "API": --max-draft, where 0
+ * runs the whole block): later verifies check only the first
+ * N = min(max_draft, B-1) drafts (N = B-1 for max_draft = 0).  Each verify
+ * then runs V rows, V the smallest multiple of the target attention's row
+ * quantum (G*V query rows of one KV head fill whole 16-row MFMA blocks, G =
+ * query heads per KV head; 1 for fp32 models) that is >= N+1, capped at B:
+ * d_argmax[0..V-1] and d_logits [V][vocab] are written, rows past N+1 are
+ * computed but play no part.  The caller passes N+1 as `block` to
+ * dflash_accept so that a <= N.  The drafter still drafts B-1 tokens and
+ * prefill still runs whole blocks.  *h_verify_rows = V and *h_accept_block =
+ * N+1 (either may be NULL).  Errors: DFLASH_E_INVALID (null state),
+ * DFLASH_E_SHAPE (max_draft < 0).  Host-only call; it changes what later
+ * calls enqueue, so a captured graph must be recaptured. */
+int dflash_set_max_draft(dflash_state *st, int max_draft, int *h_verify_rows, int *h_accept_block);
 
 /* Longest-prefix acceptance: a = max{k <= B-1 : d_block[j] == d_argmax[j-1]
  * for all 1 <= j <= k}.  d_accept[0] = a; d_emit[0..a-1] = drafts d_1..d_a,

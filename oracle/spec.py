@@ -17,6 +17,12 @@ One draft+verify step (mirror-sd README, "How It Works"; dflash-mlx note,
    target hidden states of those a+1 rows become new drafter context rows;
    GatedDeltaNet layers replay their tape for the a+1 tokens.
 
+Draft cap (mlx-dspark v0.0.3, "Highlights" and "API", --max-draft; its
+head-to-head table compares a cap of 2 with the full 16-block): with N > 0
+only the first min(N, B-1) drafts are verified -- the target forward runs the
+anchor and those drafts and a <= N; 0 verifies the whole block.  The drafter
+still drafts the whole block.
+
 Greedy speculative output equals plain greedy decoding of the target
 (mlx-dspark v0.0.3 intro; agentlens summary, "Highlights") -- the invariant
 tests check on this oracle.
@@ -195,9 +201,11 @@ def inject_drafts(drafts, n: int, k: int, ref, filler_row, vocab: int):
 
 
 class OraclePair:
-    def __init__(self, cfg, ckpt: Dict, cap: int):
+    def __init__(self, cfg, ckpt: Dict, cap: int, max_draft: int = 0):
         self.cfg = cfg
         self.B = cfg.block
+        # drafts verified per step
+        self.N = self.B - 1 if max_draft == 0 else min(int(max_draft), self.B - 1)
         self.t = OracleTarget(cfg.target, ckpt["target"], cfg.sel_layers, cap)
         self.d = OracleDrafter(cfg.drafter, ckpt["drafter"], ckpt["target"],
                                cfg.mask_token, cfg.block, cap)
@@ -224,10 +232,10 @@ class OraclePair:
         raw = drafts.copy()
         if inject is not None:
             drafts = inject(drafts, n)
-        block = [self.anchor] + [int(t) for t in drafts]
+        block = [self.anchor] + [int(t) for t in drafts[:self.N]]
         fwd = self.t.forward(block)
         y = argmax_first(fwd["logits"]).astype(np.int64)
-        a = accept_length(drafts, y)
+        a = accept_length(drafts[:self.N], y)
         self.t.commit(fwd, a)
         self.d.ctx_append(fwd["hidden"][: a + 1], n + np.arange(a + 1))
         emitted = [int(t) for t in drafts[:a]] + [int(y[a])]

@@ -67,13 +67,17 @@ def compare_tokens(got, ref, margin, stats, floor=0.0):
     assert np.array_equal(np.asarray(got)[ok], np.asarray(ref)[ok]), (got, ref, margin)
 
 
-def lockstep(cfg, P, forced, gdn_exact=False):
-    """Run len(forced) injected steps on GPU and oracle in lockstep."""
+def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0):
+    """Run len(forced) injected steps on GPU and oracle in lockstep; with
+    max_draft > 0 both sides verify only the first max_draft drafts."""
     B, V = cfg.block, cfg.target.vocab
     ck = synth.make_pair(cfg)
     prompt = synth.prompt(cfg, P)
     max_ctx = P + (len(forced) + 4) * B + 64
     pair = Pair(cfg, ck, max_ctx=max_ctx)
+    if max_draft:
+        rows = pair.set_max_draft(max_draft)
+        assert max_draft + 1 <= rows <= B
     first = pair.prefill(prompt)
     tapes = []
     if gdn_exact:
@@ -89,9 +93,10 @@ def lockstep(cfg, P, forced, gdn_exact=False):
     pair.rollback(P)
     if gdn_exact:
         tapes = tapes[:1]
-    op = OraclePair(cfg, ck, cap=max_ctx + 2 * B)
+    op = OraclePair(cfg, ck, cap=max_ctx + 2 * B, max_draft=max_draft)
     op.prefill(prompt)
-    op32 = OraclePair(cfg, ck, cap=max_ctx + 2 * B)
+    op32 = OraclePair(cfg, ck, cap=max_ctx + 2 * B, max_draft=max_draft)
+    N = op.N                                    # drafts verified per step
     with gemm_accumulation("f32"):
         op32.prefill(prompt)
     op32.anchor = first
@@ -125,23 +130,23 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         assert derr <= max(tl, 2 * dfloor)
         sched.fill_(int(k))
         pair.inject(ref, sched, fill[s:s + 1].contiguous())
-        block = pair.block[:B].cpu().numpy()
+        block = pair.block[:N + 1].cpu().numpy()
         pair.verify(vlog)
-        y = pair.y[:B].cpu().numpy()
+        y = pair.y[:N + 1].cpu().numpy()
         fwd = op.t.forward([int(t) for t in block])
         with gemm_accumulation("f32"):
             fwd32 = op32.t.forward([int(t) for t in block])
         vm = top2_margin(fwd["logits"])
-        verr = float(np.max(np.abs(vlog.cpu().numpy() - fwd["logits"])))
+        verr = float(np.max(np.abs(vlog[:N + 1].cpu().numpy() - fwd["logits"])))
         vfloor = float(np.max(np.abs(fwd32["logits"] - fwd["logits"])))
         compare_tokens(y, argmax_first(fwd["logits"]), vm, stats, vfloor)
-        herr = float(np.max(np.abs(pair.side().cpu().numpy() - fwd["hidden"])))
+        herr = float(np.max(np.abs(pair.side()[:N + 1].cpu().numpy() - fwd["hidden"])))
         hfloor = float(np.max(np.abs(fwd32["hidden"] - fwd["hidden"])))
         print(f"[{cfg.name} step {s}] verify logits max err {verr:.3e} (floor {vfloor:.3e}), hidden max err "
               f"{herr:.3e} (floor {hfloor:.3e}, |hidden| max {np.max(np.abs(fwd['hidden'])):.2f}), "
               f"a={int(pair.acc.item())}", flush=True)
         assert verr <= max(tl, 2 * vfloor)
-        check_hidden(cfg, pair.side().cpu().numpy(), fwd["hidden"], hfloor)
+        check_hidden(cfg, pair.side()[:N + 1].cpu().numpy(), fwd["hidden"], hfloor)
         pair.accept()
         pair.commit()
         a = int(pair.acc.item())
@@ -149,7 +154,7 @@ def lockstep(cfg, P, forced, gdn_exact=False):
         if np.all(vm[:max(a, a_o) + 1] >= max(TIE, 2 * vfloor)):
             assert a == a_o
             if on_ref:
-                assert a == k, "injected acceptance not realised"
+                assert a == min(k, N), "injected acceptance not realised"
         emit = pair.emit[:a + 1].cpu().numpy()
         assert emit.tolist() == [int(t) for t in block[1:a + 1]] + [int(y[a])]
         if gdn_exact:
@@ -178,6 +183,32 @@ def test_tiny_generate_equals_oracle_greedy():
     pair = Pair(cfg, ck, max_ctx=256)
     out = pair.generate(pr, cfg.new_tokens)
     assert out == ref
+
+
+@pytest.mark.parametrize("max_draft", [1, 5])
+def test_tiny_generate_with_draft_cap_equals_oracle_greedy(max_draft):
+    cfg = C.tiny()
+    ck = synth.make_pair(cfg)
+    pr = synth.prompt(cfg, 64)
+    ref = greedy(cfg, ck, pr, cfg.new_tokens, cap=256)
+    pair = Pair(cfg, ck, max_ctx=256)
+    assert pair.set_max_draft(max_draft) == max_draft + 1      # fp32: no row quantum
+    out = pair.generate(pr, cfg.new_tokens)
+    assert out == ref
+    acc = pair.acc_log().cpu().numpy()[:pair.query()["steps"]]
+    assert acc.max() <= max_draft
+
+
+def test_reduced_8b_lockstep_draft_cap_half_block():
+    # 15 of 31 drafts: the verify runs 16 rows, one token block in every GEMM
+    cfg = reduced("8b")
+    _, _, stats, _ = lockstep(cfg, 300, [0, 31, 9, 15, 4], max_draft=15)
+    assert stats["compared"] >= 5 * 16
+
+
+def test_tiny_hybrid_lockstep_draft_cap():
+    cfg = tiny_hybrid_config()
+    lockstep(cfg, 16, [0, 15, 6, 2], gdn_exact=True, max_draft=6)
 
 
 def test_tiny_lockstep_injected():

@@ -145,3 +145,50 @@ def test_bf16_stack_rounds_activations():
     from oracle.numerics import round_bf16
     assert np.array_equal(round_bf16(f["hidden"]), f["hidden"])
     assert np.array_equal(round_bf16(t.K[0]), t.K[0])
+
+
+@pytest.mark.parametrize("max_draft", [1, 2, 6, 0])
+def test_draft_cap_is_lossless_and_bounds_acceptance(tiny, max_draft):
+    # a cap on the drafts verified per step changes how many tokens a step
+    # emits, never which tokens: the output stays plain greedy decoding
+    cfg, ck, pr = tiny
+    ref = greedy(cfg, ck, pr, cfg.new_tokens, cap=256)
+    op = OraclePair(cfg, ck, cap=256, max_draft=max_draft)
+    out = op.generate(pr, cfg.new_tokens)
+    assert out == ref
+    N = cfg.block - 1 if max_draft == 0 else max_draft
+    for rec in op.steps:
+        assert len(rec["block"]) == N + 1            # anchor + verified drafts
+        assert rec["logits"].shape[0] == N + 1
+        assert 0 <= rec["a"] <= N
+        assert len(rec["emitted"]) == rec["a"] + 1
+
+
+@pytest.mark.parametrize("max_draft", [3, 9])
+def test_draft_cap_realises_min_of_forced_and_cap(tiny, max_draft):
+    cfg, ck, pr = tiny
+    ref_tail = greedy(cfg, ck, pr, 200, cap=512)
+    ref = list(pr) + ref_tail
+    ks = synth.accept_schedule(cfg, 64, forced=[0, 15, 2, 7, 12])
+    fill = synth.filler_tokens(cfg, 64)
+    op = OraclePair(cfg, ck, cap=512, max_draft=max_draft)
+    op.prefill(pr)
+    out = [op.anchor]
+    s = 0
+    while len(out) < 96:
+        k = int(ks[s])
+        rec = op.step(lambda d, n: inject_drafts(d, n, k, ref, fill[s], cfg.target.vocab))
+        assert rec["a"] == min(k, max_draft)
+        out += rec["emitted"]
+        s += 1
+    assert out[:96] == ref_tail[:96]
+
+
+def test_draft_cap_lossless_tiny_hybrid():
+    cfg = tiny_hybrid_config()
+    ck = synth.make_pair(cfg)
+    pr = synth.prompt(cfg, 40)
+    ref = greedy(cfg, ck, pr, 40, cap=256)
+    op = OraclePair(cfg, ck, cap=256, max_draft=4)
+    assert op.generate(pr, 40) == ref
+    assert all(rec["a"] <= 4 for rec in op.steps)
