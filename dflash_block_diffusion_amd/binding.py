@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int, c_int32, c_int64,
+from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_uint64,
                     c_size_t, c_void_p)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,12 @@ SIGNATURES = {
     "dflash_verify_block": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_accept": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_set_max_draft": (c_int, [c_void_p, c_int, POINTER(c_int), POINTER(c_int)]),
+    "dflash_set_sampling": (c_int, [c_void_p, c_float, c_uint64]),
+    "dflash_accept_sampled": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dflash_sample_logits": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_uint64, c_int, c_int, c_int,
+                                     c_void_p, c_void_p, c_void_p]),
+    "dflash_accept_logits": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_uint64, c_int,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_kv_commit": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_kv_rollback": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
     "dflash_gdn_snapshot": (c_int, [c_void_p, c_void_p]),

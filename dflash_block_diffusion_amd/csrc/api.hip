@@ -270,6 +270,11 @@ struct dflash_state {
   int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
   int vrows = 0;          // rows a verify runs (B, or fewer under a draft cap)
   int max_draft = 0;      // drafts verified per step (0 = the whole block)
+  float temp = 0.f;       // sampling temperature (0 = greedy)
+  uint64_t seed = 0;
+  float* dlog = nullptr;  // [B][vocab] drafter logits of slots 1..B-1 (sampling)
+  float* vlog = nullptr;  // [B][vocab] target logits of the verify rows (sampling)
+  float* lse = nullptr;   // [2][B] log-normalisers at T: drafter slots, target rows
   char* base = nullptr;
   size_t bytes = 0;
   int32_t* scal = nullptr;
@@ -376,6 +381,9 @@ static void carve(dflash_state* s, Carver& c) {
   s->gdn_S = t->n_gdn ? c.take<float>(sf) : nullptr;
   s->gdn_snap = t->n_gdn ? c.take<float>(sf) : nullptr;
   s->gdn_tape = t->n_gdn ? c.take<float>((size_t)t->n_gdn * B * t->d.gdn_heads * gdn_rec(t)) : nullptr;
+  s->dlog = c.take<float>((size_t)B * t->d.vocab);
+  s->vlog = c.take<float>((size_t)B * t->d.vocab);
+  s->lse = c.take<float>((size_t)2 * B);
 }
 
 static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model* d, int max_ctx, int block) {
@@ -560,7 +568,16 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
     RC(ffn(s, d, d->layers[l], pend, B, st, nullptr, 0, 0, 0));
   }
   RC(norm(s, d, pend, d->d.final_norm, s->bu, t->gin, B, st));
-  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 1, block + 1));
+  const int V = t->d.vocab;
+  if (s->temp > 0.f) {
+    // slots 1..B-1 draw from softmax(z / T); their logits stay for the acceptance
+    RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, s->dlog, V, 1, block + 1));
+    HIPCHK(launch_sample_rows(s->dlog, V, V, B - 1, s->temp, s->seed, s->scal + SC_N, 0, 1, 0, block + 1, s->lse,
+                              st));
+    if (logits) HIPCHK(hipMemcpyAsync(logits, s->dlog, (size_t)(B - 1) * V * 4, hipMemcpyDeviceToDevice, st));
+    return DFLASH_OK;
+  }
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, V, 1, block + 1));
   return DFLASH_OK;
 }
 
@@ -599,7 +616,14 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
     RC(ffn(s, t, L, pend, B, st, side, d->d.n_sel * H, d->gin, col0));
   }
   RC(norm(s, t, pend, t->d.final_norm, s->bu, t->gin, B, st));
-  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, t->d.vocab, 0, argmax));
+  const int V = t->d.vocab;
+  if (s->temp > 0.f) {
+    // the acceptance reads the target's tempered distributions of these rows
+    RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, s->vlog, V, 0, argmax));
+    if (logits) HIPCHK(hipMemcpyAsync(logits, s->vlog, (size_t)B * V * 4, hipMemcpyDeviceToDevice, st));
+    return DFLASH_OK;
+  }
+  RC(gemm(s, t->lm, s->bu, H, B, EPI_ARGMAX, st, nullptr, nullptr, 0, logits, V, 0, argmax));
   return DFLASH_OK;
 }
 
@@ -630,11 +654,14 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
   int last = 0;
   for (int c0 = 0; c0 < n_tokens; c0 += s->B) {
     const int len = std::min(s->B, n_tokens - c0);
-    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, s->B, st));
+    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, s->B, st));   // logits land in vlog when sampling
     RC(do_commit(s, nullptr, len, nullptr, st));
     RC(do_draft(s, s->blk, nullptr, st));          // appends the chunk's drafter context rows
     last = len;
   }
+  if (s->temp > 0.f)   // the first token is a draw from the last prompt row at T (stream 3, counter (P, 0))
+    HIPCHK(launch_sample_rows(s->vlog + (size_t)(last - 1) * t->d.vocab, t->d.vocab, t->d.vocab, 1, s->temp,
+                              s->seed, nullptr, n_tokens, 0, 3, s->ybuf + last - 1, nullptr, st));
   HIPCHK(launch_copy_tokens(s->ybuf + last - 1, s->tokens + n_tokens, 1, st));
   HIPCHK(launch_copy_tokens(s->ybuf + last - 1, d_first, 1, st));
   HIPCHK(launch_set_scalars(s->scal, -1, 0, 0, st));
@@ -674,6 +701,60 @@ extern "C" int dflash_set_max_draft(dflash_state* s, int max_draft, int* h_verif
   s->vrows = V;
   if (h_verify_rows) *h_verify_rows = V;
   if (h_accept_block) *h_accept_block = N + 1;
+  return DFLASH_OK;
+}
+
+// Temperature sampling (mlx-dspark v0.0.3 "Highlights": --temperature T > 0
+// is an exact sample of the target at T).
+extern "C" int dflash_set_sampling(dflash_state* s, float temperature, uint64_t seed) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "temperature must be finite and >= 0");
+  s->temp = temperature;
+  s->seed = seed;
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_accept_sampled(dflash_state* s, const int32_t* d_block, int32_t* d_accept, int32_t* d_emit,
+                                     int32_t* d_next_anchor, void* stream) {
+  if (!s || !d_block || !d_accept || !d_emit) return fail(DFLASH_E_INVALID, "null argument");
+  if (!(s->temp > 0.f)) return fail(DFLASH_E_UNSUPPORTED, "sampling is off (temperature 0): use dflash_accept");
+  hipStream_t st = (hipStream_t)stream;
+  const int V = s->t->d.vocab;
+  const int N = s->max_draft == 0 ? s->B - 1 : std::min(s->max_draft, s->B - 1);
+  HIPCHK(launch_sample_rows(s->vlog, V, V, N + 1, s->temp, s->seed, s->scal + SC_N, 0, 0, -1, nullptr,
+                            s->lse + s->B, st));
+  HIPCHK(launch_spec_accept(d_block, s->dlog, s->vlog, V, N, s->lse, s->lse + s->B, s->temp, s->seed,
+                            s->scal + SC_N, 0, s->B, d_accept, d_emit, d_next_anchor, st));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_sample_logits(const float* d_logits, int ld, int rows, int vocab, float temperature,
+                                    uint64_t seed, int n, int row0, int stream_id, int32_t* d_tokens, float* d_lse,
+                                    void* stream) {
+  if (!d_logits || (!d_tokens && stream_id >= 0)) return fail(DFLASH_E_INVALID, "null argument");
+  if (rows < 0 || vocab < 1 || ld < vocab || n < 0 || row0 < 0 || stream_id > 3)
+    return fail(DFLASH_E_SHAPE, "bad shape or counter");
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(DFLASH_E_SHAPE, "temperature must be > 0");
+  HIPCHK(launch_sample_rows(d_logits, ld, vocab, rows, temperature, seed, nullptr, n, row0, stream_id, d_tokens,
+                            d_lse, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_accept_logits(const int32_t* d_block, const float* d_dlog, const float* d_vlog, int vocab,
+                                    int n_drafts, int block, float temperature, uint64_t seed, int n,
+                                    float* d_lse, int32_t* d_accept, int32_t* d_emit, int32_t* d_next_anchor,
+                                    void* stream) {
+  if (!d_block || !d_dlog || !d_vlog || !d_lse || !d_accept || !d_emit) return fail(DFLASH_E_INVALID, "null argument");
+  if (vocab < 1 || n < 0 || block < 2 || block > 64 || n_drafts < 1 || n_drafts >= block)
+    return fail(DFLASH_E_SHAPE, "need 1 <= n_drafts < block <= 64");
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(DFLASH_E_SHAPE, "temperature must be > 0");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(launch_sample_rows(d_dlog, vocab, vocab, n_drafts, temperature, seed, nullptr, n, 1, -1, nullptr, d_lse, st));
+  HIPCHK(launch_sample_rows(d_vlog, vocab, vocab, n_drafts + 1, temperature, seed, nullptr, n, 0, -1, nullptr,
+                            d_lse + block, st));
+  HIPCHK(launch_spec_accept(d_block, d_dlog, d_vlog, vocab, n_drafts, d_lse, d_lse + block, temperature, seed,
+                            nullptr, n, block, d_accept, d_emit, d_next_anchor, st));
   return DFLASH_OK;
 }
 

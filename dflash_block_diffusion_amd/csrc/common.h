@@ -182,6 +182,21 @@ struct AttnCall {
 };
 hipError_t launch_attention(const AttnCall& c, hipStream_t s);
 
+// Temperature sampling (csrc/sample.hip).  launch_sample_rows: per row of
+// logits ([rows][ld] fp32) the log-normaliser log sum exp(z/T) -> out_lse[r]
+// (if not null) and, for stream >= 0, a draw from softmax(z/T) with Philox
+// counter (n, row0 + r, stream), n = *dev_n + n_add (n_add when dev_n is
+// null) -> out_tok[r].  launch_spec_accept: speculative-sampling acceptance
+// over N verified drafts plus the correction/bonus draw (accept/emit/next
+// anchor as dflash_accept).
+hipError_t launch_sample_rows(const float* logits, int ld, int vocab, int rows, float temperature, uint64_t seed,
+                              const int* dev_n, int n_add, int row0, int stream, int32_t* out_tok, float* out_lse,
+                              hipStream_t s);
+hipError_t launch_spec_accept(const int32_t* block, const float* dlog, const float* vlog, int vocab, int N,
+                              const float* lse_q, const float* lse_p, float temperature, uint64_t seed,
+                              const int* dev_n, int n_add, int B, int32_t* acc, int32_t* emit,
+                              int32_t* next_anchor, hipStream_t s);
+
 // Residual update + RMSNorm of `rows` rows of width h, one work-group per row:
 //   NORM_ONLY  v = x
 //   NORM_RESID v = round(x + round(sum of in)); x <- v; side copy of v (optional)

@@ -160,6 +160,7 @@ class Pair:
         check(lib().dflash_state_buffers(self.st, byref(self.view)))
         self.prompt_len = 0
         self.vrows, self.accept_block = self.B, self.B
+        self.temperature = 0.0
 
     # ------------------------------------------------------------- views
     def _arena_slice(self, addr: int, nbytes: int, dtype) -> torch.Tensor:
@@ -217,7 +218,16 @@ class Pair:
         self.vrows, self.accept_block = v.value, a.value
         return self.vrows
 
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """Speculative sampling at `temperature` (0 = greedy) with Philox seed `seed`."""
+        check(lib().dflash_set_sampling(self.st, float(temperature), int(seed) & (2 ** 64 - 1)))
+        self.temperature = float(temperature)
+
     def accept(self):
+        if self.temperature > 0:
+            check(lib().dflash_accept_sampled(self.st, ptr(self.block), ptr(self.acc), ptr(self.emit),
+                                              ptr(self.block), stream_handle()))
+            return
         check(lib().dflash_accept(ptr(self.block), ptr(self.y), self.accept_block, ptr(self.acc), ptr(self.emit),
                                   ptr(self.block), stream_handle()))
 

@@ -221,6 +221,52 @@ int dflash_verify_block(dflash_state *st, const int32_t *d_block, int32_t *d_arg
  * calls enqueue, so a captured graph must be recaptured. */
 int dflash_set_max_draft(dflash_state *st, int max_draft, int *h_verify_rows, int *h_accept_block);
 
+/* Temperature sampling (mlx-dspark v0.0.3, "Highlights": --temperature T > 0
+ * stays lossless, an exact sample of the target at T).  temperature 0 (the
+ * default) is greedy decoding; T > 0 switches later calls to speculative
+ * sampling: dflash_draft_block draws slot j from softmax(z_j / T) of the
+ * drafter's logits; dflash_verify_block keeps the target's logits of its
+ * rows; dflash_accept_sampled (instead of dflash_accept) keeps d_j while
+ * u_j < p_{j-1}(d_j) / q_j(d_j) and draws the correction from
+ * max(0, p_a - q_{a+1}) renormalised, or a bonus token from p_N when all N
+ * verified drafts are kept; dflash_prefill draws the first token from the
+ * last prompt row.  Uniforms: Philox4x32-10 (Salmon et al., SC 2011) with
+ * counter (n, row, stream, 0) and key (seed low 32 bits, seed high 32 bits),
+ * n the committed length at the start of the step; stream 0 drafts, 1
+ * acceptance tests, 2 correction/bonus, 3 first token (counter (P, 0, 3, 0)).
+ * Errors: DFLASH_E_INVALID (null state), DFLASH_E_SHAPE (T < 0 or not
+ * finite).  Host-only call; recapture a graph after changing it. */
+int dflash_set_sampling(dflash_state *st, float temperature, uint64_t seed);
+
+/* Speculative-sampling acceptance of the last draft+verify at the state's
+ * temperature, over the N drafts the verify checked (dflash_set_max_draft):
+ * d_accept[0] = a; d_emit[0..a-1] = d_1..d_a, d_emit[a] = the drawn
+ * correction or bonus token, d_emit[a+1..B-1] = -1; d_next_anchor (may alias
+ * d_block, may be NULL) receives d_emit[a].  Reads the drafter and target
+ * logits the state kept from those calls.  Errors: DFLASH_E_INVALID (null
+ * argument), DFLASH_E_UNSUPPORTED (temperature 0), DFLASH_E_DEVICE. */
+int dflash_accept_sampled(dflash_state *st, const int32_t *d_block, int32_t *d_accept, int32_t *d_emit,
+                          int32_t *d_next_anchor, void *stream);
+
+/* Stateless forms of the two sampling steps, on caller logits (fp32, device):
+ * dflash_sample_logits: for r < rows, the log-normaliser log sum_v
+ * exp(logits[r][v] / T) -> d_lse[r] (may be NULL) and, for stream_id in
+ * [0, 3], a draw from softmax(logits[r] / T) with counter (n, row0 + r,
+ * stream_id) -> d_tokens[r]; stream_id < 0 computes d_lse only.  Row r
+ * starts at d_logits + r*ld (ld >= vocab).
+ * dflash_accept_logits: the acceptance of dflash_accept_sampled for one
+ * block: d_block[0..block-1] (anchor, drafts), d_dlog [n_drafts][vocab] the
+ * drafter logits of slots 1..n_drafts, d_vlog [n_drafts+1][vocab] the target
+ * logits of rows 0..n_drafts, n the committed length of the step;
+ * d_lse [2*block] fp32 is caller scratch.  Outputs as dflash_accept_sampled.
+ * Errors: DFLASH_E_INVALID (null pointer), DFLASH_E_SHAPE (sizes, counter,
+ * T <= 0).  Neither allocates. */
+int dflash_sample_logits(const float *d_logits, int ld, int rows, int vocab, float temperature, uint64_t seed,
+                         int n, int row0, int stream_id, int32_t *d_tokens, float *d_lse, void *stream);
+int dflash_accept_logits(const int32_t *d_block, const float *d_dlog, const float *d_vlog, int vocab,
+                         int n_drafts, int block, float temperature, uint64_t seed, int n, float *d_lse,
+                         int32_t *d_accept, int32_t *d_emit, int32_t *d_next_anchor, void *stream);
+
 /* Longest-prefix acceptance: a = max{k <= B-1 : d_block[j] == d_argmax[j-1]
  * for all 1 <= j <= k}.  d_accept[0] = a; d_emit[0..a-1] = drafts d_1..d_a,
  * d_emit[a] = d_argmax[a] (the correction), d_emit[a+1..B-1] = -1.

@@ -23,6 +23,10 @@ only the first min(N, B-1) drafts are verified -- the target forward runs the
 anchor and those drafts and a <= N; 0 verifies the whole block.  The drafter
 still drafts the whole block.
 
+Temperature T > 0 (mlx-dspark v0.0.3, "Highlights"): drafts are sampled
+from the drafter's tempered distributions and accepted by the speculative
+sampling rule of oracle/sampling.py; T = 0 is the greedy loop above.
+
 Greedy speculative output equals plain greedy decoding of the target
 (mlx-dspark v0.0.3 intro; agentlens summary, "Highlights") -- the invariant
 tests check on this oracle.
@@ -37,6 +41,7 @@ from .gdn import gdn_layer, recurrence
 from .model import (F64, LAYER_ATTN, Shape, argmax_first, attention, ffn_block,
                     norm_rope, qkv_heads, rmsnorm, rope_table, top2_margin)
 from .numerics import linear, rounder
+from .sampling import STREAM_FIRST, categorical, draft_samples, spec_accept, tempered, uniform
 
 
 class OracleTarget:
@@ -201,8 +206,10 @@ def inject_drafts(drafts, n: int, k: int, ref, filler_row, vocab: int):
 
 
 class OraclePair:
-    def __init__(self, cfg, ckpt: Dict, cap: int, max_draft: int = 0):
+    def __init__(self, cfg, ckpt: Dict, cap: int, max_draft: int = 0, temperature: float = 0.0,
+                 seed: int = 0):
         self.cfg = cfg
+        self.T, self.seed = float(temperature), int(seed)
         self.B = cfg.block
         # drafts verified per step
         self.N = self.B - 1 if max_draft == 0 else min(int(max_draft), self.B - 1)
@@ -220,7 +227,11 @@ class OraclePair:
         self.t.commit(fwd, P - 1)
         self.d.ctx_append(fwd["hidden"], np.arange(P))
         self.anchor = int(argmax_first(fwd["logits"][-1]))
+        if self.T > 0:
+            self.anchor = categorical(tempered(fwd["logits"][-1], self.T),
+                                      uniform(self.seed, P, 0, STREAM_FIRST))
         self.prefill_margin = float(top2_margin(fwd["logits"][-1]))
+        self.prefill_logits = fwd["logits"][-1]
         self.seq = prompt + [self.anchor]
         return self.anchor
 
@@ -229,23 +240,31 @@ class OraclePair:
         overwrite the drafts (benchmark acceptance schedule)."""
         n = self.t.n
         drafts, dlogits = self.d.draft(self.anchor, n)
+        if self.T > 0:
+            drafts = np.array(draft_samples(dlogits, self.T, self.seed, n), dtype=np.int64)
         raw = drafts.copy()
         if inject is not None:
             drafts = inject(drafts, n)
         block = [self.anchor] + [int(t) for t in drafts[:self.N]]
         fwd = self.t.forward(block)
         y = argmax_first(fwd["logits"]).astype(np.int64)
-        a = accept_length(drafts[:self.N], y)
+        sample_info = None
+        if self.T > 0:
+            a, nxt, sample_info = spec_accept(drafts[:self.N], dlogits[:self.N], fwd["logits"], self.T,
+                                              self.seed, n)
+        else:
+            a = accept_length(drafts[:self.N], y)
+            nxt = int(y[a])
         self.t.commit(fwd, a)
         self.d.ctx_append(fwd["hidden"][: a + 1], n + np.arange(a + 1))
-        emitted = [int(t) for t in drafts[:a]] + [int(y[a])]
-        self.anchor = int(y[a])
+        emitted = [int(t) for t in drafts[:a]] + [int(nxt)]
+        self.anchor = int(nxt)
         self.seq += emitted
         rec = {"n": n, "block": block, "raw_drafts": raw, "drafts": drafts, "y": y,
                "a": a, "emitted": emitted, "draft_logits": dlogits,
                "logits": fwd["logits"], "hidden": fwd["hidden"],
                "draft_margin": top2_margin(dlogits),
-               "verify_margin": top2_margin(fwd["logits"]), "fwd": fwd}
+               "verify_margin": top2_margin(fwd["logits"]), "fwd": fwd, "sample": sample_info}
         self.steps.append(rec)
         return rec
 
