@@ -169,6 +169,8 @@ def main():
     ap.add_argument("--no-prof", action="store_true")
     ap.add_argument("--max-draft", type=int, default=0,
                     help="verify only the first N drafts per step (0 = the whole block)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="speculative sampling at this temperature (drafts drawn, no injection)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the draft+verify step of one sequence runs on a single "
@@ -198,26 +200,30 @@ def main():
     torch.cuda.empty_cache()
     log(f"model ready in {time.time() - t0:.1f} s ({cfg.name}, {(pair.t.weight_bytes() + pair.d.weight_bytes()) / 1e9:.2f} GB)")
 
+    sampling = args.temperature > 0
+    if sampling:
+        pair.set_sampling(args.temperature, args.seed + 17)
     prompt = synth.prompt(cfg, ctx, seed=1)
     t0 = time.time()
     pair.prefill(prompt)
     pair.snapshot()
     log(f"prefill {ctx} tokens in {time.time() - t0:.2f} s")
-    # reference greedy stream: the lossless loop itself, no injection
-    need = ctx + (W + K + 3) * B
-    t0 = time.time()
-    while pair.query()["n"] < need:
-        for _ in range(8):
-            pair.step()
-    n_ref = pair.query()["n"]
-    ref = pair.tokens(n_ref + 1).clone()
-    pair.rollback(ctx)
-    log(f"reference stream of {n_ref - ctx} tokens in {time.time() - t0:.1f} s")
-
     n_sched = W + K + 8
     sched = torch.as_tensor(synth.accept_schedule(cfg, n_sched, seed=2), device="cuda")
-    filler = torch.as_tensor(synth.filler_tokens(cfg, n_sched, seed=3), device="cuda")
-    inj = (ref, sched, filler)
+    inj = None
+    if not sampling:
+        # reference greedy stream: the lossless loop itself, no injection
+        need = ctx + (W + K + 3) * B
+        t0 = time.time()
+        while pair.query()["n"] < need:
+            for _ in range(8):
+                pair.step()
+        n_ref = pair.query()["n"]
+        ref = pair.tokens(n_ref + 1).clone()
+        pair.rollback(ctx)
+        log(f"reference stream of {n_ref - ctx} tokens in {time.time() - t0:.1f} s")
+        filler = torch.as_tensor(synth.filler_tokens(cfg, n_sched, seed=3), device="cuda")
+        inj = (ref, sched, filler)
     # capture one step
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -254,7 +260,7 @@ def main():
     if q["status"] != 0:
         log(f"WARNING: device status word {q['status']}")
     log(f"timed {K} steps: {ms:.3f} ms, n {ctx} -> {q['n']}, accepted {a_run.tolist()}, "
-        f"schedule {a_sched.tolist()}")
+        + ("drafts sampled (natural acceptance)" if sampling else f"schedule {a_sched.tolist()}"))
 
     steps_per_s = K / (ms / 1e3)
     tok_per_s = tokens / (ms / 1e3)
@@ -319,7 +325,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {fmt_name[cfg.target.fmt]} target {cfg.target.n_layers} layers "
                                 f"H{cfg.target.hidden} + {fmt_name[cfg.drafter.fmt]} drafter "
-                                f"{cfg.drafter.n_layers} layers, block {B}, ctx {ctx}, injected acceptance"
+                                f"{cfg.drafter.n_layers} layers, block {B}, ctx {ctx}, "
+                                + (f"temperature {args.temperature} (drafts sampled, natural acceptance)"
+                                   if sampling else "injected acceptance")
                                 + (f", draft cap {n_drafts} ({pair.vrows} verify rows)" if args.max_draft else "")),
                    "block": B, "ctx": ctx, "global_batch": 1, "verify_rows": pair.vrows, "drafts_verified": n_drafts,
                    "target_format": fmt_name[cfg.target.fmt], "drafter_format": fmt_name[cfg.drafter.fmt]},
