@@ -16,10 +16,11 @@
 // bonus, 3 = the first token after the prompt.  u = (x0 / 2^8 + 1/2) / 2^24.
 //
 // A categorical draw over a vocabulary row is one work-group of 1024
-// threads: each thread owns a contiguous chunk of the row, the chunk sums are
-// scanned in a fixed order, and the thread whose interval holds u * sum walks
-// its chunk; the drawn index is the smallest v whose running sum exceeds
-// u * sum.  Every sum has a fixed order, so a draw is bit-reproducible.
+// threads: the row is cut into tiles of 1024 consecutive entries, the tile
+// sums are formed with coalesced loads and prefixed in index order, and the
+// work-group scans the tile that holds u * sum; the drawn index is the
+// smallest v whose running sum exceeds u * sum.  Every sum has a fixed
+// order, so a draw is bit-reproducible.
 #include "common.h"
 
 namespace dfl {
@@ -63,44 +64,69 @@ __device__ float wg_max(float v, float* red) {
 }
 
 // Smallest v in [0, vocab) whose running sum of w exceeds u * sum(w); -1 when
-// sum(w) is 0.  Every thread returns the same index.
+// sum(w) is 0.  Every thread returns the same index.  The row is cut into
+// tiles of 1024 consecutive entries: the 16 waves form the tile sums with
+// coalesced loads (wave w takes tiles w, w+16, ...; fixed reduction order),
+// one thread turns them into exclusive prefixes, and the work-group scans
+// the one tile that holds u * sum.
+constexpr int CAT_TILE = SAMPLE_THREADS;
+constexpr int CAT_MAX_TILES = 256;            // vocab up to 262144
 template <class W>
-__device__ int wg_categorical(const W& w, int vocab, float u, float* scan, int* pick, float* total) {
-  const int t = threadIdx.x;
-  const int chunk = (vocab + SAMPLE_THREADS - 1) / SAMPLE_THREADS;
-  const int v0 = min(t * chunk, vocab), v1 = min(v0 + chunk, vocab);
-  float s = 0.f;
-  for (int v = v0; v < v1; ++v) s += w(v);
-  // inclusive scan of the chunk sums, Hillis-Steele (fixed order)
-  scan[t] = s;
-  if (t == 0) *pick = -1;
-  __syncthreads();
-  for (int o = 1; o < SAMPLE_THREADS; o <<= 1) {
-    const float add = t >= o ? scan[t - o] : 0.f;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  const float incl = scan[t], excl = t ? scan[t - 1] : 0.f;
-  const float S = scan[SAMPLE_THREADS - 1];
-  if (t == 0) *total = S;
-  float target = u * S;
-  if (target >= S) target = S * 0.99999994f;      // u * S rounded up to the total
-  if (S > 0.f && s > 0.f && excl <= target && target < incl) {
-    float c = excl;
-    int last = -1, got = -1;
-    for (int v = v0; v < v1; ++v) {
-      const float x = w(v);
-      if (x > 0.f) {
-        last = v;
-        c += x;
-        if (c > target) { got = v; break; }
-      }
+__device__ int wg_categorical(const W& w, int vocab, float u, float* scan, float* tile, int* pick, float* total) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int ntiles = (vocab + CAT_TILE - 1) / CAT_TILE;
+  for (int k = wave; k < ntiles; k += SAMPLE_THREADS / 64) {
+    float s = 0.f;
+#pragma unroll 4
+    for (int e = 0; e < CAT_TILE / 64; ++e) {
+      const int v = k * CAT_TILE + e * 64 + lane;
+      if (v < vocab) s += w(v);
     }
-    atomicMax(pick, got >= 0 ? got : last);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) tile[k] = s;
   }
   __syncthreads();
-  const int r = *pick;
+  if (t == 0) {
+    float acc = 0.f;
+    for (int k = 0; k < ntiles; ++k) {
+      const float x = tile[k];
+      tile[k] = acc;                           // exclusive prefix
+      acc += x;
+    }
+    tile[ntiles] = acc;
+    *total = acc;
+    pick[0] = 0x7fffffff;
+    pick[1] = -1;
+    pick[2] = -1;
+  }
+  __syncthreads();
+  const float S = *total;
+  int r = -1;
+  if (S > 0.f) {
+    float target = u * S;
+    if (target >= S) target = S * 0.99999994f;    // u * S rounded up to the total
+    if (t < ntiles && tile[t] <= target && target < tile[t + 1]) pick[2] = t;
+    __syncthreads();
+    const int k = pick[2] < 0 ? ntiles - 1 : pick[2];
+    const int v = k * CAT_TILE + t;
+    const float x = v < vocab ? w(v) : 0.f;
+    // inclusive scan of the tile, Hillis-Steele (fixed order)
+    scan[t] = x;
+    __syncthreads();
+    for (int o = 1; o < SAMPLE_THREADS; o <<= 1) {
+      const float add = t >= o ? scan[t - o] : 0.f;
+      __syncthreads();
+      scan[t] += add;
+      __syncthreads();
+    }
+    if (x > 0.f) {
+      if (tile[k] + scan[t] > target) atomicMin(&pick[0], v);
+      atomicMax(&pick[1], v);                    // last entry of the tile with weight
+    }
+    __syncthreads();
+    r = pick[0] != 0x7fffffff ? pick[0] : pick[1];
+  }
   __syncthreads();
   return r;
 }
@@ -114,7 +140,8 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_rows_kernel(const float
                                                                     int stream, int32_t* out_tok,
                                                                     float* out_lse) {
   __shared__ float red[SAMPLE_THREADS];
-  __shared__ int pick;
+  __shared__ float tile[CAT_MAX_TILES + 1];
+  __shared__ int pick[3];
   __shared__ float total;
   const int r = blockIdx.x, t = threadIdx.x;
   const float* z = logits + (size_t)r * ld;
@@ -123,12 +150,25 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_rows_kernel(const float
   const float M = wg_max(m, red);
   const float scale = invT;
   auto w = [&](int v) { return exp_f((z[v] - M) * scale); };
+  if (stream < 0) {
+    // normaliser only: strided (coalesced) sums, then a fixed-order tree
+    float sum = 0.f;
+    for (int v = t; v < vocab; v += SAMPLE_THREADS) sum += w(v);
+    red[t] = sum;
+    __syncthreads();
+    for (int o = SAMPLE_THREADS / 2; o > 0; o >>= 1) {
+      if (t < o) red[t] += red[t + o];
+      __syncthreads();
+    }
+    if (t == 0 && out_lse) out_lse[r] = M * invT + logf(red[0]);
+    return;
+  }
   const int n = (dev_n ? *dev_n : 0) + n_add;
-  const float u = stream >= 0 ? uniform01(seed, (uint32_t)n, (uint32_t)(row0 + r), (uint32_t)stream) : 0.5f;
-  const int tok = wg_categorical(w, vocab, u, red, &pick, &total);
+  const float u = uniform01(seed, (uint32_t)n, (uint32_t)(row0 + r), (uint32_t)stream);
+  const int tok = wg_categorical(w, vocab, u, red, tile, pick, &total);
   if (t == 0) {
     if (out_lse) out_lse[r] = M * invT + logf(total);
-    if (stream >= 0 && out_tok) out_tok[r] = tok;
+    if (out_tok) out_tok[r] = tok;
   }
 }
 
@@ -143,29 +183,30 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void spec_accept_kernel(
     const float* __restrict__ lse_q, const float* __restrict__ lse_p, float invT, uint64_t seed, const int* dev_n,
     int n_add, int B, int32_t* acc, int32_t* emit, int32_t* next_anchor) {
   __shared__ float scan[SAMPLE_THREADS];
-  __shared__ int pick;
+  __shared__ float tile[CAT_MAX_TILES + 1];
+  __shared__ int pick[3];
   __shared__ float total;
-  __shared__ int s_a;
+  __shared__ int s_fail;
   __shared__ int32_t drafts[64];
   const int t = threadIdx.x;
   const uint32_t n = (uint32_t)((dev_n ? *dev_n : 0) + n_add);
   if (t < B) drafts[t] = block[t];
+  if (t == 0) s_fail = N + 1;
   __syncthreads();
-  if (t == 0) {
-    int a = 0;
-    for (int j = 1; j <= N; ++j) {
-      const int d = drafts[j];
-      if (d < 0 || d >= vocab) break;           // not a token: rejected (q(d) undefined)
-      const float lp = vlog[(size_t)(j - 1) * vocab + d] * invT - lse_p[j - 1];
-      const float lq = dlog[(size_t)(j - 1) * vocab + d] * invT - lse_q[j - 1];
-      const float u = uniform01(seed, n, (uint32_t)j, 1u);
-      if (!(u < exp_f(lp - lq))) break;
-      a = j;
+  // thread j tests draft j (all N tests at once); a = first rejected j - 1
+  if (t >= 1 && t <= N) {
+    const int d = drafts[t];
+    bool keep = d >= 0 && d < vocab;           // not a token: rejected (q(d) undefined)
+    if (keep) {
+      const float lp = vlog[(size_t)(t - 1) * vocab + d] * invT - lse_p[t - 1];
+      const float lq = dlog[(size_t)(t - 1) * vocab + d] * invT - lse_q[t - 1];
+      const float u = uniform01(seed, n, (uint32_t)t, 1u);
+      keep = u < exp_f(lp - lq);
     }
-    s_a = a;
+    if (!keep) atomicMin(&s_fail, t);
   }
   __syncthreads();
-  const int a = s_a;
+  const int a = s_fail - 1;
   const float* y = vlog + (size_t)a * vocab;
   const float ly = lse_p[a];
   const float u = uniform01(seed, n, (uint32_t)a, 2u);
@@ -175,9 +216,9 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void spec_accept_kernel(
     const float* z = dlog + (size_t)a * vocab;      // slot a+1
     const float lz = lse_q[a];
     auto wr = [&](int v) { return fmaxf(exp_f(y[v] * invT - ly) - exp_f(z[v] * invT - lz), 0.f); };
-    tok = wg_categorical(wr, vocab, u, scan, &pick, &total);
+    tok = wg_categorical(wr, vocab, u, scan, tile, pick, &total);
   }
-  if (tok < 0) tok = wg_categorical(wp, vocab, u, scan, &pick, &total);
+  if (tok < 0) tok = wg_categorical(wp, vocab, u, scan, tile, pick, &total);
   for (int i = t; i < B; i += SAMPLE_THREADS) emit[i] = i < a ? drafts[i + 1] : (i == a ? tok : -1);
   if (t == 0) {
     acc[0] = a;
@@ -191,7 +232,7 @@ hipError_t launch_sample_rows(const float* logits, int ld, int vocab, int rows, 
                               const int* dev_n, int n_add, int row0, int stream, int32_t* out_tok, float* out_lse,
                               hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (!(temperature > 0.f) || vocab < 1) return hipErrorInvalidValue;
+  if (!(temperature > 0.f) || vocab < 1 || vocab > CAT_TILE * CAT_MAX_TILES) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sample_rows_kernel, dim3(rows), dim3(SAMPLE_THREADS), 0, s, logits, ld, vocab,
                      1.0f / temperature, seed, dev_n, n_add, row0, stream, out_tok, out_lse);
   return hipGetLastError();
@@ -201,7 +242,8 @@ hipError_t launch_spec_accept(const int32_t* block, const float* dlog, const flo
                               const float* lse_q, const float* lse_p, float temperature, uint64_t seed,
                               const int* dev_n, int n_add, int B, int32_t* acc, int32_t* emit,
                               int32_t* next_anchor, hipStream_t s) {
-  if (N < 1 || N >= B || B > 64 || vocab < 1 || !(temperature > 0.f)) return hipErrorInvalidValue;
+  if (N < 1 || N >= B || B > 64 || vocab < 1 || vocab > CAT_TILE * CAT_MAX_TILES || !(temperature > 0.f))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(spec_accept_kernel, dim3(1), dim3(SAMPLE_THREADS), 0, s, block, dlog, vlog, vocab, N, lse_q,
                      lse_p, 1.0f / temperature, seed, dev_n, n_add, B, acc, emit, next_anchor);
   return hipGetLastError();
