@@ -30,48 +30,52 @@ static constexpr float LOG2E = 1.4426950408889634f;
 // ------------------------------------------------------------ QK norm + RoPE
 __global__ __launch_bounds__(64) void qk_rope_kernel(RopeCall c) {
   const int row = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
-  const int n = *c.dev_n;
-  const int p = c.dev_p ? *c.dev_p : 0;
-  int pos;
-  if (row < c.block_rows) {
-    pos = n + row;
-  } else {
-    const int j = row - c.block_rows;
-    if (j >= p || head < c.hq) return;      // context rows only carry k/v
-    pos = n - p + j;
-  }
-  if (pos < 0 || pos >= c.capacity) return;
+  if (row >= c.block_rows && head < c.hq) return;      // context rows only carry k/v
   const int d = c.d, half = d >> 1;
   const bool act = lane < half;
   const int i = act ? lane : 0;
+  const bool kv = head >= c.hq;
+  const int kh = head - c.hq;
   const int src = head * d;                 // q heads, then k heads, then v heads
-  const float* gain = head < c.hq ? c.q_norm : c.k_norm;
-  // the QKV projection is materialised in the activation format
-  const float x1 = act ? act_round(c.atype, parts_sum(c.qkv, row, src + i)) : 0.f;
-  const float x2 = act ? act_round(c.atype, parts_sum(c.qkv, row, src + i + half)) : 0.f;
-  const float ss = wave_sum(x1 * x1 + x2 * x2);
-  const float r = 1.0f / sqrtf(ss / (float)d + c.eps);
-  const float a = x1 * r * gain[i];
-  const float b = x2 * r * gain[i + half];
+  const int vs = (c.hq + c.hkv + kh) * d;
+  const float* gain = kv ? c.k_norm : c.q_norm;
+  // the loads that do not depend on the committed length go out with it
+  float q1[MAX_SPLITS], q2[MAX_SPLITS], v1[MAX_SPLITS], v2[MAX_SPLITS];
+  parts_fetch(c.qkv, row, src + i, q1);
+  parts_fetch(c.qkv, row, src + i + half, q2);
+  if (kv) {
+    parts_fetch(c.qkv, row, vs + i, v1);
+    parts_fetch(c.qkv, row, vs + i + half, v2);
+  }
+  const float g1 = gain[i], g2 = gain[i + half];
+  const int n = *c.dev_n;
+  const int p = c.dev_p ? *c.dev_p : 0;
+  const int pos = row < c.block_rows ? n + row : n - p + (row - c.block_rows);
+  if ((row >= c.block_rows && row - c.block_rows >= p) || pos < 0 || pos >= c.capacity) return;
   const float cs = c.cos_t[(size_t)pos * half + i];
   const float sn = c.sin_t[(size_t)pos * half + i];
+  const int page = kv ? c.page_table[pos / PAGE] : 0;
+  // the QKV projection is materialised in the activation format
+  const float x1 = act ? act_round(c.atype, parts_add(c.qkv, q1)) : 0.f;
+  const float x2 = act ? act_round(c.atype, parts_add(c.qkv, q2)) : 0.f;
+  const float ss = wave_sum(x1 * x1 + x2 * x2);
+  const float r = 1.0f / sqrtf(ss / (float)d + c.eps);
+  const float a = x1 * r * g1;
+  const float b = x2 * r * g2;
   const float o1 = a * cs - b * sn;
   const float o2 = b * cs + a * sn;
   if (!act) return;
-  if (head < c.hq) {
+  if (!kv) {
     const size_t q = ((size_t)row * c.hq + head) * d;
     store_act(c.q_out, q + i, c.atype, o1);
     store_act(c.q_out, q + i + half, c.atype, o2);
   } else {
-    const int kh = head - c.hq;
-    const int page = c.page_table[pos / PAGE];
     const size_t slot = (((size_t)page * c.hkv + kh) * PAGE + (pos % PAGE)) * d;
     store_act(c.kc, slot + i, c.atype, o1);
     store_act(c.kc, slot + i + half, c.atype, o2);
-    const int vs = (c.hq + c.hkv + kh) * d;
     const size_t vt = ((size_t)page * c.hkv + kh) * PAGE * d + (pos % PAGE);   // V^T page: [d][64]
-    store_act(c.vc, vt + (size_t)i * PAGE, c.atype, parts_sum(c.qkv, row, vs + i));
-    store_act(c.vc, vt + (size_t)(i + half) * PAGE, c.atype, parts_sum(c.qkv, row, vs + i + half));
+    store_act(c.vc, vt + (size_t)i * PAGE, c.atype, parts_add(c.qkv, v1));
+    store_act(c.vc, vt + (size_t)(i + half) * PAGE, c.atype, parts_add(c.qkv, v2));
   }
 }
 
@@ -90,6 +94,11 @@ struct AttnArgs {
 };
 
 constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
+constexpr int ATTN_DMAS = 4 * ATTN_PAGES;            // K (or V^T) page DMAs per wave
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15: not waited on)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -127,20 +136,21 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, sidx = blockIdx.x;
-  const int n = *a.dev_n;
-  const int kv_len = n + a.B;
   const int key0 = sidx * ATTN_SPLIT;
-  if (key0 >= kv_len) return;                 // uniform over the work-group
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
 
   // 1. stage K / V^T of the split (pages past the table re-read the last one;
   //    their keys are masked below, and the arena holds finite values).  The
-  //    page indices are read first so that no load waits on another.
+  //    page indices and q are read together with the committed length, so
+  //    that no load waits on another; a split past the keys then leaves.
+  // (one vector load for the split's page indices: scalar loads of them
+  // would each wait for the previous one)
+  const int my_page = a.pt[min(key0 / PAGE + (lane % ATTN_PAGES), a.npages - 1)];
   size_t pbase[ATTN_PAGES];
 #pragma unroll
   for (int p = 0; p < ATTN_PAGES; ++p)
-    pbase[p] = ((size_t)a.pt[min(key0 / PAGE + p, a.npages - 1)] * a.hkv + h) * PAGE * D;
+    pbase[p] = ((size_t)__builtin_amdgcn_readlane(my_page, p) * a.hkv + h) * PAGE * D;
   const int rbi = blockIdx.z * 4 + wave;      // this wave's 16-row block
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
@@ -152,9 +162,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
   }
+  const int n = *a.dev_n;
+  const int kv_len = n + a.B;
+  if (key0 >= kv_len) return;                 // uniform over the work-group
   // K pages first, then V^T pages: the scores and the softmax run while the
-  // V^T loads are still in flight.  Each of the 4 waves issues 16 K and then
-  // 16 V^T 1 KiB blocks.
+  // V^T loads are still in flight.  Each of the 4 waves issues ATTN_DMAS K
+  // and then ATTN_DMAS V^T 1 KiB blocks.
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -176,9 +189,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       }
     }
   }
-  // this wave's q and K loads are done once at most its 16 V^T loads are
-  // outstanding (vmcnt 16 = 0x4000 | 0; expcnt and lgkmcnt not waited on)
-  __builtin_amdgcn_s_waitcnt(0x4F70);
+  // this wave's q and K loads are done once at most its V^T loads are
+  // outstanding
+  __builtin_amdgcn_s_waitcnt(vm_wait(ATTN_DMAS));
   __builtin_amdgcn_s_barrier();
 
   // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr),
@@ -333,17 +346,18 @@ constexpr int COMBINE_MAX_SPLITS = 32;
 
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
-                                                          int B, int hq, int d, void* out, int otype, int ldo) {
+                                                          int max_splits, int B, int hq, int d, void* out, int otype,
+                                                          int ldo) {
   const int row = blockIdx.x;          // token * hq + qh
   const int tok = row / hq, qh = row % hq;
-  const int kv_len = *dev_n + B;
-  const int ns = min((kv_len + ATTN_SPLIT - 1) / ATTN_SPLIT, COMBINE_MAX_SPLITS);
   const size_t stride = (size_t)B * hq;
   const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
+  // the partials of every split the grid had go out together with the
+  // committed length; the splits past the keys are then left out
   float ms[COMBINE_MAX_SPLITS], ls[COMBINE_MAX_SPLITS], o0[COMBINE_MAX_SPLITS], o1[COMBINE_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
-    if (s < ns) {
+    if (s < max_splits) {
       const size_t r = s * stride + row;
       ms[s] = ml_part[r * 2];
       ls[s] = ml_part[r * 2 + 1];
@@ -351,6 +365,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
       o1[s] = e1 < d ? o_part[r * d + e1] : 0.f;
     }
   }
+  const int kv_len = *dev_n + B;
+  const int ns = min((kv_len + ATTN_SPLIT - 1) / ATTN_SPLIT, max_splits);
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s)
@@ -396,8 +412,9 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
-                     c.dev_n, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo);
+                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo);
   return hipGetLastError();
 }
 

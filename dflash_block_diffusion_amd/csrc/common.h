@@ -145,17 +145,24 @@ struct Parts {
 };
 constexpr int MAX_SPLITS = 8;
 // All S loads are issued before the first add (S <= MAX_SPLITS), so the
-// partials cost one memory round trip, not S.
-__device__ __forceinline__ float parts_sum(const Parts& P, int t, int n) {
+// partials cost one memory round trip, not S.  parts_fetch only issues the
+// loads, so that a kernel can put other loads in flight before parts_add.
+__device__ __forceinline__ void parts_fetch(const Parts& P, int t, int n, float (&x)[MAX_SPLITS]) {
   const float* q = P.p + (size_t)t * P.ld + n;
-  float x[MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < MAX_SPLITS; ++s) x[s] = s < P.S ? q[(size_t)s * P.stride] : 0.f;
+}
+__device__ __forceinline__ float parts_add(const Parts& P, const float (&x)[MAX_SPLITS]) {
   float v = x[0];
 #pragma unroll
   for (int s = 1; s < MAX_SPLITS; ++s)
     if (s < P.S) v = v + x[s];
   return v;
+}
+__device__ __forceinline__ float parts_sum(const Parts& P, int t, int n) {
+  float x[MAX_SPLITS];
+  parts_fetch(P, t, n, x);
+  return parts_add(P, x);
 }
 
 // ------------------------------------------------------------ other kernels

@@ -12,21 +12,6 @@ namespace dfl {
 // chunks, kept in registers between the reduction and the output, and writes
 // one 16-byte store per chunk (8 consecutive columns are contiguous in the
 // tiled layout as well as in a row-major one).  h % 8 == 0, h <= 8192.
-__device__ __forceinline__ void load8_act(const void* p, size_t i, int t, float (&v)[8]) {
-  if (t == T_F32) {
-    const float4 a = *(const float4*)((const float*)p + i), b = *(const float4*)((const float*)p + i + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 q = *(const uint4*)((const uint16_t*)p + i);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      v[e] = t == T_BF16 ? bf16_bits_to_f32(h) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-    }
-  }
-}
-
 __device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float (&y)[8]) {
   if (t == T_F32) {
     float4* q = (float4*)((float*)p + i);
@@ -47,7 +32,10 @@ __device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float
   *(uint4*)((uint16_t*)p + i) = uint4{w[0], w[1], w[2], w[3]};
 }
 
-// one thread per 8-column chunk (blockDim = h/8 rounded up to a wave, <= 1024)
+// one thread per 8-column chunk (blockDim = h/8 rounded up to a wave, <= 1024).
+// Every load of the row (the splits' partial sums, the residual chunk, the
+// gains) is issued before any loaded value is used, so the kernel waits for
+// memory once rather than once per operand.
 __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
   const int row = blockIdx.x;
   const int nch = c.h >> 3;
@@ -55,14 +43,11 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
   const bool live = ch < nch;
   const int j0 = live ? ch * 8 : 0;
   const int rt = c.xtype;                       // activation (rounding) type of the stack
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  float4 pa[MAX_SPLITS], pb[MAX_SPLITS];
+  float4 xa = {0.f, 0.f, 0.f, 0.f}, xb = xa;    // fp32 residual chunk, or the 16-bit one in xa's bits
+  float g[8];
   if (live) {
-    if (c.mode != NORM_PROJ) load8_act(c.x, (size_t)row * c.ldx + j0, c.xtype, v);
     if (c.mode != NORM_ONLY) {
-      // every split's 8 values are loaded before any is added
-      float4 pa[MAX_SPLITS], pb[MAX_SPLITS];
       const float* q = c.in.p + (size_t)row * c.in.ld + j0;
 #pragma unroll
       for (int s = 0; s < MAX_SPLITS; ++s) {
@@ -71,26 +56,61 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
           pb[s] = *(const float4*)(q + (size_t)s * c.in.stride + 4);
         }
       }
-      float y[8] = {pa[0].x, pa[0].y, pa[0].z, pa[0].w, pb[0].x, pb[0].y, pb[0].z, pb[0].w};
-#pragma unroll
-      for (int s = 1; s < MAX_SPLITS; ++s) {
-        if (s < c.in.S) {
-          y[0] = y[0] + pa[s].x; y[1] = y[1] + pa[s].y; y[2] = y[2] + pa[s].z; y[3] = y[3] + pa[s].w;
-          y[4] = y[4] + pb[s].x; y[5] = y[5] + pb[s].y; y[6] = y[6] + pb[s].z; y[7] = y[7] + pb[s].w;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = c.mode == NORM_RESID ? act_round(rt, v[e] + act_round(rt, y[e])) : act_round(rt, y[e]);
-      if (c.mode == NORM_RESID) {
-        store8_act(c.x, (size_t)row * c.ldx + j0, c.xtype, v);
-        if (c.side) {
-          const int col = c.side_col0 + j0;
-          const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
-          store8_act(c.side, o, c.side_type, v);
-        }
+    }
+    if (c.mode != NORM_PROJ) {
+      const size_t xi = (size_t)row * c.ldx + j0;
+      if (c.xtype == T_F32) {
+        xa = *(const float4*)((const float*)c.x + xi);
+        xb = *(const float4*)((const float*)c.x + xi + 4);
+      } else {
+        xa = __builtin_bit_cast(float4, *(const uint4*)((const uint16_t*)c.x + xi));
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = c.gain[j0 + e];
+  }
+  float v[8];
+  if (c.mode != NORM_PROJ) {
+    if (c.xtype == T_F32) {
+      v[0] = xa.x; v[1] = xa.y; v[2] = xa.z; v[3] = xa.w; v[4] = xb.x; v[5] = xb.y; v[6] = xb.z; v[7] = xb.w;
+    } else {
+      const uint4 q = __builtin_bit_cast(uint4, xa);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t hb = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        v[e] = c.xtype == T_BF16 ? bf16_bits_to_f32(hb) : (float)__builtin_bit_cast(_Float16, (uint16_t)hb);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  if (live && c.mode != NORM_ONLY) {
+    // the splits are added in split order
+    float y[8] = {pa[0].x, pa[0].y, pa[0].z, pa[0].w, pb[0].x, pb[0].y, pb[0].z, pb[0].w};
+#pragma unroll
+    for (int s = 1; s < MAX_SPLITS; ++s) {
+      if (s < c.in.S) {
+        y[0] = y[0] + pa[s].x; y[1] = y[1] + pa[s].y; y[2] = y[2] + pa[s].z; y[3] = y[3] + pa[s].w;
+        y[4] = y[4] + pb[s].x; y[5] = y[5] + pb[s].y; y[6] = y[6] + pb[s].z; y[7] = y[7] + pb[s].w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = c.mode == NORM_RESID ? act_round(rt, v[e] + act_round(rt, y[e])) : act_round(rt, y[e]);
+    if (c.mode == NORM_RESID) {
+      store8_act(c.x, (size_t)row * c.ldx + j0, c.xtype, v);
+      if (c.side) {
+        const int col = c.side_col0 + j0;
+        const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
+        store8_act(c.side, o, c.side_type, v);
+      }
+    }
+  }
+  if (!live) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
   }
   float ss = 0.f;
 #pragma unroll
@@ -108,7 +128,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
   const int fmK = (c.tiled && c.otype != T_F32) ? c.h : 0;
   float y[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = v[e] * r * c.gain[j0 + e];
+  for (int e = 0; e < 8; ++e) y[e] = v[e] * r * g[e];
   const size_t o = fmK ? fm_index(row, j0, fmK) : (size_t)row * c.ldo + j0;
   store8_act(c.out, o, c.otype, y);
 }
