@@ -296,7 +296,6 @@ struct dflash_state {
   float* ml_part = nullptr;
   Workspace ws{};
   int32_t* ybuf = nullptr;   // [64] prefill argmax scratch
-  int32_t* blk = nullptr;    // [64] prefill draft scratch
   float* gdn_S = nullptr;
   float* gdn_snap = nullptr;
   float* gdn_tape = nullptr;
@@ -376,7 +375,6 @@ static void carve(dflash_state* s, Carver& c) {
   s->ws.am_cap = am;
   s->ws.logits_tmp = t->d.fmt == DFLASH_FMT_F32 ? c.take<float>((size_t)MAX_ROWS * t->d.vocab) : nullptr;
   s->ybuf = c.take<int32_t>(64);
-  s->blk = c.take<int32_t>(64);
   const size_t sf = (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk;
   s->gdn_S = t->n_gdn ? c.take<float>(sf) : nullptr;
   s->gdn_snap = t->n_gdn ? c.take<float>(sf) : nullptr;
@@ -546,20 +544,54 @@ static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& 
   return DFLASH_OK;
 }
 
+// Context projection of the rows the last verify committed -> QKV input rows
+// B..2B-1 (whole 16-row blocks after the block rows of the tiled input).
+static int draft_context(dflash_state* s, hipStream_t st) {
+  const dflash_model* d = s->dr;
+  const int H = d->d.hidden, B = s->B;
+  Parts fc;
+  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
+  NormCall c{};
+  c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
+  c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = B;
+  c.out = (char*)s->bu + (size_t)B * H * elem_bytes(d->gin); c.otype = d->gin; c.ldo = H; c.tiled = 1;
+  HIPCHK(launch_norm(c, st));
+  return DFLASH_OK;
+}
+
+// The part of a draft a prompt chunk needs: every drafter layer's K/V of the
+// pending context rows, written to the drafter cache.  Each layer projects
+// the same context rows (they do not pass through the layers), so the block
+// rows, the attention, the FFNs and the lm-head are not run.  The block rows'
+// cache slots the full draft would write are transient (the next context rows
+// take them before any read).
+static int draft_context_kv(dflash_state* s, hipStream_t st) {
+  const dflash_model* d = s->dr;
+  const int H = d->d.hidden, B = s->B;
+  RC(draft_context(s, st));
+  const void* ctx_in = (const char*)s->bu + (size_t)B * H * elem_bytes(d->gin);
+  for (int l = 0; l < d->d.n_layers; ++l) {
+    const Layer& L = d->layers[l];
+    Parts qkv;
+    RC(gemm(s, L.qkv, ctx_in, H, B, EPI_PARTIAL, st, &qkv));
+    RopeCall rc;
+    rc.qkv = qkv; rc.atype = d->act;
+    rc.block_rows = 0; rc.ctx_rows = B;      // partial row j = context row j
+    rc.dev_n = s->scal + SC_N; rc.dev_p = s->scal + SC_P;
+    rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = d->d.eps;
+    rc.cos_t = s->cos_t; rc.sin_t = s->sin_t; rc.q_out = s->bq;
+    rc.kc = s->dk[l]; rc.vc = s->dv[l];
+    rc.page_table = s->pt; rc.capacity = s->capacity;
+    rc.hq = d->d.n_q_heads; rc.hkv = d->d.n_kv_heads; rc.d = d->d.head_dim;
+    HIPCHK(launch_qk_rope(rc, st));
+  }
+  return DFLASH_OK;
+}
+
 static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t st) {
   const dflash_model *t = s->t, *d = s->dr;
   const int H = d->d.hidden, B = s->B;
-  // context projection of the rows the last verify committed -> QKV input rows B..2B-1
-  Parts fc;
-  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
-  {
-    NormCall c{};
-    c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
-    c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = B;
-    // rows B..2B-1 of the tiled QKV input: whole 16-row blocks after the block rows
-    c.out = (char*)s->bu + (size_t)B * H * elem_bytes(d->gin); c.otype = d->gin; c.ldo = H; c.tiled = 1;
-    HIPCHK(launch_norm(c, st));
-  }
+  RC(draft_context(s, st));
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 1, d->d.mask_token, B, s->x, H,
                       s->scal + SC_STATUS, st));
   Pending pend;
@@ -583,7 +615,8 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
 
 // Target forward of rows 0..B-1 of block (B = s->B for prefill chunks, the
 // verify rows otherwise).
-static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, int B, hipStream_t st) {
+static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, int B, hipStream_t st,
+                     bool head = true) {
   const dflash_model *t = s->t, *d = s->dr;
   const int H = t->d.hidden;
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 0, 0, B, s->x, H, s->scal + SC_STATUS, st));
@@ -615,7 +648,12 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
     }
     RC(ffn(s, t, L, pend, B, st, side, d->d.n_sel * H, d->gin, col0));
   }
+  // (this norm also completes the last layer's residual update, which writes
+  // its conditioning rows when that layer is a selected one)
   RC(norm(s, t, pend, t->d.final_norm, s->bu, t->gin, B, st));
+  // a prompt chunk before the last needs only the caches, the GatedDeltaNet
+  // state and the conditioning rows: no logits
+  if (!head) return DFLASH_OK;
   const int V = t->d.vocab;
   if (s->temp > 0.f) {
     // the acceptance reads the target's tempered distributions of these rows
@@ -654,9 +692,12 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
   int last = 0;
   for (int c0 = 0; c0 < n_tokens; c0 += s->B) {
     const int len = std::min(s->B, n_tokens - c0);
-    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, s->B, st));   // logits land in vlog when sampling
+    // only the last chunk's last row is read: the first token (logits land in
+    // vlog when sampling)
+    const bool final_chunk = c0 + s->B >= n_tokens;
+    RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, s->B, st, final_chunk));
     RC(do_commit(s, nullptr, len, nullptr, st));
-    RC(do_draft(s, s->blk, nullptr, st));          // appends the chunk's drafter context rows
+    RC(draft_context_kv(s, st));                   // the chunk's drafter context rows
     last = len;
   }
   if (s->temp > 0.f)   // the first token is a draw from the last prompt row at T (stream 3, counter (P, 0))

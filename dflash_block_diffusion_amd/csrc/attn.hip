@@ -352,12 +352,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const int tok = row / hq, qh = row % hq;
   const size_t stride = (size_t)B * hq;
   const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
-  // the partials of every split the grid had go out together with the
-  // committed length; the splits past the keys are then left out
+  const int kv_len = *dev_n + B;
+  const int ns = min((kv_len + ATTN_SPLIT - 1) / ATTN_SPLIT, max_splits);
   float ms[COMBINE_MAX_SPLITS], ls[COMBINE_MAX_SPLITS], o0[COMBINE_MAX_SPLITS], o1[COMBINE_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
-    if (s < max_splits) {
+    if (s < ns) {
       const size_t r = s * stride + row;
       ms[s] = ml_part[r * 2];
       ls[s] = ml_part[r * 2 + 1];
@@ -365,8 +365,6 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
       o1[s] = e1 < d ? o_part[r * d + e1] : 0.f;
     }
   }
-  const int kv_len = *dev_n + B;
-  const int ns = min((kv_len + ATTN_SPLIT - 1) / ATTN_SPLIT, max_splits);
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s)
