@@ -91,10 +91,10 @@ static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
   LinearWs L;
   size_t off = 0;
   auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
-  const Plan p = make_plan(fmt, n, k, m, EPI_PARTIAL);
-  L.part_floats = (size_t)p.S * m * n;
+  const int S = m > MAX_ROWS ? dense_splits(n, k, m, EPI_PARTIAL) : make_plan(fmt, n, k, m, EPI_PARTIAL).S;
+  L.part_floats = (size_t)S * m * n;
   L.part_off = take(L.part_floats * 4);
-  const int am = std::max(1, gemm_am_blocks(fmt, n, m));
+  const int am = m > MAX_ROWS ? 1 : std::max(1, gemm_am_blocks(fmt, n, m));
   L.amv_off = take((size_t)am * 64 * 4);
   L.ami_off = take((size_t)am * 64 * 4);
   L.lg_off = take(fmt == DFLASH_FMT_F32 ? (size_t)MAX_ROWS * n * 4 : 4);
@@ -102,8 +102,15 @@ static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
   return L;
 }
 
+// rows a dflash_linear call takes: up to 64 for every format, and prompt
+// chunks (multiples of 16 up to 1024) for W4A16 with the fp32 output
+static bool linear_rows_ok(int fmt, int n, int k, int m, int epilogue) {
+  if (m >= 1 && m <= MAX_ROWS) return true;
+  return epilogue == 0 && dense_ok(fmt, n, k, m, EPI_PARTIAL);
+}
+
 extern "C" size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m) {
-  if (!fmt_ok(fmt) || check_gemm_shape(fmt, n, k, 0) || m < 1 || m > MAX_ROWS) return 0;
+  if (!fmt_ok(fmt) || check_gemm_shape(fmt, n, k, 0) || !linear_rows_ok(fmt, n, k, m, 0)) return 0;
   return linear_ws_layout(fmt, n, k, m).total;
 }
 
@@ -112,7 +119,8 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   if (!fmt_ok(fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
   int rc = check_gemm_shape(fmt, n, k, 0);
   if (rc) return rc;
-  if (m < 1 || m > MAX_ROWS) return fail(DFLASH_E_SHAPE, "m must be in [1, 64]");
+  if (!linear_rows_ok(fmt, n, k, m, epilogue))
+    return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, W4A16 with epilogue 0, a multiple of 16 up to 1024)");
   if (fmt == DFLASH_FMT_F32 && ldx < k) return fail(DFLASH_E_SHAPE, "ldx must be >= k");
   if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
   if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");

@@ -96,11 +96,7 @@ struct AttnArgs {
 constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
 constexpr int ATTN_DMAS = 4 * ATTN_PAGES;            // K (or V^T) page DMAs per wave
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15: not waited on)
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // round-to-nearest-even to bf16 of a finite value (softmax weights), branch-free
 __device__ __forceinline__ uint32_t bf16_bits_finite(float f) {

@@ -124,6 +124,10 @@ struct Workspace {
 // split (nwg = PR * S), align = row tiles per balancing unit (2 for gate/up)
 struct Plan { int RT, MB, S, PR, ngroups, nwg, ktiles, ntile16, align, NW; };
 Plan make_plan(int fmt, int n, int k, int m, int epi);
+// prompt chunks: m in (64, 1024], m % 16 == 0, W4 weights, partial-sum or
+// SiLU epilogue (launch_gemm takes this path for m > 64)
+bool dense_ok(int fmt, int n, int k, int m, int epi);
+int dense_splits(int n, int k, int m, int epi);
 struct Workspace;
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
@@ -143,6 +147,12 @@ struct Parts {
   size_t stride;   // floats between splits (m * n of the launch)
   int ld;          // row stride (n of the launch)
 };
+// LDS pointer, the destination of direct global->LDS loads
+typedef __attribute__((address_space(3))) void* lds_ptr;
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15: not waited on)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 constexpr int MAX_SPLITS = 8;
 // All S loads are issued before the first add (S <= MAX_SPLITS), so the
 // partials cost one memory round trip, not S.  parts_fetch only issues the

@@ -783,6 +783,224 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
   return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
 }
 
+// ------------------------------------------------------- dense (prompt chunks)
+// W4 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
+// that the MFMAs, not the weight stream, set the time, so activations are
+// reused across many weight rows instead of being re-read per row tile.
+// Work-group = 4 token blocks (64 rows) x 16 row tiles (256 weight rows) x one
+// of S K ranges; wave w owns row tiles 4w..4w+3 for all 4 token blocks.  Per K
+// tile (128 columns) the work-group stages the 16 activation fragments (4
+// blocks x 4 MFMA steps, 1 KiB each) in LDS by direct global->LDS loads,
+// double-buffered, while each wave holds its four weight tiles and their
+// group scales in registers, also double-buffered.  The arithmetic is the
+// stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
+// scaled by the group's fp16 scale and accumulated in fp32.
+constexpr int DENSE_MT = 4;                  // token blocks per work-group
+
+// 16 bytes per lane from src to LDS at lds + 16 * lane.  Issued from asm so
+// that the compiler does not track it: its wait analysis would otherwise
+// drain every such load before unrelated register reads.  Callers wait for it
+// with explicit vmcnt waits (it is a vector-memory load in issue order).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+// The pipeline's register loads go the same way (weights non-temporal): the
+// explicit per-tile wait is then the only one, and every register they write
+// is read only after it (the waits are scheduling barriers).
+__device__ __forceinline__ uint4 gload16_nt(const void* p) {
+  uint4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t gload4(const void* p) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+constexpr int DENSE_RW = 4;                  // row tiles per wave
+constexpr int DENSE_MAX_ROWS = 1024;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_per) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const int nblk = (a.m + 15) >> 4;
+  const int tb0 = blockIdx.y * DENSE_MT;
+  const int rt0 = blockIdx.x * (4 * DENSE_RW) + wave * DENSE_RW;
+  const int sidx = blockIdx.z;
+  const int kt0 = sidx * kt_per, kt1 = min(a.ktiles, kt0 + kt_per);
+  const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
+  const size_t xfrag = (size_t)(a.k >> 5);
+  uint32_t rtile[DENSE_RW];                  // row tiles past the end re-read the last one
+#pragma unroll
+  for (int i = 0; i < DENSE_RW; ++i) rtile[i] = (uint32_t)min(rt0 + i, a.ntile16 - 1);
+
+  floatx4 acc[DENSE_MT][DENSE_RW];
+#pragma unroll
+  for (int tb = 0; tb < DENSE_MT; ++tb)
+#pragma unroll
+    for (int i = 0; i < DENSE_RW; ++i) acc[tb][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's DENSE_MT of the K tile's 4*DENSE_MT activation fragments:
+  // fragment f = DENSE_MT*w + j is token block f/4 (blocks past the chunk
+  // re-read its last one), MFMA step f%4
+  auto stage = [&](int t, uint8_t* xs) {
+#pragma unroll
+    for (int j = 0; j < DENSE_MT; ++j) {
+      const int f = DENSE_MT * wave + j, tb = min(tb0 + (f >> 2), nblk - 1);
+      const uint16_t* src = a.x + ((size_t)tb * xfrag + (size_t)t * 4 + (f & 3)) * 512 + lane * 8;
+      lds_dma16(src, (uint32_t)(uintptr_t)(lds_ptr)(xs + f * 1024));
+    }
+  };
+  auto wload = [&](int t, uint4 (&w)[DENSE_RW], uint32_t (&sc)[DENSE_RW]) {
+#pragma unroll
+    for (int i = 0; i < DENSE_RW; ++i) {
+      const size_t tile = (size_t)rtile[i] * a.ktiles + t;
+      w[i] = gload16_nt(a.w + tile * 1024 + lane * 16);
+      sc[i] = gload4(a.s + tile * 32 + lr * 2);
+    }
+  };
+  auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW]) {
+    half8 b[DENSE_RW][4];
+    float sg[DENSE_RW][2];
+#pragma unroll
+    for (int i = 0; i < DENSE_RW; ++i) {
+      const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) b[i][ss] = deq_w4(wd[ss], mlo, mhi, magic);
+      const half2v s2 = h2(sc[i]);
+      sg[i][0] = (float)s2[0];
+      sg[i][1] = (float)s2[1];
+    }
+#pragma unroll
+    for (int tb = 0; tb < DENSE_MT; ++tb)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const half8 x0 = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg) * 1024 + lane * 16));
+        const half8 x1 = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg + 1) * 1024 + lane * 16));
+#pragma unroll
+        for (int i = 0; i < DENSE_RW; ++i) {
+          floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, b[i][2 * gg], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, b[i][2 * gg + 1], tmp, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[tb][i][v] += sg[i][gg] * tmp[v];
+        }
+      }
+  };
+  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs, 4
+  // weight and 4 scale loads, the youngest) stay in flight; past the last
+  // tile the next loads re-read it, so the wait is always the same.  The wait
+  // is kept apart from the first use so that the compiler adds none there.
+  auto wait_tile = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + 2 * DENSE_RW));
+    asm volatile("s_nop 0");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
+  };
+
+  uint4 w0[DENSE_RW], w1[DENSE_RW];
+  uint32_t s0[DENSE_RW], s1[DENSE_RW];
+  if (kt0 < kt1) {
+    stage(kt0, xs0);
+    wload(kt0, w0, s0);
+    for (int t = kt0; t < kt1; t += 2) {
+      // tile t: xs0, w0.  The barrier frees xs1 (read for tile t - 1).
+      __builtin_amdgcn_s_barrier();
+      const int t1n = min(t + 1, kt1 - 1);
+      stage(t1n, xs1);
+      wload(t1n, w1, s1);
+      wait_tile();
+      compute(xs0, w0, s0);
+      if (t + 1 >= kt1) break;
+      // tile t + 1: xs1, w1
+      __builtin_amdgcn_s_barrier();
+      const int t2n = min(t + 2, kt1 - 1);
+      stage(t2n, xs0);
+      wload(t2n, w0, s0);
+      wait_tile();
+      compute(xs1, w1, s1);
+    }
+    // the last loads re-read a tile nobody uses: let them land before the
+    // work-group (and its LDS) ends
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  }
+
+  // lane (lr, g) holds weight row (rt0 + i)*16 + lr for tokens
+  // (tb0 + tb)*16 + 4g + v
+  if (EPI == EPI_PARTIAL) {
+    float* part = a.part + (size_t)sidx * a.m * a.n;
+#pragma unroll
+    for (int i = 0; i < DENSE_RW; ++i) {
+      if (rt0 + i >= a.ntile16) continue;
+      const int n = (rt0 + i) * 16 + lr;
+#pragma unroll
+      for (int tb = 0; tb < DENSE_MT; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = (tb0 + tb) * 16 + 4 * g + v;
+          if (t < a.m) part[(size_t)t * a.n + n] = acc[tb][i][v];
+        }
+    }
+  } else {  // EPI_SILU: row tiles (2p, 2p+1) are a (gate, up) pair
+    const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
+    const int half_n = a.n >> 1;
+#pragma unroll
+    for (int p = 0; p < DENSE_RW / 2; ++p) {
+      if (rt0 + 2 * p + 1 >= a.ntile16) continue;
+      const int n_out = ((rt0 >> 1) + p) * 16 + lr;
+#pragma unroll
+      for (int tb = 0; tb < DENSE_MT; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = (tb0 + tb) * 16 + 4 * g + v;
+          if (t >= a.m) continue;
+          const float gv = act_round(rnd, acc[tb][2 * p][v]);
+          const float uv = act_round(rnd, acc[tb][2 * p + 1][v]);
+          const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
+          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
+        }
+    }
+  }
+}
+
+// K splits of a dense launch: partial sums go to S slices so that the grid
+// reaches the chip's 256 CUs, each split keeping at least 4 K tiles
+int dense_splits(int n, int k, int m, int epi) {
+  if (epi != EPI_PARTIAL) return 1;
+  const int ktiles = k / 128;
+  const int base = ((n / 16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((m / 16 + DENSE_MT - 1) / DENSE_MT);
+  int S = 1;
+  while (S < MAX_SPLITS && base * S < 256 && ktiles / (2 * S) >= 4) S *= 2;
+  return S;
+}
+
+bool dense_ok(int fmt, int n, int k, int m, int epi) {
+  return fmt == W_W4 && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
+         (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
+}
+
+static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t s, int* splits) {
+  const GemmW& W = *c.W;
+  if (!dense_ok(W.fmt, W.n, W.k, c.m, c.epi)) return hipErrorInvalidValue;
+  const int S = dense_splits(W.n, W.k, c.m, c.epi);
+  if (c.epi == EPI_PARTIAL && (size_t)S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
+  a.n = W.n; a.k = W.k; a.ktiles = W.k / 128; a.ntile16 = W.n / 16; a.m = c.m; a.splits = S; a.align = 1;
+  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
+  a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
+  const int kt_per = (a.ktiles + S - 1) / S;
+  const dim3 grid((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW), (c.m / 16 + DENSE_MT - 1) / DENSE_MT, S);
+  if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_PARTIAL>, grid, dim3(256), 0, s, a, kt_per);
+  else hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_SILU>, grid, dim3(256), 0, s, a, kt_per);
+  if (splits) *splits = S;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
                        double* bytes, int* splits) {
   const GemmW& W = *c.W;
@@ -810,6 +1028,10 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
     return launch_argmax_rows(w.logits_tmp, W.n, W.n, c.row0, c.m - c.row0, c.am_out, c.logits, c.ldl, s);
+  }
+  if (c.m > MAX_ROWS) {
+    if (variant) *variant = c.epi == EPI_SILU ? "gemm_dense_w4_silu" : "gemm_dense_w4";
+    return launch_gemm_dense(c, w, s, splits);
   }
   const Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);
   if (variant) *variant = variant_name(W.fmt, p);

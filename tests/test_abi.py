@@ -120,3 +120,14 @@ def test_model_create_rejects_bad_head_dim_and_sel():
     assert L.dflash_drafter_bind(d, t) == -2
     L.dflash_model_destroy(d)
     L.dflash_model_destroy(t)
+
+
+def test_linear_rows_beyond_the_limits_are_refused():
+    # prompt chunks: W4A16 only, multiples of 16 up to 1024 rows
+    from dflash_block_diffusion_amd import configs as C
+    L = bn.lib()
+    assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 72) == 0      # not a multiple of 16
+    assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 1040) == 0    # above 1024
+    assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 512, 128) == 0     # the dense path is W4 only
+    assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 128) > 0
+    assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 64) > 0

@@ -163,3 +163,52 @@ def test_lm_head_argmax_full_size():
     assert np.max(np.abs(logits - ref) / (bound(x, w))) <= 1.0
     ok = top2_margin(ref) >= 1e-2
     assert np.array_equal(am[ok], np.argmax(ref, axis=1)[ok])
+
+
+# ------------------------------------------------------------ prompt chunks
+# m > 64 (multiples of 16) takes the dense W4 kernel of prefill: activations
+# staged in LDS and shared by 256 weight rows, K split for the partial sums.
+@pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 4096, 1024), (4128, 512, 96),
+                                   (784, 2048, 512), (256, 128, 208)])
+def test_linear_dense_w4_parity(n, k, m):
+    # ragged row-tile groups (N/16 not a multiple of 16), ragged token groups
+    # (m/16 not a multiple of 4), one K tile, splits of uneven length
+    g = synth.HostSynth(300)
+    w = g.weight(f"dense{n}x{k}", n, k, C.FMT_W4A16)
+    x = x_values(np.random.default_rng(n + k + m), m, k, C.FMT_W4A16)
+    y, _, _ = run_linear(w, x, C.FMT_W4A16)
+    ref = linear(x, w)
+    assert np.all(np.isfinite(y))
+    assert np.all(np.abs(y - ref) <= bound(x, w))
+
+
+def test_linear_dense_w4_repeat_is_bitwise():
+    g = synth.HostSynth(301)
+    w = g.weight("dense_rep", 1024, 4096, C.FMT_W4A16)
+    x = x_values(np.random.default_rng(8), 256, 4096, C.FMT_W4A16)
+    y1, _, _ = run_linear(w, x, C.FMT_W4A16)
+    y2, _, _ = run_linear(w, x, C.FMT_W4A16)
+    assert np.array_equal(y1, y2)
+
+
+DENSE_FULL = [  # the target projections of an 8B / 27B prompt chunk
+    ("8b_qkv_dense", 6144, 4096, 512),
+    ("8b_down_dense", 4096, 12288, 512),
+    ("8b_o_dense", 4096, 4096, 1024),
+    ("27b_gateup_dense", 34816, 5120, 512),
+]
+
+
+@pytest.mark.parametrize("name,n,k,m", DENSE_FULL)
+def test_linear_dense_w4_full_size_sampled(name, n, k, m):
+    g = synth.HostSynth(302)
+    w = g.weight(name, n, k, C.FMT_W4A16)
+    x = x_values(np.random.default_rng(14), m, k, C.FMT_W4A16)
+    y, _, _ = run_linear(w, x, C.FMT_W4A16)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(15)
+    for r0 in list(rng.integers(0, n // 16, 4) * 16) + [n - 16]:
+        ref = linear(x, w, rows=(int(r0), int(r0) + 16))
+        got = y[:, r0:r0 + 16]
+        assert np.all(np.abs(got - ref) <= bound(x, w, rows=(int(r0), int(r0) + 16))), (name, r0)
+
