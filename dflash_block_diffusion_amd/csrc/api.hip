@@ -277,6 +277,7 @@ struct dflash_state {
   const dflash_model* dr = nullptr;
   int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
   int vrows = 0;          // rows a verify runs (B, or fewer under a draft cap)
+  int pm = 0;             // rows of a dense prompt chunk (0: prompts run in blocks of B)
   int max_draft = 0;      // drafts verified per step (0 = the whole block)
   float temp = 0.f;       // sampling temperature (0 = greedy)
   uint64_t seed = 0;
@@ -328,6 +329,9 @@ struct Carver {
 
 static int gdn_rec(const dflash_model* t) { return t->d.gdn_dk + t->d.gdn_dv + 2; }
 
+// rows of a dense prompt chunk (a multiple of both block sizes)
+constexpr int DENSE_PROMPT_ROWS = 512;
+
 static void carve(dflash_state* s, Carver& c) {
   const dflash_model *t = s->t, *d = s->dr;
   const int H = t->d.hidden, B = s->B;
@@ -355,16 +359,18 @@ static void carve(dflash_state* s, Carver& c) {
     }
     F = std::max(F, m->d.ffn);
   }
-  s->x = c.take<char>((size_t)MAX_ROWS * H * 4);
-  s->bu = c.take<char>((size_t)MAX_ROWS * H * 4);
-  s->ba = c.take<char>((size_t)MAX_ROWS * att_w * 4);
-  s->bf = c.take<char>((size_t)MAX_ROWS * F * 4);
-  s->bqkv = c.take<char>((size_t)MAX_ROWS * qkv_n * 4);
-  s->bq = c.take<char>((size_t)B * t->d.n_q_heads * t->d.head_dim * 4 + (size_t)B * d->d.n_q_heads * d->d.head_dim * 4);
-  s->side = c.take<char>((size_t)MAX_ROWS * d->d.n_sel * H * 4);
+  // row buffers: a block (+ its context rows), or a dense prompt chunk
+  const size_t R = std::max(MAX_ROWS, s->pm), RB = std::max(B, s->pm);
+  s->x = c.take<char>(R * H * 4);
+  s->bu = c.take<char>(R * H * 4);
+  s->ba = c.take<char>(R * att_w * 4);
+  s->bf = c.take<char>(R * F * 4);
+  s->bqkv = c.take<char>(R * qkv_n * 4);
+  s->bq = c.take<char>(RB * t->d.n_q_heads * t->d.head_dim * 4 + (size_t)B * d->d.n_q_heads * d->d.head_dim * 4);
+  s->side = c.take<char>(R * d->d.n_sel * H * 4);
   const int hq = std::max(t->d.n_q_heads, d->d.n_q_heads), hd = std::max(t->d.head_dim, d->d.head_dim);
-  s->o_part = c.take<float>((size_t)s->max_splits * B * hq * hd);
-  s->ml_part = c.take<float>((size_t)s->max_splits * B * hq * 2);
+  s->o_part = c.take<float>((size_t)s->max_splits * RB * hq * hd);
+  s->ml_part = c.take<float>((size_t)s->max_splits * RB * hq * 2);
   // GEMM workspaces: the largest need over every weight of both stacks
   size_t pf = 1;
   int am = 0;
@@ -373,6 +379,14 @@ static void carve(dflash_state* s, Carver& c) {
     pf = std::max(pf, (size_t)p.S * m * g.n);
   };
   for (const Layer& L : t->layers) { need(L.qkv, B); need(L.o, B); need(L.down, B); }
+  // a prompt chunk is any multiple of B up to pm rows; fewer rows can take
+  // more K splits
+  if (s->pm)
+    for (int m = B; m <= s->pm; m += B)
+      if (m > MAX_ROWS)
+        for (const Layer& L : t->layers)
+          for (const GemmW* g : {&L.qkv, &L.o, &L.down})
+            pf = std::max(pf, (size_t)dense_splits(g->n, g->k, m, EPI_PARTIAL) * m * g->n);
   for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.down, B); }
   need(d->fc, B);
   am = std::max(1, gemm_am_blocks(t->lm.fmt, t->lm.n, B));
@@ -404,6 +418,18 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   s->capacity = s->pages * PAGE;
   s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
   if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
+  // dense prompt chunks: an int4 target of attention layers (the projections
+  // have the dense kernel; GatedDeltaNet layers take B tokens at a time)
+  s->pm = 0;
+  if (t->d.fmt == DFLASH_FMT_W4A16 && t->n_gdn == 0 && t->act == T_BF16 && max_ctx > 2 * block) {
+    bool ok = true;
+    for (const Layer& L : t->layers)
+      ok = ok && dense_ok(L.qkv.fmt, L.qkv.n, L.qkv.k, DENSE_PROMPT_ROWS, EPI_PARTIAL) &&
+           dense_ok(L.o.fmt, L.o.n, L.o.k, DENSE_PROMPT_ROWS, EPI_PARTIAL) &&
+           dense_ok(L.gu.fmt, L.gu.n, L.gu.k, DENSE_PROMPT_ROWS, EPI_SILU) &&
+           dense_ok(L.down.fmt, L.down.n, L.down.k, DENSE_PROMPT_ROWS, EPI_PARTIAL);
+    if (ok) s->pm = DENSE_PROMPT_ROWS;
+  }
   return DFLASH_OK;
 }
 
@@ -554,11 +580,13 @@ static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& 
 
 // Context projection of the rows the last verify committed -> QKV input rows
 // B..2B-1 (whole 16-row blocks after the block rows of the tiled input).
-static int draft_context(dflash_state* s, hipStream_t st) {
+static int draft_context(dflash_state* s, hipStream_t st, int side_row0 = 0) {
   const dflash_model* d = s->dr;
   const int H = d->d.hidden, B = s->B;
+  // conditioning rows side_row0.. (whole 16-row blocks of the tiled input)
+  const void* side = (const char*)s->side + (size_t)side_row0 * d->d.n_sel * H * elem_bytes(d->gin);
   Parts fc;
-  RC(gemm(s, d->fc, s->side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
+  RC(gemm(s, d->fc, side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
   NormCall c{};
   c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
   c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = B;
@@ -573,10 +601,10 @@ static int draft_context(dflash_state* s, hipStream_t st) {
 // rows, the attention, the FFNs and the lm-head are not run.  The block rows'
 // cache slots the full draft would write are transient (the next context rows
 // take them before any read).
-static int draft_context_kv(dflash_state* s, hipStream_t st) {
+static int draft_context_kv(dflash_state* s, hipStream_t st, int side_row0 = 0) {
   const dflash_model* d = s->dr;
   const int H = d->d.hidden, B = s->B;
-  RC(draft_context(s, st));
+  RC(draft_context(s, st, side_row0));
   const void* ctx_in = (const char*)s->bu + (size_t)B * H * elem_bytes(d->gin);
   for (int l = 0; l < d->d.n_layers; ++l) {
     const Layer& L = d->layers[l];
@@ -697,8 +725,23 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
   if (t->n_gdn)
     HIPCHK(launch_fill_i32((int32_t*)s->gdn_S,
                            (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk, 0, st));
-  int last = 0;
-  for (int c0 = 0; c0 < n_tokens; c0 += s->B) {
+  int last = 0, c0 = 0;
+  if (s->pm > 0) {
+    // the whole blocks before the one holding the last token run as dense
+    // chunks of up to pm rows; their drafter context rows then go in B at a
+    // time (the commit of each block makes it the pending context)
+    const int dense_end = ((n_tokens - 1) / s->B) * s->B;
+    while (c0 < dense_end) {
+      const int rows = std::min(s->pm, dense_end - c0);
+      RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, rows, st, false));
+      for (int j = 0; j < rows; j += s->B) {
+        RC(do_commit(s, nullptr, s->B, nullptr, st));
+        RC(draft_context_kv(s, st, j));
+      }
+      c0 += rows;
+    }
+  }
+  for (; c0 < n_tokens; c0 += s->B) {
     const int len = std::min(s->B, n_tokens - c0);
     // only the last chunk's last row is read: the first token (logits land in
     // vlog when sampling)

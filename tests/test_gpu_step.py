@@ -230,6 +230,14 @@ def test_reduced_lockstep(name, P):
     assert stats["compared"] >= len(forced) * cfg.block
 
 
+def test_reduced_8b_dense_prompt_chunks_lockstep():
+    # 700 prompt tokens: dense chunks of 512 and 160 rows (the int4 prompt
+    # GEMM, attention over a 512-row block), then the last 28 tokens as a block
+    cfg = reduced("8b")
+    _, _, stats, _ = lockstep(cfg, 700, [0, 31, 9])
+    assert stats["compared"] >= 3 * cfg.block
+
+
 def test_rollback_replays_identically():
     cfg = reduced("8b")
     ck = synth.make_pair(cfg)
