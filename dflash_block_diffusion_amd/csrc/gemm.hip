@@ -790,9 +790,11 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // Work-group = 4 token blocks (64 rows) x 16 row tiles (256 weight rows) x one
 // of S K ranges; wave w owns row tiles 4w..4w+3 for all 4 token blocks.  Per K
 // tile (128 columns) the work-group stages the 16 activation fragments (4
-// blocks x 4 MFMA steps, 1 KiB each) in LDS by direct global->LDS loads,
-// double-buffered, while each wave holds its four weight tiles and their
-// group scales in registers, also double-buffered.  The arithmetic is the
+// blocks x 4 MFMA steps, 1 KiB each) in LDS by direct global->LDS loads while
+// each wave holds its four weight tiles and their group scales in registers;
+// both go through three stages, so the loads of tiles t+1 and t+2 are in
+// flight while tile t is multiplied (one tile of compute is shorter than a
+// load's latency).  The arithmetic is the
 // stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
 // scaled by the group's fp16 scale and accumulated in fp32.
 constexpr int DENSE_MT = 4;                  // token blocks per work-group
@@ -824,6 +826,7 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_per) {
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t xs2[DENSE_MT * 4 * 1024];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
@@ -863,66 +866,87 @@ __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_p
       sc[i] = gload4(a.s + tile * 32 + lr * 2);
     }
   };
+  // Per 64-wide group: its two weight steps dequantised for the 4 row tiles,
+  // its two activation steps of the 4 token blocks read from LDS, then for
+  // each half of the token blocks 8 independent MFMA chains (2 MFMAs each)
+  // before their sums are scaled into the accumulators, so no MFMA waits on
+  // the one before it and no FMA on an MFMA just issued.
   auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW]) {
-    half8 b[DENSE_RW][4];
-    float sg[DENSE_RW][2];
 #pragma unroll
-    for (int i = 0; i < DENSE_RW; ++i) {
-      const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+    for (int gg = 0; gg < 2; ++gg) {
+      half8 b[DENSE_RW][2];
+      float sg[DENSE_RW];
 #pragma unroll
-      for (int ss = 0; ss < 4; ++ss) b[i][ss] = deq_w4(wd[ss], mlo, mhi, magic);
-      const half2v s2 = h2(sc[i]);
-      sg[i][0] = (float)s2[0];
-      sg[i][1] = (float)s2[1];
-    }
-#pragma unroll
-    for (int tb = 0; tb < DENSE_MT; ++tb)
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const half8 x0 = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg) * 1024 + lane * 16));
-        const half8 x1 = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg + 1) * 1024 + lane * 16));
-#pragma unroll
-        for (int i = 0; i < DENSE_RW; ++i) {
-          floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, b[i][2 * gg], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, b[i][2 * gg + 1], tmp, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[tb][i][v] += sg[i][gg] * tmp[v];
-        }
+      for (int i = 0; i < DENSE_RW; ++i) {
+        const uint32_t wd0 = gg ? w[i].z : w[i].x, wd1 = gg ? w[i].w : w[i].y;
+        b[i][0] = deq_w4(wd0, mlo, mhi, magic);
+        b[i][1] = deq_w4(wd1, mlo, mhi, magic);
+        sg[i] = (float)h2(sc[i])[gg];
       }
+      half8 x[DENSE_MT][2];
+#pragma unroll
+      for (int tb = 0; tb < DENSE_MT; ++tb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          x[tb][h] = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg + h) * 1024 + lane * 16));
+#pragma unroll
+      for (int hb = 0; hb < DENSE_MT; hb += 2) {
+        floatx4 tmp[2][DENSE_RW];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < DENSE_RW; ++i)
+            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[hb + j][0], b[i][0], floatx4{0.f, 0.f, 0.f, 0.f},
+                                                               0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < DENSE_RW; ++i)
+            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[hb + j][1], b[i][1], tmp[j][i], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < DENSE_RW; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[hb + j][i][v] += sg[i] * tmp[j][i][v];
+      }
+    }
   };
-  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs, 4
-  // weight and 4 scale loads, the youngest) stay in flight; past the last
-  // tile the next loads re-read it, so the wait is always the same.  The wait
-  // is kept apart from the first use so that the compiler adds none there.
+  // Every tile's wait lets the loads of the next two tiles (2 x (DENSE_MT
+  // fragment DMAs + 4 weight + 4 scale loads), the youngest) stay in flight;
+  // past the last tile the loads re-read it, so the wait is always the same.
+  // It is kept apart from the first use so that the compiler adds none there.
   auto wait_tile = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + 2 * DENSE_RW));
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * (DENSE_MT + 2 * DENSE_RW)));
     asm volatile("s_nop 0");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
   };
-
-  uint4 w0[DENSE_RW], w1[DENSE_RW];
-  uint32_t s0[DENSE_RW], s1[DENSE_RW];
+  uint4 w0[DENSE_RW], w1[DENSE_RW], w2[DENSE_RW];
+  uint32_t s0[DENSE_RW], s1[DENSE_RW], s2[DENSE_RW];
+  // tile t from stage (xs, w, sc); tile t + 2 goes to stage (xn, wn, sn), the
+  // one tile t - 1 used: the barrier first lets every wave finish with it
+  auto step = [&](int t, const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW], uint8_t* xn,
+                  uint4 (&wn)[DENSE_RW], uint32_t (&sn)[DENSE_RW]) {
+    __builtin_amdgcn_s_barrier();
+    const int tn = min(t + 2, kt1 - 1);
+    stage(tn, xn);
+    wload(tn, wn, sn);
+    wait_tile();
+    compute(xs, w, sc);
+  };
   if (kt0 < kt1) {
     stage(kt0, xs0);
     wload(kt0, w0, s0);
-    for (int t = kt0; t < kt1; t += 2) {
-      // tile t: xs0, w0.  The barrier frees xs1 (read for tile t - 1).
-      __builtin_amdgcn_s_barrier();
-      const int t1n = min(t + 1, kt1 - 1);
-      stage(t1n, xs1);
-      wload(t1n, w1, s1);
-      wait_tile();
-      compute(xs0, w0, s0);
+    stage(min(kt0 + 1, kt1 - 1), xs1);
+    wload(min(kt0 + 1, kt1 - 1), w1, s1);
+    for (int t = kt0; t < kt1; t += 3) {
+      step(t, xs0, w0, s0, xs2, w2, s2);
       if (t + 1 >= kt1) break;
-      // tile t + 1: xs1, w1
-      __builtin_amdgcn_s_barrier();
-      const int t2n = min(t + 2, kt1 - 1);
-      stage(t2n, xs0);
-      wload(t2n, w0, s0);
-      wait_tile();
-      compute(xs1, w1, s1);
+      step(t + 1, xs1, w1, s1, xs0, w0, s0);
+      if (t + 2 >= kt1) break;
+      step(t + 2, xs2, w2, s2, xs1, w1, s1);
     }
     // the last loads re-read a tile nobody uses: let them land before the
     // work-group (and its LDS) ends
