@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0      # dense fp16 MFMA (the int4 GEMMs multiply fp16)
 
 
 def log(msg):
@@ -157,6 +158,38 @@ def cpu_baseline(cfg, ctx, budget_s=30.0):
             "step_seconds": step_s}
 
 
+def prefill_gemm_rate(pair, prompt, cfg, ctx):
+    """MFMA throughput of the prompt pass's dense GEMMs: one profiled prompt
+    pass records every launch; the dense ones are replayed back to back
+    between two HIP events on the launch stream.  FLOPs = 2 * rows * the
+    target's projection parameters over the rows that run as dense chunks."""
+    import torch
+    B = cfg.block
+    dense_rows = ((ctx - 1) // B) * B
+    pair.prof(True)
+    pair.prefill(prompt)
+    torch.cuda.synchronize()
+    pair.prof(False)
+    recs = {r["kernel"]: r for r in pair.prof_read()}
+    names = [n for n in ("gemm_dense_w4", "gemm_dense_w4_silu") if n in recs]
+    if not names or dense_rows <= 64:
+        return None
+    ms, launches = 0.0, 0
+    for n in names:
+        m, c = pair.prof_replay(n, reps=1)
+        ms += m
+        launches += c
+    t = cfg.target
+    params = (t.qkv_rows * t.hidden + t.hidden * t.n_q_heads * t.head_dim + 2 * t.ffn * t.hidden
+              + t.hidden * t.ffn) * t.n_layers
+    flops = 2.0 * dense_rows * params
+    achieved = flops / (ms / 1e3) / 1e12
+    log(f"prompt pass dense GEMMs: {launches} launches, {ms:.2f} ms back to back, {achieved:.0f} TFLOP/s")
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_FP16_PEAK_TFLOPS, 4), "kernel": "gemm_dense_w4 (+_silu)",
+            "launches": launches, "dense_rows": dense_rows, "avg_launch_us": round(ms * 1e3 / launches, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +204,8 @@ def main():
                     help="verify only the first N drafts per step (0 = the whole block)")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="speculative sampling at this temperature (drafts drawn, no injection)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="measure only the prompt pass (time to first token) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the draft+verify step of one sequence runs on a single "
@@ -207,13 +242,22 @@ def main():
     t0 = time.time()
     pair.prefill(prompt)
     log(f"prefill {ctx} tokens in {time.time() - t0:.2f} s (first call)")
-    # time to first token: a second prefill of the same prompt (the state is reset by it)
+    dense = None if args.no_prof else prefill_gemm_rate(pair, prompt, cfg, ctx)
+    # time to first token: a prefill of the same prompt (the state is reset by it)
     torch.cuda.synchronize()
     t0 = time.time()
     pair.prefill(prompt)
     prefill_s = time.time() - t0
     pair.snapshot()
     log(f"prefill {ctx} tokens in {prefill_s * 1e3:.1f} ms ({ctx / prefill_s:.0f} tok/s)")
+    prefill = {"tokens": ctx, "ms": round(prefill_s * 1e3, 2), "tok_per_s": round(ctx / prefill_s, 1),
+               "dense_gemm_roofline": dense}
+    if args.prefill_only:
+        print(json.dumps({"metric": "prompt pass tokens/s (time to first token)", "value": prefill["tok_per_s"],
+                          "unit": "tok/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": f"{cfg.name}: prompt of {ctx} tokens", "ctx": ctx},
+                          "prefill": prefill}), flush=True)
+        return
     n_sched = W + K + 8
     sched = torch.as_tensor(synth.accept_schedule(cfg, n_sched, seed=2), device="cuda")
     inj = None
@@ -341,7 +385,7 @@ def main():
         "tokens_per_step": round(tokens / K, 3),
         "bytes_per_step": int(step_bytes),
         "hbm_frac_step": round(step_frac, 4),
-        "prefill": {"tokens": ctx, "ms": round(prefill_s * 1e3, 2), "tok_per_s": round(ctx / prefill_s, 1)},
+        "prefill": prefill,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -831,8 +831,22 @@ __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
   const int nblk = (a.m + 15) >> 4;
-  const int tb0 = blockIdx.y * DENSE_MT;
-  const int rt0 = blockIdx.x * (4 * DENSE_RW) + wave * DENSE_RW;
+  // Work-groups are dealt to the 8 XCDs round-robin by index.  When the
+  // row-tile groups come in multiples of 8, XCD x takes row-tile groups
+  // x, x + 8, ... and runs all token groups of one before the next, so the
+  // weights a group reads stay in that XCD's L2 for all of its token groups.
+  const int ngx = (a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW), ngy = (nblk + DENSE_MT - 1) / DENSE_MT;
+  const int id = blockIdx.x;
+  int gx, gy;
+  if (ngx % 8 == 0) {
+    gx = (id / (8 * ngy)) * 8 + id % 8;
+    gy = (id / 8) % ngy;
+  } else {
+    gx = id % ngx;
+    gy = id / ngx;
+  }
+  const int tb0 = gy * DENSE_MT;
+  const int rt0 = gx * (4 * DENSE_RW) + wave * DENSE_RW;
   const int sidx = blockIdx.z;
   const int kt0 = sidx * kt_per, kt1 = min(a.ktiles, kt0 + kt_per);
   const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
@@ -1018,7 +1032,7 @@ static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipSt
   a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   const int kt_per = (a.ktiles + S - 1) / S;
-  const dim3 grid((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW), (c.m / 16 + DENSE_MT - 1) / DENSE_MT, S);
+  const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + DENSE_MT - 1) / DENSE_MT), 1, S);
   if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_PARTIAL>, grid, dim3(256), 0, s, a, kt_per);
   else hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_SILU>, grid, dim3(256), 0, s, a, kt_per);
   if (splits) *splits = S;
