@@ -792,9 +792,9 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // tile (128 columns) the work-group stages the 16 activation fragments (4
 // blocks x 4 MFMA steps, 1 KiB each) in LDS by direct global->LDS loads while
 // each wave holds its four weight tiles and their group scales in registers;
-// both go through three stages, so the loads of tiles t+1 and t+2 are in
-// flight while tile t is multiplied (one tile of compute is shorter than a
-// load's latency).  The arithmetic is the
+// both are double-buffered, so tile t+1 loads while tile t is multiplied.
+// At most 256 registers a lane, so that two waves share each SIMD and one's
+// MFMAs overlap the other's dequantisation and group-scale FMAs.  The arithmetic is the
 // stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
 // scaled by the group's fp16 scale and accumulated in fp32.
 constexpr int DENSE_MT = 4;                  // token blocks per work-group
@@ -823,10 +823,10 @@ constexpr int DENSE_RW = 4;                  // row tiles per wave
 constexpr int DENSE_MAX_ROWS = 1024;
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_per) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_w4_kernel(GemmArgs a,
+                                                                                          int kt_per) {
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t xs2[DENSE_MT * 4 * 1024];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
@@ -897,26 +897,25 @@ __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_p
         b[i][1] = deq_w4(wd1, mlo, mhi, magic);
         sg[i] = (float)h2(sc[i])[gg];
       }
-      half8 x[DENSE_MT][2];
-#pragma unroll
-      for (int tb = 0; tb < DENSE_MT; ++tb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          x[tb][h] = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + 2 * gg + h) * 1024 + lane * 16));
 #pragma unroll
       for (int hb = 0; hb < DENSE_MT; hb += 2) {
+        half8 x[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            x[j][h] = __builtin_bit_cast(half8, *(const uint4*)(xs + ((hb + j) * 4 + 2 * gg + h) * 1024 + lane * 16));
         floatx4 tmp[2][DENSE_RW];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int i = 0; i < DENSE_RW; ++i)
-            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[hb + j][0], b[i][0], floatx4{0.f, 0.f, 0.f, 0.f},
-                                                               0, 0, 0);
+            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[j][0], b[i][0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int i = 0; i < DENSE_RW; ++i)
-            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[hb + j][1], b[i][1], tmp[j][i], 0, 0, 0);
+            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[j][1], b[i][1], tmp[j][i], 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -926,25 +925,25 @@ __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_p
       }
     }
   };
-  // Every tile's wait lets the loads of the next two tiles (2 x (DENSE_MT
-  // fragment DMAs + 4 weight + 4 scale loads), the youngest) stay in flight;
-  // past the last tile the loads re-read it, so the wait is always the same.
-  // It is kept apart from the first use so that the compiler adds none there.
+  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs, 4
+  // weight and 4 scale loads, the youngest) stay in flight; past the last
+  // tile the loads re-read it, so the wait is always the same.  It is kept
+  // apart from the first use so that the compiler adds none there.
   auto wait_tile = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(2 * (DENSE_MT + 2 * DENSE_RW)));
+    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + 2 * DENSE_RW));
     asm volatile("s_nop 0");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
   };
-  uint4 w0[DENSE_RW], w1[DENSE_RW], w2[DENSE_RW];
-  uint32_t s0[DENSE_RW], s1[DENSE_RW], s2[DENSE_RW];
-  // tile t from stage (xs, w, sc); tile t + 2 goes to stage (xn, wn, sn), the
+  uint4 w0[DENSE_RW], w1[DENSE_RW];
+  uint32_t s0[DENSE_RW], s1[DENSE_RW];
+  // tile t from stage (xs, w, sc); tile t + 1 goes to stage (xn, wn, sn), the
   // one tile t - 1 used: the barrier first lets every wave finish with it
   auto step = [&](int t, const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW], uint8_t* xn,
                   uint4 (&wn)[DENSE_RW], uint32_t (&sn)[DENSE_RW]) {
     __builtin_amdgcn_s_barrier();
-    const int tn = min(t + 2, kt1 - 1);
+    const int tn = min(t + 1, kt1 - 1);
     stage(tn, xn);
     wload(tn, wn, sn);
     wait_tile();
@@ -953,14 +952,10 @@ __global__ __launch_bounds__(256) void gemm_dense_w4_kernel(GemmArgs a, int kt_p
   if (kt0 < kt1) {
     stage(kt0, xs0);
     wload(kt0, w0, s0);
-    stage(min(kt0 + 1, kt1 - 1), xs1);
-    wload(min(kt0 + 1, kt1 - 1), w1, s1);
-    for (int t = kt0; t < kt1; t += 3) {
-      step(t, xs0, w0, s0, xs2, w2, s2);
+    for (int t = kt0; t < kt1; t += 2) {
+      step(t, xs0, w0, s0, xs1, w1, s1);
       if (t + 1 >= kt1) break;
       step(t + 1, xs1, w1, s1, xs0, w0, s0);
-      if (t + 2 >= kt1) break;
-      step(t + 2, xs2, w2, s2, xs1, w1, s1);
     }
     // the last loads re-read a tile nobody uses: let them land before the
     // work-group (and its LDS) ends
