@@ -103,7 +103,7 @@ static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
 }
 
 // rows a dflash_linear call takes: up to 64 for every format, and prompt
-// chunks (multiples of 16 up to 1024) for W4A16 with the fp32 output
+// chunks (multiples of 16 up to 1024) for W4A16 / W8A16 with the fp32 output
 static bool linear_rows_ok(int fmt, int n, int k, int m, int epilogue) {
   if (m >= 1 && m <= MAX_ROWS) return true;
   return epilogue == 0 && dense_ok(fmt, n, k, m, EPI_PARTIAL);
@@ -120,7 +120,7 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   int rc = check_gemm_shape(fmt, n, k, 0);
   if (rc) return rc;
   if (!linear_rows_ok(fmt, n, k, m, epilogue))
-    return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, W4A16 with epilogue 0, a multiple of 16 up to 1024)");
+    return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, W4A16/W8A16 with epilogue 0, a multiple of 16 up to 1024)");
   if (fmt == DFLASH_FMT_F32 && ldx < k) return fail(DFLASH_E_SHAPE, "ldx must be >= k");
   if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
   if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");
@@ -278,6 +278,7 @@ struct dflash_state {
   int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
   int vrows = 0;          // rows a verify runs (B, or fewer under a draft cap)
   int pm = 0;             // rows of a dense prompt chunk (0: prompts run in blocks of B)
+  bool pm_draft = false;  // the drafter's context pass of a chunk runs dense as well
   int max_draft = 0;      // drafts verified per step (0 = the whole block)
   float temp = 0.f;       // sampling temperature (0 = greedy)
   uint64_t seed = 0;
@@ -362,7 +363,8 @@ static void carve(dflash_state* s, Carver& c) {
   // row buffers: a block (+ its context rows), or a dense prompt chunk
   const size_t R = std::max(MAX_ROWS, s->pm), RB = std::max(B, s->pm);
   s->x = c.take<char>(R * H * 4);
-  s->bu = c.take<char>(R * H * 4);
+  // (the drafter's context rows sit after the B block rows)
+  s->bu = c.take<char>(std::max(R, (size_t)B + (s->pm_draft ? s->pm : 0)) * H * 4);
   s->ba = c.take<char>(R * att_w * 4);
   s->bf = c.take<char>(R * F * 4);
   s->bqkv = c.take<char>(R * qkv_n * 4);
@@ -387,6 +389,13 @@ static void carve(dflash_state* s, Carver& c) {
         for (const Layer& L : t->layers)
           for (const GemmW* g : {&L.qkv, &L.o, &L.down})
             pf = std::max(pf, (size_t)dense_splits(g->n, g->k, m, EPI_PARTIAL) * m * g->n);
+  if (s->pm_draft)
+    for (int m = B; m <= s->pm; m += B)
+      if (m > MAX_ROWS) {
+        pf = std::max(pf, (size_t)dense_splits(d->fc.n, d->fc.k, m, EPI_PARTIAL) * m * d->fc.n);
+        for (const Layer& L : d->layers)
+          pf = std::max(pf, (size_t)dense_splits(L.qkv.n, L.qkv.k, m, EPI_PARTIAL) * m * L.qkv.n);
+      }
   for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.down, B); }
   need(d->fc, B);
   am = std::max(1, gemm_am_blocks(t->lm.fmt, t->lm.n, B));
@@ -429,6 +438,14 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
            dense_ok(L.gu.fmt, L.gu.n, L.gu.k, DENSE_PROMPT_ROWS, EPI_SILU) &&
            dense_ok(L.down.fmt, L.down.n, L.down.k, DENSE_PROMPT_ROWS, EPI_PARTIAL);
     if (ok) s->pm = DENSE_PROMPT_ROWS;
+  }
+  // and the drafter's context pass of a chunk, if its projections have the
+  // dense kernel too (else it runs B rows at a time)
+  s->pm_draft = false;
+  if (s->pm) {
+    bool ok = dense_ok(d->fc.fmt, d->fc.n, d->fc.k, s->pm, EPI_PARTIAL);
+    for (const Layer& L : d->layers) ok = ok && dense_ok(L.qkv.fmt, L.qkv.n, L.qkv.k, s->pm, EPI_PARTIAL);
+    s->pm_draft = ok;
   }
   return DFLASH_OK;
 }
@@ -580,16 +597,17 @@ static int ffn(dflash_state* s, const dflash_model* m, const Layer& L, Pending& 
 
 // Context projection of the rows the last verify committed -> QKV input rows
 // B..2B-1 (whole 16-row blocks after the block rows of the tiled input).
-static int draft_context(dflash_state* s, hipStream_t st, int side_row0 = 0) {
+static int draft_context(dflash_state* s, hipStream_t st, int side_row0 = 0, int rows = 0) {
   const dflash_model* d = s->dr;
   const int H = d->d.hidden, B = s->B;
+  if (rows == 0) rows = B;
   // conditioning rows side_row0.. (whole 16-row blocks of the tiled input)
   const void* side = (const char*)s->side + (size_t)side_row0 * d->d.n_sel * H * elem_bytes(d->gin);
   Parts fc;
-  RC(gemm(s, d->fc, side, d->d.n_sel * H, B, EPI_PARTIAL, st, &fc));
+  RC(gemm(s, d->fc, side, d->d.n_sel * H, rows, EPI_PARTIAL, st, &fc));
   NormCall c{};
   c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
-  c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = B;
+  c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = rows;
   c.out = (char*)s->bu + (size_t)B * H * elem_bytes(d->gin); c.otype = d->gin; c.ldo = H; c.tiled = 1;
   HIPCHK(launch_norm(c, st));
   return DFLASH_OK;
@@ -601,18 +619,20 @@ static int draft_context(dflash_state* s, hipStream_t st, int side_row0 = 0) {
 // rows, the attention, the FFNs and the lm-head are not run.  The block rows'
 // cache slots the full draft would write are transient (the next context rows
 // take them before any read).
-static int draft_context_kv(dflash_state* s, hipStream_t st, int side_row0 = 0) {
+// rows = the pending context rows (B, or a whole dense prompt chunk).
+static int draft_context_kv(dflash_state* s, hipStream_t st, int side_row0 = 0, int rows = 0) {
   const dflash_model* d = s->dr;
   const int H = d->d.hidden, B = s->B;
-  RC(draft_context(s, st, side_row0));
+  if (rows == 0) rows = B;
+  RC(draft_context(s, st, side_row0, rows));
   const void* ctx_in = (const char*)s->bu + (size_t)B * H * elem_bytes(d->gin);
   for (int l = 0; l < d->d.n_layers; ++l) {
     const Layer& L = d->layers[l];
     Parts qkv;
-    RC(gemm(s, L.qkv, ctx_in, H, B, EPI_PARTIAL, st, &qkv));
+    RC(gemm(s, L.qkv, ctx_in, H, rows, EPI_PARTIAL, st, &qkv));
     RopeCall rc;
     rc.qkv = qkv; rc.atype = d->act;
-    rc.block_rows = 0; rc.ctx_rows = B;      // partial row j = context row j
+    rc.block_rows = 0; rc.ctx_rows = rows;   // partial row j = context row j
     rc.dev_n = s->scal + SC_N; rc.dev_p = s->scal + SC_P;
     rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = d->d.eps;
     rc.cos_t = s->cos_t; rc.sin_t = s->sin_t; rc.q_out = s->bq;
@@ -734,9 +754,14 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
     while (c0 < dense_end) {
       const int rows = std::min(s->pm, dense_end - c0);
       RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, rows, st, false));
-      for (int j = 0; j < rows; j += s->B) {
-        RC(do_commit(s, nullptr, s->B, nullptr, st));
-        RC(draft_context_kv(s, st, j));
+      if (s->pm_draft) {
+        RC(do_commit(s, nullptr, rows, nullptr, st));
+        RC(draft_context_kv(s, st, 0, rows));
+      } else {
+        for (int j = 0; j < rows; j += s->B) {
+          RC(do_commit(s, nullptr, s->B, nullptr, st));
+          RC(draft_context_kv(s, st, j));
+        }
       }
       c0 += rows;
     }

@@ -124,7 +124,7 @@ struct Workspace {
 // split (nwg = PR * S), align = row tiles per balancing unit (2 for gate/up)
 struct Plan { int RT, MB, S, PR, ngroups, nwg, ktiles, ntile16, align, NW; };
 Plan make_plan(int fmt, int n, int k, int m, int epi);
-// prompt chunks: m in (64, 1024], m % 16 == 0, W4 weights, partial-sum or
+// prompt chunks: m in (64, 1024], m % 16 == 0, W4 or W8 weights (K % 128 == 0), partial-sum or
 // SiLU epilogue (launch_gemm takes this path for m > 64)
 bool dense_ok(int fmt, int n, int k, int m, int epi);
 int dense_splits(int n, int k, int m, int epi);

@@ -784,7 +784,7 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 }
 
 // ------------------------------------------------------- dense (prompt chunks)
-// W4 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
+// W4 / W8 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
 // that the MFMAs, not the weight stream, set the time, so activations are
 // reused across many weight rows instead of being re-read per row tile.
 // Work-group = 4 token blocks (64 rows) x 16 row tiles (256 weight rows) x one
@@ -796,7 +796,8 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // At most 256 registers a lane, so that two waves share each SIMD and one's
 // MFMAs overlap the other's dequantisation and group-scale FMAs.  The arithmetic is the
 // stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
-// scaled by the group's fp16 scale and accumulated in fp32.
+// scaled by the group's fp16 scale and accumulated in fp32 (W8: one fp32
+// sum per row, times the row's fp16 scale at the end).
 constexpr int DENSE_MT = 4;                  // token blocks per work-group
 
 // 16 bytes per lane from src to LDS at lds + 16 * lane.  Issued from asm so
@@ -822,9 +823,14 @@ __device__ __forceinline__ uint32_t gload4(const void* p) {
 constexpr int DENSE_RW = 4;                  // row tiles per wave
 constexpr int DENSE_MAX_ROWS = 1024;
 
-template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_w4_kernel(GemmArgs a,
-                                                                                          int kt_per) {
+// FMT W4: per 128-column step one 1 KiB tile and one scale dword per row
+// tile; W8: two 64-column tiles per row tile and the per-row scale applied to
+// the finished sum (as the stream kernel does).
+template <int FMT, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
+                                                                                       int kt_per) {
+  static_assert(FMT == W_W4 || FMT == W_W8, "dense kernel: int4 or int8 weights");
+  constexpr int WT = FMT == W_W4 ? 1 : 2;     // weight tiles per row tile and 128-column step
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -848,7 +854,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int tb0 = gy * DENSE_MT;
   const int rt0 = gx * (4 * DENSE_RW) + wave * DENSE_RW;
   const int sidx = blockIdx.z;
-  const int kt0 = sidx * kt_per, kt1 = min(a.ktiles, kt0 + kt_per);
+  const int ptiles = a.k >> 7;               // 128-column steps
+  const int kt0 = sidx * kt_per, kt1 = min(ptiles, kt0 + kt_per);
   const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
   const size_t xfrag = (size_t)(a.k >> 5);
   uint32_t rtile[DENSE_RW];                  // row tiles past the end re-read the last one
@@ -872,12 +879,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       lds_dma16(src, (uint32_t)(uintptr_t)(lds_ptr)(xs + f * 1024));
     }
   };
-  auto wload = [&](int t, uint4 (&w)[DENSE_RW], uint32_t (&sc)[DENSE_RW]) {
+  // 2*DENSE_RW loads per step either way: W4 a tile and a scale dword, W8
+  // two tiles, per row tile
+  auto wload = [&](int t, uint4 (&w)[DENSE_RW][WT], uint32_t (&sc)[DENSE_RW]) {
 #pragma unroll
     for (int i = 0; i < DENSE_RW; ++i) {
-      const size_t tile = (size_t)rtile[i] * a.ktiles + t;
-      w[i] = gload16_nt(a.w + tile * 1024 + lane * 16);
-      sc[i] = gload4(a.s + tile * 32 + lr * 2);
+      const size_t tile = (size_t)rtile[i] * a.ktiles + (size_t)t * WT;
+      w[i][0] = gload16_nt(a.w + tile * 1024 + lane * 16);
+      if (FMT == W_W4) sc[i] = gload4(a.s + tile * 32 + lr * 2);
+      else w[i][WT - 1] = gload16_nt(a.w + (tile + 1) * 1024 + lane * 16);
     }
   };
   // Per 64-wide group: its two weight steps dequantised for the 4 row tiles,
@@ -885,14 +895,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // each half of the token blocks 8 independent MFMA chains (2 MFMAs each)
   // before their sums are scaled into the accumulators, so no MFMA waits on
   // the one before it and no FMA on an MFMA just issued.
-  auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW]) {
+  auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW][WT], const uint32_t (&sc)[DENSE_RW]) {
+    if (FMT == W_W8) {
+      // 4 MFMA steps straight into the accumulators; step ks is dwords
+      // 2(ks%2), 2(ks%2)+1 of tile ks/2
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        half8 b[DENSE_RW];
+#pragma unroll
+        for (int i = 0; i < DENSE_RW; ++i) {
+          const uint4 wt = w[i][(ks >> 1) & (WT - 1)];
+          b[i] = (ks & 1) ? deq_w8(wt.z, wt.w, magic) : deq_w8(wt.x, wt.y, magic);
+        }
+#pragma unroll
+        for (int tb = 0; tb < DENSE_MT; ++tb) {
+          const half8 x = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + ks) * 1024 + lane * 16));
+#pragma unroll
+          for (int i = 0; i < DENSE_RW; ++i)
+            acc[tb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, b[i], acc[tb][i], 0, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
       half8 b[DENSE_RW][2];
       float sg[DENSE_RW];
 #pragma unroll
       for (int i = 0; i < DENSE_RW; ++i) {
-        const uint32_t wd0 = gg ? w[i].z : w[i].x, wd1 = gg ? w[i].w : w[i].y;
+        const uint32_t wd0 = gg ? w[i][0].z : w[i][0].x, wd1 = gg ? w[i][0].w : w[i][0].y;
         b[i][0] = deq_w4(wd0, mlo, mhi, magic);
         b[i][1] = deq_w4(wd1, mlo, mhi, magic);
         sg[i] = (float)h2(sc[i])[gg];
@@ -936,12 +967,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
   };
-  uint4 w0[DENSE_RW], w1[DENSE_RW];
+  uint4 w0[DENSE_RW][WT], w1[DENSE_RW][WT];
   uint32_t s0[DENSE_RW], s1[DENSE_RW];
   // tile t from stage (xs, w, sc); tile t + 1 goes to stage (xn, wn, sn), the
   // one tile t - 1 used: the barrier first lets every wave finish with it
-  auto step = [&](int t, const uint8_t* xs, const uint4 (&w)[DENSE_RW], const uint32_t (&sc)[DENSE_RW], uint8_t* xn,
-                  uint4 (&wn)[DENSE_RW], uint32_t (&sn)[DENSE_RW]) {
+  auto step = [&](int t, const uint8_t* xs, const uint4 (&w)[DENSE_RW][WT], const uint32_t (&sc)[DENSE_RW],
+                  uint8_t* xn, uint4 (&wn)[DENSE_RW][WT], uint32_t (&sn)[DENSE_RW]) {
     __builtin_amdgcn_s_barrier();
     const int tn = min(t + 1, kt1 - 1);
     stage(tn, xn);
@@ -964,18 +995,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   // lane (lr, g) holds weight row (rt0 + i)*16 + lr for tokens
   // (tb0 + tb)*16 + 4g + v
+  // W8: the row's fp16 scale on the finished sum; W4 sums are scaled already
+  auto scale_of = [&](int n) -> float {
+    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, a.s[n]) : 1.0f;
+  };
   if (EPI == EPI_PARTIAL) {
     float* part = a.part + (size_t)sidx * a.m * a.n;
 #pragma unroll
     for (int i = 0; i < DENSE_RW; ++i) {
       if (rt0 + i >= a.ntile16) continue;
       const int n = (rt0 + i) * 16 + lr;
+      const float sc = scale_of(n);
 #pragma unroll
       for (int tb = 0; tb < DENSE_MT; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = (tb0 + tb) * 16 + 4 * g + v;
-          if (t < a.m) part[(size_t)t * a.n + n] = acc[tb][i][v];
+          if (t < a.m) part[(size_t)t * a.n + n] = acc[tb][i][v] * sc;
         }
     }
   } else {  // EPI_SILU: row tiles (2p, 2p+1) are a (gate, up) pair
@@ -985,14 +1021,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     for (int p = 0; p < DENSE_RW / 2; ++p) {
       if (rt0 + 2 * p + 1 >= a.ntile16) continue;
       const int n_out = ((rt0 >> 1) + p) * 16 + lr;
+      const int ng = (rt0 + 2 * p) * 16 + lr;
+      const float sg = scale_of(ng), su = scale_of(ng + 16);
 #pragma unroll
       for (int tb = 0; tb < DENSE_MT; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = (tb0 + tb) * 16 + 4 * g + v;
           if (t >= a.m) continue;
-          const float gv = act_round(rnd, acc[tb][2 * p][v]);
-          const float uv = act_round(rnd, acc[tb][2 * p + 1][v]);
+          const float gv = act_round(rnd, acc[tb][2 * p][v] * sg);
+          const float uv = act_round(rnd, acc[tb][2 * p + 1][v] * su);
           const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
           store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
         }
@@ -1012,7 +1050,7 @@ int dense_splits(int n, int k, int m, int epi) {
 }
 
 bool dense_ok(int fmt, int n, int k, int m, int epi) {
-  return fmt == W_W4 && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
+  return (fmt == W_W4 || fmt == W_W8) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
          (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
 }
 
@@ -1023,13 +1061,18 @@ static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipSt
   if (c.epi == EPI_PARTIAL && (size_t)S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
   GemmArgs a{};
   a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
-  a.n = W.n; a.k = W.k; a.ktiles = W.k / 128; a.ntile16 = W.n / 16; a.m = c.m; a.splits = S; a.align = 1;
+  a.n = W.n; a.k = W.k; a.ktiles = W.k / tile_k(W.fmt); a.ntile16 = W.n / 16; a.m = c.m; a.splits = S; a.align = 1;
   a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
-  const int kt_per = (a.ktiles + S - 1) / S;
+  const int kt_per = (W.k / 128 + S - 1) / S;
   const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + DENSE_MT - 1) / DENSE_MT), 1, S);
-  if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_PARTIAL>, grid, dim3(256), 0, s, a, kt_per);
-  else hipLaunchKernelGGL(gemm_dense_w4_kernel<EPI_SILU>, grid, dim3(256), 0, s, a, kt_per);
+  if (W.fmt == W_W4) {
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU>), grid, dim3(256), 0, s, a, kt_per);
+  } else {
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU>), grid, dim3(256), 0, s, a, kt_per);
+  }
   if (splits) *splits = S;
   return hipGetLastError();
 }
@@ -1063,7 +1106,9 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
     return launch_argmax_rows(w.logits_tmp, W.n, W.n, c.row0, c.m - c.row0, c.am_out, c.logits, c.ldl, s);
   }
   if (c.m > MAX_ROWS) {
-    if (variant) *variant = c.epi == EPI_SILU ? "gemm_dense_w4_silu" : "gemm_dense_w4";
+    if (variant)
+      *variant = W.fmt == W_W4 ? (c.epi == EPI_SILU ? "gemm_dense_w4_silu" : "gemm_dense_w4")
+                               : (c.epi == EPI_SILU ? "gemm_dense_w8_silu" : "gemm_dense_w8");
     return launch_gemm_dense(c, w, s, splits);
   }
   const Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);

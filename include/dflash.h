@@ -107,11 +107,12 @@ int dflash_pack_weight(int fmt, int n, int k, int gate_up, const void *d_src_cod
  *   d_ws     device workspace of dflash_linear_workspace_bytes(fmt,n,k,m)
  *            bytes, zero-filled once before first use (every call leaves its
  *            counters zero again).
- *   Prompt chunks: W4A16 with epilogue 0 also takes m = 80, 96, ..., 1024
- *            (multiples of 16 above 64).  These run the dense kernel prefill
- *            uses (activations staged in LDS and reused across 256 weight
- *            rows; same exact dequantisation: fp16 MFMA on the raw codes, one
- *            fp32 sum per 64-wide group times its scale).
+ *   Prompt chunks: W4A16 and W8A16 (K % 128 == 0) with epilogue 0 also take
+ *            m = 80, 96, ..., 1024 (multiples of 16 above 64).  These run the
+ *            dense kernel prefill uses (activations staged in LDS and reused
+ *            across 256 weight rows; same exact dequantisation: fp16 MFMA on
+ *            the raw codes, one fp32 sum per 64-wide group times its scale for
+ *            W4, the row scale on the finished sum for W8).
  * Errors: SHAPE for unsupported dims, INVALID for null pointers or an
  * undersized workspace. */
 size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m);

@@ -128,6 +128,8 @@ def test_linear_rows_beyond_the_limits_are_refused():
     L = bn.lib()
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 72) == 0      # not a multiple of 16
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 1040) == 0    # above 1024
-    assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 512, 128) == 0     # the dense path is W4 only
+    assert L.dflash_linear_workspace_bytes(C.FMT_BF16, 256, 512, 128) == 0      # dense path: W4 and W8 only
+    assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 448, 128) == 0     # W8 dense needs K % 128
+    assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 64) > 0

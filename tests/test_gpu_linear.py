@@ -182,6 +182,24 @@ def test_linear_dense_w4_parity(n, k, m):
     assert np.all(np.abs(y - ref) <= bound(x, w))
 
 
+@pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 4096, 512), (4096, 20480, 96)])
+def test_linear_dense_w8_parity(n, k, m):
+    # the int8 dense path (the drafter's context pass of a prompt chunk):
+    # the row scale on the finished sum
+    g = synth.HostSynth(303)
+    w = g.weight(f"dense8_{n}x{k}", n, k, C.FMT_W8A16)
+    x = x_values(np.random.default_rng(n + k + m + 1), m, k, C.FMT_W8A16)
+    y, _, _ = run_linear(w, x, C.FMT_W8A16)
+    if n * k > 4096 * 4096:                    # full-size drafter fc: sampled rows
+        for r0 in (0, 2048, n - 16):
+            ref = linear(x, w, rows=(r0, r0 + 16))
+            assert np.all(np.abs(y[:, r0:r0 + 16] - ref) <= bound(x, w, rows=(r0, r0 + 16)))
+        return
+    ref = linear(x, w)
+    assert np.all(np.isfinite(y))
+    assert np.all(np.abs(y - ref) <= bound(x, w))
+
+
 def test_linear_dense_w4_repeat_is_bitwise():
     g = synth.HostSynth(301)
     w = g.weight("dense_rep", 1024, 4096, C.FMT_W4A16)
