@@ -334,10 +334,228 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   ml_part[row * 2 + 1] = l;
 }
 
+// ------------------------------------------------ prompt-chunk attention
+// Causal attention of a prompt chunk (B > 64 rows at positions n..n+B-1) in
+// one pass, no split-KV partials: work-group = (group of 4 row blocks, KV
+// head), as in attn_mfma_kernel, and it walks the keys 0..n+t_last (t_last
+// its last token) in stages of 128 keys (2 pages of K and 2 of V^T), staged
+// by direct global->LDS loads into two buffers so that stage s+1 loads while
+// stage s is multiplied.  Per stage and row: scores, the row's running max
+// m, p = exp2(s - m) as bf16 hi + lo (16 significant bits), the running sum
+// l and O^T rescaled by exp2(m_old - m) when the max grows (the split-KV
+// combine's arithmetic applied stage by stage).  The normalised row goes
+// straight to the O projection's input.
+constexpr int PF_PAGES = 2;                            // pages per stage
+constexpr int PF_KEYS = PF_PAGES * PAGE;               // 128 keys
+constexpr int PF_DMAS = 4 * PF_PAGES;                  // K (or V^T) DMAs per wave and stage
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, void* out, int otype, int ldo) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t ldsK0[PF_PAGES * 16384];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsV0[PF_PAGES * 16384];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsK1[PF_PAGES * 16384];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsV1[PF_PAGES * 16384];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y;
+  const int G = a.hq / a.hkv;
+  const int nrb = G * a.B / 16;
+  const int rbi = blockIdx.x * 4 + wave;
+  const bool live = rbi < nrb;                 // wave-uniform
+  const int rb = live ? rbi : nrb - 1;
+  const int r = rb * 16 + lr;
+  const int tok = r / G, qh = h * G + r % G;
+  bf16x8 qf[4];
+  {
+    const uint16_t* qp = a.q + ((size_t)tok * a.hq + qh) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks));
+  }
+  // the page table (at most 128 pages: 8192 positions), lane l holding pages
+  // l and 64 + l, read before the first stage
+  const int pg0 = a.pt[min(lane, a.npages - 1)], pg1 = a.pt[min(64 + lane, a.npages - 1)];
+  const int n = *a.dev_n;
+  // keys 0..n+t_last of the work-group's last row
+  const int t_last = (min(blockIdx.x * 4 + 3, nrb - 1) * 16 + 15) / G;
+  const int nst = (n + t_last + 1 + PF_KEYS - 1) / PF_KEYS;
+  // the q fragments and the page table are in registers before the first
+  // stage: inside the loop the only vector-memory operations are the stage
+  // loads, waited for explicitly
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // stage s: K pages into kb, V^T pages into vb (wave w issues blocks w, w+4,
+  // w+8, w+12 of each 16 KiB page; pages past the table re-read the last one,
+  // their keys are masked)
+  auto page_of = [&](int pi) {
+    pi = min(pi, a.npages - 1);
+    return pi < 64 ? __builtin_amdgcn_readlane(pg0, pi) : __builtin_amdgcn_readlane(pg1, pi - 64);
+  };
+  auto stage = [&](int st, uint8_t* kb, uint8_t* vb) {
+#pragma unroll
+    for (int p = 0; p < PF_PAGES; ++p) {
+      const size_t pbase = ((size_t)page_of(st * PF_PAGES + p) * a.hkv + h) * PAGE * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = wave + 4 * j;
+        const int q = blk * 64 + lane;
+        const int key = q >> 4, c = (q & 15) ^ (key & 15);
+        lds_dma16(a.kc + pbase + key * D + c * 8, lds_addr(kb + (size_t)p * 16384 + blk * 1024));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PF_PAGES; ++p) {
+      const size_t pbase = ((size_t)page_of(st * PF_PAGES + p) * a.hkv + h) * PAGE * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = wave + 4 * j;
+        const int q = blk * 64 + lane;
+        const int d = q >> 3, c = (q & 7) ^ ((d >> 1) & 7);
+        lds_dma16(a.vc + pbase + d * PAGE + c * 8, lds_addr(vb + (size_t)p * 16384 + blk * 1024));
+      }
+    }
+  };
+
+  float m_run = -INFINITY, lsum = 0.f;
+  floatx4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int kmax = n + tok;                    // last key this row sees
+
+  auto compute = [&](int st, const uint8_t* kb, const uint8_t* vb) {
+    constexpr int NT = PF_KEYS / 16;
+    const int key0 = st * PF_KEYS;
+    // the K pages of the stage are in LDS once at most its V^T loads and the
+    // next stage's loads are outstanding
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(PF_DMAS + 2 * PF_DMAS));
+    asm volatile("s_nop 0");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    uint32_t ph[NT / 2][4], pl[NT / 2][4];
+    float alpha = 1.f;
+    if (live) {
+      float sv[NT][4];
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) {
+        const int p = kt >> 2, key = (kt & 3) * 16 + lr;
+        const uint8_t* kpage = kb + (size_t)p * 16384 + (size_t)key * 256;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int c = (4 * ks + g) ^ (key & 15);
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sv[kt][v] = acc[v] * a.scale2;
+      }
+      if (key0 + PF_KEYS - 1 > n) {            // the stage reaches into the chunk: causal mask
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (key0 + kt * 16 + 4 * g + v > kmax) sv[kt][v] = -INFINITY;
+      }
+      float mx = m_run;
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(sv[kt][0], sv[kt][1]), fmaxf(sv[kt][2], sv[kt][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // a row that sees no key yet keeps m = -inf and subtracts 0 (no NaN);
+      // its p are 0
+      const float mref = mx == -INFINITY ? 0.f : mx;
+      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mref);
+      m_run = mx;
+      lsum *= alpha;
+#pragma unroll
+      for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float pe = __builtin_amdgcn_exp2f(sv[2 * ks2 + hh][v] - mref);
+            lsum += pe;
+            const uint32_t u = __float_as_uint(pe);
+            const float hv = __uint_as_float(u & 0xffff0000u);
+            const uint32_t lu = __float_as_uint(pe - hv);
+            hb[v] = u;
+            lb[v] = lu + 0x7fffu + ((lu >> 16) & 1u);
+          }
+          ph[ks2][2 * hh] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+          ph[ks2][2 * hh + 1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
+          pl[ks2][2 * hh] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
+          pl[ks2][2 * hh + 1] = __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u);
+        }
+      }
+    }
+    // and its V^T pages once only the next stage's loads are outstanding
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * PF_DMAS));
+    asm volatile("s_nop 0");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    if (!live) return;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[dt][v] *= alpha;
+#pragma unroll
+    for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
+      const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[ks2][0], ph[ks2][1], ph[ks2][2], ph[ks2][3]});
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[ks2][0], pl[ks2][1], pl[ks2][2], pl[ks2][3]});
+      const int p = ks2 >> 1;
+      const uint8_t* vpage = vb + (size_t)p * 16384;
+      const int c0 = 4 * (ks2 & 1) + (g >> 1), hoff = (g & 1) * 8;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = dt * 16 + lr, sw = (d >> 1) & 7;
+        const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + hoff);
+        const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + hoff);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // stages 2i from buffer 0 and 2i+1 from buffer 1; the stage after the one
+  // being multiplied loads into the other buffer (past the last stage the
+  // last one again, so that every wait counts the same loads).  The barrier
+  // at the top of each stage lets every wave finish with that buffer first.
+  stage(0, ldsK0, ldsV0);
+  for (int st = 0; st < nst; st += 2) {
+    __builtin_amdgcn_s_barrier();
+    stage(min(st + 1, nst - 1), ldsK1, ldsV1);
+    compute(st, ldsK0, ldsV0);
+    if (st + 1 >= nst) break;
+    __builtin_amdgcn_s_barrier();
+    stage(min(st + 2, nst - 1), ldsK0, ldsV0);
+    compute(st + 1, ldsK1, ldsV1);
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));      // the last (unused) loads land before the LDS is released
+  if (!live) return;
+
+  // normalised O of row (tok, qh): lane holds d = dt*16 + 4g + v
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const int fmK = otype == T_F32 ? 0 : a.hq * D;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      store_act(out, act_index(tok, qh * D + dt * 16 + 4 * g + v, ldo, fmK), otype, o[dt][v] * inv);
+}
+
+// thread are issued before any is consumed (no dependent load chain).
 // ------------------------------------------------------------ combine
 // Merge the per-split partials of one query row: M = max m_s,
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  All split loads of a
-// thread are issued before any is consumed (no dependent load chain).
+
 constexpr int COMBINE_MAX_SPLITS = 32;
 
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
@@ -402,6 +620,11 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     a.npages = c.npages;
     const int nrb = (c.hq / c.hkv) * c.block_rows / 16;
     if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
+    if (c.block_rows > 64 && c.causal && c.d == 128 && c.npages <= 128) {
+      // a prompt chunk: one pass over the keys, normalised output, no combine
+      hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4, c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();

@@ -152,6 +152,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15: not waited on)
 constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// 16 bytes per lane from src to LDS at lds + 16 * lane (lds wave-uniform).
+// Issued from asm so that the compiler does not track it: its wait analysis
+// would otherwise drain every such load before unrelated register reads.
+// Callers wait for it with explicit vmcnt waits (a vector-memory load, in
+// issue order with the others).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr)p; }
 
 constexpr int MAX_SPLITS = 8;
 // All S loads are issued before the first add (S <= MAX_SPLITS), so the

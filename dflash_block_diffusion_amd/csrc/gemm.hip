@@ -800,13 +800,6 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // sum per row, times the row's fp16 scale at the end).
 constexpr int DENSE_MT = 4;                  // token blocks per work-group
 
-// 16 bytes per lane from src to LDS at lds + 16 * lane.  Issued from asm so
-// that the compiler does not track it: its wait analysis would otherwise
-// drain every such load before unrelated register reads.  Callers wait for it
-// with explicit vmcnt waits (it is a vector-memory load in issue order).
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-}
 // The pipeline's register loads go the same way (weights non-temporal): the
 // explicit per-tile wait is then the only one, and every register they write
 // is read only after it (the waits are scheduling barriers).
