@@ -331,7 +331,7 @@ struct Carver {
 static int gdn_rec(const dflash_model* t) { return t->d.gdn_dk + t->d.gdn_dv + 2; }
 
 // rows of a dense prompt chunk (a multiple of both block sizes)
-constexpr int DENSE_PROMPT_ROWS = 512;
+constexpr int DENSE_PROMPT_ROWS = 1024;
 
 static void carve(dflash_state* s, Carver& c) {
   const dflash_model *t = s->t, *d = s->dr;

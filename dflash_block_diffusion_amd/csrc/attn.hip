@@ -338,18 +338,20 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
 // Causal attention of a prompt chunk (B > 64 rows at positions n..n+B-1) in
 // one pass, no split-KV partials: work-group = (group of 4 row blocks, KV
 // head), as in attn_mfma_kernel, and it walks the keys 0..n+t_last (t_last
-// its last token) in stages of 128 keys (2 pages of K and 2 of V^T), staged
+// its last token) in stages of 64 keys (a page of K and one of V^T), staged
 // by direct global->LDS loads into two buffers so that stage s+1 loads while
-// stage s is multiplied.  Per stage and row: scores, the row's running max
+// stage s is multiplied.  64 KiB of LDS and at most 256 registers per wave
+// let two work-groups share a CU, so one's MFMAs overlap the other's
+// softmax.  Per stage and row: scores, the row's running max
 // m, p = exp2(s - m) as bf16 hi + lo (16 significant bits), the running sum
 // l and O^T rescaled by exp2(m_old - m) when the max grows (the split-KV
 // combine's arithmetic applied stage by stage).  The normalised row goes
 // straight to the O projection's input.
-constexpr int PF_PAGES = 2;                            // pages per stage
-constexpr int PF_KEYS = PF_PAGES * PAGE;               // 128 keys
+constexpr int PF_PAGES = 1;                            // pages per stage
+constexpr int PF_KEYS = PF_PAGES * PAGE;               // 64 keys
 constexpr int PF_DMAS = 4 * PF_PAGES;                  // K (or V^T) DMAs per wave and stage
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, void* out, int otype, int ldo) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_prefill_kernel(AttnArgs a, void* out, int otype, int ldo) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ldsK0[PF_PAGES * 16384];
   __shared__ __attribute__((aligned(16))) uint8_t ldsV0[PF_PAGES * 16384];
@@ -358,10 +360,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, void* out
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y;
+  // work-group i serves KV head i mod hkv: the 8 XCDs take work-groups
+  // round-robin, so with hkv = 8 each XCD's L2 only ever holds one head's
+  // K/V pages (with hkv = 4, two XCDs share a head)
+  const int h = blockIdx.x % a.hkv, wg = blockIdx.x / a.hkv;
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
-  const int rbi = blockIdx.x * 4 + wave;
+  const int rbi = wg * 4 + wave;
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
   const int r = rb * 16 + lr;
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, void* out
   const int pg0 = a.pt[min(lane, a.npages - 1)], pg1 = a.pt[min(64 + lane, a.npages - 1)];
   const int n = *a.dev_n;
   // keys 0..n+t_last of the work-group's last row
-  const int t_last = (min(blockIdx.x * 4 + 3, nrb - 1) * 16 + 15) / G;
+  const int t_last = (min(wg * 4 + 3, nrb - 1) * 16 + 15) / G;
   const int nst = (n + t_last + 1 + PF_KEYS - 1) / PF_KEYS;
   // the q fragments and the page table are in registers before the first
   // stage: inside the loop the only vector-memory operations are the stage
@@ -622,7 +627,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
     if (c.block_rows > 64 && c.causal && c.d == 128 && c.npages <= 128) {
       // a prompt chunk: one pass over the keys, normalised output, no combine
-      hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4, c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo);
+      hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4 * c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo);
       return hipGetLastError();
     }
     hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);

@@ -233,15 +233,18 @@ def test_reduced_lockstep(name, P):
     assert stats["compared"] >= len(forced) * cfg.block
 
 
-@pytest.mark.parametrize("P", [700, 545, 96, 33])
+@pytest.mark.parametrize("P", [1200, 700, 545, 96, 33])
 def test_reduced_8b_dense_prompt_chunks_lockstep(P):
-    # 700 prompt tokens: dense chunks of 512 and 160 rows (the int4 prompt
-    # GEMM, attention over a 512-row block), then the last 28 tokens as a
-    # block; 545: chunks of 512 and 32 rows, then a 1-token block; 96: one
-    # 64-row chunk on the block GEMMs; 33: one 32-row chunk
+    # 1200 prompt tokens: dense chunks of 1024 and 160 rows (the int4 prompt
+    # GEMM and the one-pass prompt attention; the second chunk attends over
+    # the first), then the last 16 tokens as a block; 700: one 672-row chunk,
+    # then 28 tokens; 545: one 544-row chunk, then a 1-token block; 96: one
+    # 64-row chunk on the block GEMMs and split-KV attention; 33: one 32-row
+    # chunk
     cfg = reduced("8b")
     _, _, stats, _ = lockstep(cfg, P, [0, 31, 9])
     assert stats["compared"] >= 3 * cfg.block
+
 
 
 def test_rollback_replays_identically():
