@@ -91,7 +91,7 @@ static LinearWs linear_ws_layout(int fmt, int n, int k, int m) {
   LinearWs L;
   size_t off = 0;
   auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
-  const int S = m > MAX_ROWS ? dense_splits(n, k, m, EPI_PARTIAL) : make_plan(fmt, n, k, m, EPI_PARTIAL).S;
+  const int S = m > MAX_ROWS ? dense_splits(fmt, n, k, m, EPI_PARTIAL) : make_plan(fmt, n, k, m, EPI_PARTIAL).S;
   L.part_floats = (size_t)S * m * n;
   L.part_off = take(L.part_floats * 4);
   const int am = m > MAX_ROWS ? 1 : std::max(1, gemm_am_blocks(fmt, n, m));
@@ -388,13 +388,13 @@ static void carve(dflash_state* s, Carver& c) {
       if (m > MAX_ROWS)
         for (const Layer& L : t->layers)
           for (const GemmW* g : {&L.qkv, &L.o, &L.down})
-            pf = std::max(pf, (size_t)dense_splits(g->n, g->k, m, EPI_PARTIAL) * m * g->n);
+            pf = std::max(pf, (size_t)dense_splits(g->fmt, g->n, g->k, m, EPI_PARTIAL) * m * g->n);
   if (s->pm_draft)
     for (int m = B; m <= s->pm; m += B)
       if (m > MAX_ROWS) {
-        pf = std::max(pf, (size_t)dense_splits(d->fc.n, d->fc.k, m, EPI_PARTIAL) * m * d->fc.n);
+        pf = std::max(pf, (size_t)dense_splits(d->fc.fmt, d->fc.n, d->fc.k, m, EPI_PARTIAL) * m * d->fc.n);
         for (const Layer& L : d->layers)
-          pf = std::max(pf, (size_t)dense_splits(L.qkv.n, L.qkv.k, m, EPI_PARTIAL) * m * L.qkv.n);
+          pf = std::max(pf, (size_t)dense_splits(L.qkv.fmt, L.qkv.n, L.qkv.k, m, EPI_PARTIAL) * m * L.qkv.n);
       }
   for (const Layer& L : d->layers) { need(L.qkv, 2 * B); need(L.o, B); need(L.down, B); }
   need(d->fc, B);

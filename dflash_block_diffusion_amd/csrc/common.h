@@ -127,7 +127,7 @@ Plan make_plan(int fmt, int n, int k, int m, int epi);
 // prompt chunks: m in (64, 1024], m % 16 == 0, W4 or W8 weights (K % 128 == 0), partial-sum or
 // SiLU epilogue (launch_gemm takes this path for m > 64)
 bool dense_ok(int fmt, int n, int k, int m, int epi);
-int dense_splits(int n, int k, int m, int epi);
+int dense_splits(int fmt, int n, int k, int m, int epi);
 struct Workspace;
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,

@@ -787,10 +787,11 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // W4 / W8 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
 // that the MFMAs, not the weight stream, set the time, so activations are
 // reused across many weight rows instead of being re-read per row tile.
-// Work-group = 4 token blocks (64 rows) x 16 row tiles (256 weight rows) x one
-// of S K ranges; wave w owns row tiles 4w..4w+3 for all 4 token blocks.  Per K
-// tile (128 columns) the work-group stages the 16 activation fragments (4
-// blocks x 4 MFMA steps, 1 KiB each) in LDS by direct global->LDS loads while
+// Work-group = MT token blocks (MT = 4 or 8: 64 or 128 rows) x 16 row tiles
+// (256 weight rows) x one of S K ranges; wave w owns row tiles 4w..4w+3 for
+// all MT token blocks.  Per K tile (128 columns) the work-group stages the
+// 4*MT activation fragments (MT blocks x 4 MFMA steps, 1 KiB each) in LDS by
+// direct global->LDS loads while
 // each wave holds its four weight tiles and their group scales in registers;
 // both are double-buffered, so tile t+1 loads while tile t is multiplied.
 // At most 256 registers a lane, so that two waves share each SIMD and one's
@@ -798,7 +799,11 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 // stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
 // scaled by the group's fp16 scale and accumulated in fp32 (W8: one fp32
 // sum per row, times the row's fp16 scale at the end).
-constexpr int DENSE_MT = 4;                  // token blocks per work-group
+// MT = 8 halves the dequantisation and the weight loads per MFMA (each
+// weight tile serves 128 rows) but needs 128 accumulators per lane and halves
+// the grid; it is taken for the large int4 shapes of long chunks (measured on
+// the 8B-class prompt pass: gate/up 11 % and down 5 % faster at 1024 rows,
+// QKV and O no faster).
 
 // The pipeline's register loads go the same way (weights non-temporal): the
 // explicit per-tile wait is then the only one, and every register they write
@@ -819,10 +824,11 @@ constexpr int DENSE_MAX_ROWS = 1024;
 // FMT W4: per 128-column step one 1 KiB tile and one scale dword per row
 // tile; W8: two 64-column tiles per row tile and the per-row scale applied to
 // the finished sum (as the stream kernel does).
-template <int FMT, int EPI>
+template <int FMT, int EPI, int DENSE_MT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
                                                                                        int kt_per) {
   static_assert(FMT == W_W4 || FMT == W_W8, "dense kernel: int4 or int8 weights");
+  static_assert(DENSE_MT == 4 || (DENSE_MT == 8 && FMT == W_W4), "dense kernel: 4 token blocks, or 8 for int4");
   constexpr int WT = FMT == W_W4 ? 1 : 2;     // weight tiles per row tile and 128-column step
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
@@ -1031,12 +1037,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+// token blocks per work-group: 8 for int4 chunks of more than 512 rows with
+// a wide N (gate/up) or a deep K (down), else 4
+static int dense_mt(int fmt, int n, int k, int m) {
+  return fmt == W_W4 && m > 512 && (n >= 16384 || k >= 8192) ? 8 : 4;
+}
+
 // K splits of a dense launch: partial sums go to S slices so that the grid
 // reaches the chip's 256 CUs, each split keeping at least 4 K tiles
-int dense_splits(int n, int k, int m, int epi) {
+int dense_splits(int fmt, int n, int k, int m, int epi) {
   if (epi != EPI_PARTIAL) return 1;
-  const int ktiles = k / 128;
-  const int base = ((n / 16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((m / 16 + DENSE_MT - 1) / DENSE_MT);
+  const int ktiles = k / 128, mt = dense_mt(fmt, n, k, m);
+  const int base = ((n / 16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((m / 16 + mt - 1) / mt);
   int S = 1;
   while (S < MAX_SPLITS && base * S < 256 && ktiles / (2 * S) >= 4) S *= 2;
   return S;
@@ -1050,7 +1062,7 @@ bool dense_ok(int fmt, int n, int k, int m, int epi) {
 static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t s, int* splits) {
   const GemmW& W = *c.W;
   if (!dense_ok(W.fmt, W.n, W.k, c.m, c.epi)) return hipErrorInvalidValue;
-  const int S = dense_splits(W.n, W.k, c.m, c.epi);
+  const int S = dense_splits(W.fmt, W.n, W.k, c.m, c.epi), mt = dense_mt(W.fmt, W.n, W.k, c.m);
   if (c.epi == EPI_PARTIAL && (size_t)S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
   GemmArgs a{};
   a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
@@ -1058,13 +1070,16 @@ static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipSt
   a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   const int kt_per = (W.k / 128 + S - 1) / S;
-  const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + DENSE_MT - 1) / DENSE_MT), 1, S);
-  if (W.fmt == W_W4) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU>), grid, dim3(256), 0, s, a, kt_per);
+  const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + mt - 1) / mt), 1, S);
+  if (W.fmt == W_W4 && mt == 8) {
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 8>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 8>), grid, dim3(256), 0, s, a, kt_per);
+  } else if (W.fmt == W_W4) {
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
   } else {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU>), grid, dim3(256), 0, s, a, kt_per);
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
   }
   if (splits) *splits = S;
   return hipGetLastError();

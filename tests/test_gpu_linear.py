@@ -168,8 +168,10 @@ def test_lm_head_argmax_full_size():
 # ------------------------------------------------------------ prompt chunks
 # m > 64 (multiples of 16) takes the dense W4 kernel of prefill: activations
 # staged in LDS and shared by 256 weight rows, K split for the partial sums.
+# Past 512 rows, N >= 16384 or K >= 8192 take the 8-token-block work-group.
 @pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 4096, 1024), (4128, 512, 96),
-                                   (784, 2048, 512), (256, 128, 208)])
+                                   (784, 2048, 512), (256, 128, 208), (16400, 256, 784), (272, 8192, 1008),
+                                   (16384, 128, 528)])
 def test_linear_dense_w4_parity(n, k, m):
     # ragged row-tile groups (N/16 not a multiple of 16), ragged token groups
     # (m/16 not a multiple of 4), one K tile, splits of uneven length
@@ -213,6 +215,8 @@ DENSE_FULL = [  # the target projections of an 8B / 27B prompt chunk
     ("8b_qkv_dense", 6144, 4096, 512),
     ("8b_down_dense", 4096, 12288, 512),
     ("8b_o_dense", 4096, 4096, 1024),
+    ("8b_down_dense_1024", 4096, 12288, 1024),
+    ("8b_gateup_dense_1024", 24576, 4096, 1024),
     ("27b_gateup_dense", 34816, 5120, 512),
 ]
 
