@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libdflash.so")
 
-SOURCES = ["gemm.hip", "attn.hip", "misc.hip", "gdn.hip", "sample.hip", "api.hip"]
+SOURCES = ["gemm.hip", "gemm_dense.hip", "attn.hip", "misc.hip", "gdn.hip", "sample.hip", "api.hip"]
 # fp32 operation order of the GatedDeltaNet replay is pinned: no contraction
 EXTRA = {"gdn.hip": ["-ffp-contract=off"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

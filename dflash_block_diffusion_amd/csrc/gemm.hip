@@ -48,6 +48,7 @@
 #include <tuple>
 
 #include "common.h"
+#include "gemm_dev.h"
 
 namespace dfl {
 
@@ -159,57 +160,7 @@ hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, cons
   return hipGetLastError();
 }
 
-// --------------------------------------------------------------- dequant
-__device__ __forceinline__ half2v h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
-
-// (a & m) | c in one VALU op (the compiler splits it into two)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-  return r;
-}
-
-// 8 int4 codes (one dword, offset binary, nibble slots as packed) -> 8 halves
-// 0x6400 | u is the fp16 value 1024 + u; (0x6400 | 16u) scaled by 1/16 is 64 + u.
-// mlo = 0x000F000F, mhi = 0x00F000F0, magic = 0x64006400 (register operands).
-__device__ __forceinline__ half8 deq_w4(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic) {
-  const half2v c0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2v s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2v c1 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t w2 = w >> 8;
-  half2v a = h2(and_or(w, mlo, magic)) + c0;
-  half2v b = h2(and_or(w, mhi, magic)) * s16 + c1;
-  half2v c = h2(and_or(w2, mlo, magic)) + c0;
-  half2v d = h2(and_or(w2, mhi, magic)) * s16 + c1;
-  half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  return r;
-}
-
-// 8 int8 codes (two dwords, bytes in column order, offset binary) -> 8 halves:
-// byte pairs are spread to the low bytes of two fp16 lanes over the magic 0x64.
-__device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi, uint32_t magic) {
-  const half2v c = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  half2v a = h2(__builtin_amdgcn_perm(magic, lo, 0x05010500u)) + c;
-  half2v b = h2(__builtin_amdgcn_perm(magic, lo, 0x05030502u)) + c;
-  half2v d = h2(__builtin_amdgcn_perm(magic, hi, 0x05010500u)) + c;
-  half2v e = h2(__builtin_amdgcn_perm(magic, hi, 0x05030502u)) + c;
-  half8 r = {a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
-  return r;
-}
-
 // ------------------------------------------------------------------ kernel
-struct GemmArgs {
-  const uint8_t* w; const uint16_t* s; const uint16_t* x;
-  int n, k, ktiles, ntile16, m, splits, align;
-  int epi;
-  float* part;                               // EPI_PARTIAL: [splits][m][n] fp32
-  void* out; int otype;                      // EPI_SILU: tiled [m][n/2] (K = n/2)
-  float* logits; int ldl; int row0;          // EPI_ARGMAX
-  float* am_val; int* am_idx;                // EPI_ARGMAX: one (value, index) per work-group and token
-  // dequant bit masks, passed as arguments so that they live in registers
-  // (gfx9 VOP3 encodings take no literal constants)
-  uint32_t mlo, mhi, magic;
-};
 
 // registers of one ring stage (one K tile of all RT row tiles + its
 // activation fragments) and the ring depth that fits ~140 VGPRs
@@ -781,308 +732,6 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
   else e = dispatch<W_W4>(p, a, s);
   if (e != hipSuccess || c.epi != EPI_ARGMAX) return e;
   return launch_argmax_final(w.am_val, w.am_idx, p.nwg, c.row0, c.m - c.row0, c.am_out, s);
-}
-
-// ------------------------------------------------------- dense (prompt chunks)
-// W4 / W8 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
-// that the MFMAs, not the weight stream, set the time, so activations are
-// reused across many weight rows instead of being re-read per row tile.
-// Work-group = MT token blocks (MT = 4 or 8: 64 or 128 rows) x 16 row tiles
-// (256 weight rows) x one of S K ranges; wave w owns row tiles 4w..4w+3 for
-// all MT token blocks.  Per K tile (128 columns) the work-group stages the
-// 4*MT activation fragments (MT blocks x 4 MFMA steps, 1 KiB each) in LDS by
-// direct global->LDS loads while
-// each wave holds its four weight tiles and their group scales in registers;
-// both are double-buffered, so tile t+1 loads while tile t is multiplied.
-// At most 256 registers a lane, so that two waves share each SIMD and one's
-// MFMAs overlap the other's dequantisation and group-scale FMAs.  The arithmetic is the
-// stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
-// scaled by the group's fp16 scale and accumulated in fp32 (W8: one fp32
-// sum per row, times the row's fp16 scale at the end).
-// MT = 8 halves the dequantisation and the weight loads per MFMA (each
-// weight tile serves 128 rows) but needs 128 accumulators per lane and halves
-// the grid; it is taken for the large int4 shapes of long chunks (measured on
-// the 8B-class prompt pass: gate/up 11 % and down 5 % faster at 1024 rows,
-// QKV and O no faster).
-
-// The pipeline's register loads go the same way (weights non-temporal): the
-// explicit per-tile wait is then the only one, and every register they write
-// is read only after it (the waits are scheduling barriers).
-__device__ __forceinline__ uint4 gload16_nt(const void* p) {
-  uint4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ uint32_t gload4(const void* p) {
-  uint32_t r;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-constexpr int DENSE_RW = 4;                  // row tiles per wave
-constexpr int DENSE_MAX_ROWS = 1024;
-
-// FMT W4: per 128-column step one 1 KiB tile and one scale dword per row
-// tile; W8: two 64-column tiles per row tile and the per-row scale applied to
-// the finished sum (as the stream kernel does).
-template <int FMT, int EPI, int DENSE_MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
-                                                                                       int kt_per) {
-  static_assert(FMT == W_W4 || FMT == W_W8, "dense kernel: int4 or int8 weights");
-  static_assert(DENSE_MT == 4 || (DENSE_MT == 8 && FMT == W_W4), "dense kernel: 4 token blocks, or 8 for int4");
-  constexpr int WT = FMT == W_W4 ? 1 : 2;     // weight tiles per row tile and 128-column step
-  __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, g = lane >> 4;
-  const int nblk = (a.m + 15) >> 4;
-  // Work-groups are dealt to the 8 XCDs round-robin by index.  When the
-  // row-tile groups come in multiples of 8, XCD x takes row-tile groups
-  // x, x + 8, ... and runs all token groups of one before the next, so the
-  // weights a group reads stay in that XCD's L2 for all of its token groups.
-  const int ngx = (a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW), ngy = (nblk + DENSE_MT - 1) / DENSE_MT;
-  const int id = blockIdx.x;
-  int gx, gy;
-  if (ngx % 8 == 0) {
-    gx = (id / (8 * ngy)) * 8 + id % 8;
-    gy = (id / 8) % ngy;
-  } else {
-    gx = id % ngx;
-    gy = id / ngx;
-  }
-  const int tb0 = gy * DENSE_MT;
-  const int rt0 = gx * (4 * DENSE_RW) + wave * DENSE_RW;
-  const int sidx = blockIdx.z;
-  const int ptiles = a.k >> 7;               // 128-column steps
-  const int kt0 = sidx * kt_per, kt1 = min(ptiles, kt0 + kt_per);
-  const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
-  const size_t xfrag = (size_t)(a.k >> 5);
-  uint32_t rtile[DENSE_RW];                  // row tiles past the end re-read the last one
-#pragma unroll
-  for (int i = 0; i < DENSE_RW; ++i) rtile[i] = (uint32_t)min(rt0 + i, a.ntile16 - 1);
-
-  floatx4 acc[DENSE_MT][DENSE_RW];
-#pragma unroll
-  for (int tb = 0; tb < DENSE_MT; ++tb)
-#pragma unroll
-    for (int i = 0; i < DENSE_RW; ++i) acc[tb][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // this wave's DENSE_MT of the K tile's 4*DENSE_MT activation fragments:
-  // fragment f = DENSE_MT*w + j is token block f/4 (blocks past the chunk
-  // re-read its last one), MFMA step f%4
-  auto stage = [&](int t, uint8_t* xs) {
-#pragma unroll
-    for (int j = 0; j < DENSE_MT; ++j) {
-      const int f = DENSE_MT * wave + j, tb = min(tb0 + (f >> 2), nblk - 1);
-      const uint16_t* src = a.x + ((size_t)tb * xfrag + (size_t)t * 4 + (f & 3)) * 512 + lane * 8;
-      lds_dma16(src, (uint32_t)(uintptr_t)(lds_ptr)(xs + f * 1024));
-    }
-  };
-  // 2*DENSE_RW loads per step either way: W4 a tile and a scale dword, W8
-  // two tiles, per row tile
-  auto wload = [&](int t, uint4 (&w)[DENSE_RW][WT], uint32_t (&sc)[DENSE_RW]) {
-#pragma unroll
-    for (int i = 0; i < DENSE_RW; ++i) {
-      const size_t tile = (size_t)rtile[i] * a.ktiles + (size_t)t * WT;
-      w[i][0] = gload16_nt(a.w + tile * 1024 + lane * 16);
-      if (FMT == W_W4) sc[i] = gload4(a.s + tile * 32 + lr * 2);
-      else w[i][WT - 1] = gload16_nt(a.w + (tile + 1) * 1024 + lane * 16);
-    }
-  };
-  // Per 64-wide group: its two weight steps dequantised for the 4 row tiles,
-  // its two activation steps of the 4 token blocks read from LDS, then for
-  // each half of the token blocks 8 independent MFMA chains (2 MFMAs each)
-  // before their sums are scaled into the accumulators, so no MFMA waits on
-  // the one before it and no FMA on an MFMA just issued.
-  auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW][WT], const uint32_t (&sc)[DENSE_RW]) {
-    if (FMT == W_W8) {
-      // 4 MFMA steps straight into the accumulators; step ks is dwords
-      // 2(ks%2), 2(ks%2)+1 of tile ks/2
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8 b[DENSE_RW];
-#pragma unroll
-        for (int i = 0; i < DENSE_RW; ++i) {
-          const uint4 wt = w[i][(ks >> 1) & (WT - 1)];
-          b[i] = (ks & 1) ? deq_w8(wt.z, wt.w, magic) : deq_w8(wt.x, wt.y, magic);
-        }
-#pragma unroll
-        for (int tb = 0; tb < DENSE_MT; ++tb) {
-          const half8 x = __builtin_bit_cast(half8, *(const uint4*)(xs + (tb * 4 + ks) * 1024 + lane * 16));
-#pragma unroll
-          for (int i = 0; i < DENSE_RW; ++i)
-            acc[tb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, b[i], acc[tb][i], 0, 0, 0);
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      half8 b[DENSE_RW][2];
-      float sg[DENSE_RW];
-#pragma unroll
-      for (int i = 0; i < DENSE_RW; ++i) {
-        const uint32_t wd0 = gg ? w[i][0].z : w[i][0].x, wd1 = gg ? w[i][0].w : w[i][0].y;
-        b[i][0] = deq_w4(wd0, mlo, mhi, magic);
-        b[i][1] = deq_w4(wd1, mlo, mhi, magic);
-        sg[i] = (float)h2(sc[i])[gg];
-      }
-#pragma unroll
-      for (int hb = 0; hb < DENSE_MT; hb += 2) {
-        half8 x[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            x[j][h] = __builtin_bit_cast(half8, *(const uint4*)(xs + ((hb + j) * 4 + 2 * gg + h) * 1024 + lane * 16));
-        floatx4 tmp[2][DENSE_RW];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < DENSE_RW; ++i)
-            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[j][0], b[i][0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < DENSE_RW; ++i)
-            tmp[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[j][1], b[i][1], tmp[j][i], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < DENSE_RW; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[hb + j][i][v] += sg[i] * tmp[j][i][v];
-      }
-    }
-  };
-  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs, 4
-  // weight and 4 scale loads, the youngest) stay in flight; past the last
-  // tile the loads re-read it, so the wait is always the same.  It is kept
-  // apart from the first use so that the compiler adds none there.
-  auto wait_tile = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + 2 * DENSE_RW));
-    asm volatile("s_nop 0");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
-  };
-  uint4 w0[DENSE_RW][WT], w1[DENSE_RW][WT];
-  uint32_t s0[DENSE_RW], s1[DENSE_RW];
-  // tile t from stage (xs, w, sc); tile t + 1 goes to stage (xn, wn, sn), the
-  // one tile t - 1 used: the barrier first lets every wave finish with it
-  auto step = [&](int t, const uint8_t* xs, const uint4 (&w)[DENSE_RW][WT], const uint32_t (&sc)[DENSE_RW],
-                  uint8_t* xn, uint4 (&wn)[DENSE_RW][WT], uint32_t (&sn)[DENSE_RW]) {
-    __builtin_amdgcn_s_barrier();
-    const int tn = min(t + 1, kt1 - 1);
-    stage(tn, xn);
-    wload(tn, wn, sn);
-    wait_tile();
-    compute(xs, w, sc);
-  };
-  if (kt0 < kt1) {
-    stage(kt0, xs0);
-    wload(kt0, w0, s0);
-    for (int t = kt0; t < kt1; t += 2) {
-      step(t, xs0, w0, s0, xs1, w1, s1);
-      if (t + 1 >= kt1) break;
-      step(t + 1, xs1, w1, s1, xs0, w0, s0);
-    }
-    // the last loads re-read a tile nobody uses: let them land before the
-    // work-group (and its LDS) ends
-    __builtin_amdgcn_s_waitcnt(vm_wait(0));
-  }
-
-  // lane (lr, g) holds weight row (rt0 + i)*16 + lr for tokens
-  // (tb0 + tb)*16 + 4g + v
-  // W8: the row's fp16 scale on the finished sum; W4 sums are scaled already
-  auto scale_of = [&](int n) -> float {
-    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, a.s[n]) : 1.0f;
-  };
-  if (EPI == EPI_PARTIAL) {
-    float* part = a.part + (size_t)sidx * a.m * a.n;
-#pragma unroll
-    for (int i = 0; i < DENSE_RW; ++i) {
-      if (rt0 + i >= a.ntile16) continue;
-      const int n = (rt0 + i) * 16 + lr;
-      const float sc = scale_of(n);
-#pragma unroll
-      for (int tb = 0; tb < DENSE_MT; ++tb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = (tb0 + tb) * 16 + 4 * g + v;
-          if (t < a.m) part[(size_t)t * a.n + n] = acc[tb][i][v] * sc;
-        }
-    }
-  } else {  // EPI_SILU: row tiles (2p, 2p+1) are a (gate, up) pair
-    const int rnd = a.otype == T_F32 ? T_F32 : T_BF16;
-    const int half_n = a.n >> 1;
-#pragma unroll
-    for (int p = 0; p < DENSE_RW / 2; ++p) {
-      if (rt0 + 2 * p + 1 >= a.ntile16) continue;
-      const int n_out = ((rt0 >> 1) + p) * 16 + lr;
-      const int ng = (rt0 + 2 * p) * 16 + lr;
-      const float sg = scale_of(ng), su = scale_of(ng + 16);
-#pragma unroll
-      for (int tb = 0; tb < DENSE_MT; ++tb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = (tb0 + tb) * 16 + 4 * g + v;
-          if (t >= a.m) continue;
-          const float gv = act_round(rnd, acc[tb][2 * p][v] * sg);
-          const float uv = act_round(rnd, acc[tb][2 * p + 1][v] * su);
-          const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
-          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
-        }
-    }
-  }
-}
-
-// token blocks per work-group: 8 for int4 chunks of more than 512 rows with
-// a wide N (gate/up) or a deep K (down), else 4
-static int dense_mt(int fmt, int n, int k, int m) {
-  return fmt == W_W4 && m > 512 && (n >= 16384 || k >= 8192) ? 8 : 4;
-}
-
-// K splits of a dense launch: partial sums go to S slices so that the grid
-// reaches the chip's 256 CUs, each split keeping at least 4 K tiles
-int dense_splits(int fmt, int n, int k, int m, int epi) {
-  if (epi != EPI_PARTIAL) return 1;
-  const int ktiles = k / 128, mt = dense_mt(fmt, n, k, m);
-  const int base = ((n / 16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((m / 16 + mt - 1) / mt);
-  int S = 1;
-  while (S < MAX_SPLITS && base * S < 256 && ktiles / (2 * S) >= 4) S *= 2;
-  return S;
-}
-
-bool dense_ok(int fmt, int n, int k, int m, int epi) {
-  return (fmt == W_W4 || fmt == W_W8) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
-         (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
-}
-
-static hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t s, int* splits) {
-  const GemmW& W = *c.W;
-  if (!dense_ok(W.fmt, W.n, W.k, c.m, c.epi)) return hipErrorInvalidValue;
-  const int S = dense_splits(W.fmt, W.n, W.k, c.m, c.epi), mt = dense_mt(W.fmt, W.n, W.k, c.m);
-  if (c.epi == EPI_PARTIAL && (size_t)S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
-  GemmArgs a{};
-  a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
-  a.n = W.n; a.k = W.k; a.ktiles = W.k / tile_k(W.fmt); a.ntile16 = W.n / 16; a.m = c.m; a.splits = S; a.align = 1;
-  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
-  a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
-  const int kt_per = (W.k / 128 + S - 1) / S;
-  const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + mt - 1) / mt), 1, S);
-  if (W.fmt == W_W4 && mt == 8) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 8>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 8>), grid, dim3(256), 0, s, a, kt_per);
-  } else if (W.fmt == W_W4) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  } else {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  }
-  if (splits) *splits = S;
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
