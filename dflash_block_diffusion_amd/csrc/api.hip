@@ -120,7 +120,7 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   int rc = check_gemm_shape(fmt, n, k, 0);
   if (rc) return rc;
   if (!linear_rows_ok(fmt, n, k, m, epilogue))
-    return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, W4A16/W8A16 with epilogue 0, a multiple of 16 up to 1024)");
+    return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, BF16/W8A16/W4A16 with epilogue 0, a multiple of 16 up to 1024)");
   if (fmt == DFLASH_FMT_F32 && ldx < k) return fail(DFLASH_E_SHAPE, "ldx must be >= k");
   if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
   if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");
@@ -427,10 +427,12 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   s->capacity = s->pages * PAGE;
   s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
   if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
-  // dense prompt chunks: an int4 target of attention layers (the projections
-  // have the dense kernel; GatedDeltaNet layers take B tokens at a time)
+  // dense prompt chunks: an int4 or bf16 target of attention layers (the
+  // projections have the dense kernel; GatedDeltaNet layers take B tokens at
+  // a time)
   s->pm = 0;
-  if (t->d.fmt == DFLASH_FMT_W4A16 && t->n_gdn == 0 && t->act == T_BF16 && max_ctx > 2 * block) {
+  if ((t->d.fmt == DFLASH_FMT_W4A16 || t->d.fmt == DFLASH_FMT_BF16) && t->n_gdn == 0 && t->act == T_BF16 &&
+      max_ctx > 2 * block) {
     bool ok = true;
     for (const Layer& L : t->layers)
       ok = ok && dense_ok(L.qkv.fmt, L.qkv.n, L.qkv.k, DENSE_PROMPT_ROWS, EPI_PARTIAL) &&

@@ -764,8 +764,9 @@ hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, con
   }
   if (c.m > MAX_ROWS) {
     if (variant)
-      *variant = W.fmt == W_W4 ? (c.epi == EPI_SILU ? "gemm_dense_w4_silu" : "gemm_dense_w4")
-                               : (c.epi == EPI_SILU ? "gemm_dense_w8_silu" : "gemm_dense_w8");
+      *variant = W.fmt == W_W4   ? (c.epi == EPI_SILU ? "gemm_dense_w4_silu" : "gemm_dense_w4")
+                 : W.fmt == W_W8 ? (c.epi == EPI_SILU ? "gemm_dense_w8_silu" : "gemm_dense_w8")
+                                 : (c.epi == EPI_SILU ? "gemm_dense_bf16_silu" : "gemm_dense_bf16");
     return launch_gemm_dense(c, w, s, splits);
   }
   const Plan p = make_plan(W.fmt, W.n, W.k, c.m, c.epi);

@@ -1,5 +1,5 @@
-// Dense dequant-GEMM for prompt chunks (64 < m <= 1024 token rows): the
-// same packed int4 / int8 weights and tiled activations as the skinny GEMM,
+// Dense GEMM for prompt chunks (64 < m <= 1024 token rows): the same packed
+// int4 / int8 / bf16 weights and tiled activations as the skinny GEMM,
 // arranged so that MFMAs rather than the weight stream set the time.
 #include <hip/hip_runtime.h>
 
@@ -11,21 +11,22 @@
 namespace dfl {
 
 // ------------------------------------------------------- dense (prompt chunks)
-// W4 / W8 dequant-GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
+// W4 / W8 / BF16 GEMM for prompt chunks of m = 16*j rows (j <= 64): enough rows
 // that the MFMAs, not the weight stream, set the time, so activations are
 // reused across many weight rows instead of being re-read per row tile.
 // Work-group = MT token blocks (MT = 4 or 8: 64 or 128 rows) x 16 row tiles
 // (256 weight rows) x one of S K ranges; wave w owns row tiles 4w..4w+3 for
 // all MT token blocks.  Per K tile (128 columns) the work-group stages the
 // 4*MT activation fragments (MT blocks x 4 MFMA steps, 1 KiB each) in LDS by
-// direct global->LDS loads while
-// each wave holds its four weight tiles and their group scales in registers;
-// both are double-buffered, so tile t+1 loads while tile t is multiplied.
-// At most 256 registers a lane, so that two waves share each SIMD and one's
-// MFMAs overlap the other's dequantisation and group-scale FMAs.  The arithmetic is the
-// stream kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
+// direct global->LDS loads while each wave holds its four row tiles' weights
+// (and group scales) in registers; both are double-buffered, so tile t+1
+// loads while tile t is multiplied.  At most 256 registers a lane, so that
+// two waves share each SIMD and one's MFMAs overlap the other's
+// dequantisation and group-scale FMAs.  The arithmetic is the stream
+// kernel's: fp16 MFMA on the raw codes, one fp32 sum per 64-wide group,
 // scaled by the group's fp16 scale and accumulated in fp32 (W8: one fp32
-// sum per row, times the row's fp16 scale at the end).
+// sum per row, times the row's fp16 scale at the end; BF16: bf16 MFMA on
+// the stored weights, fp32 sums).
 // MT = 8 halves the dequantisation and the weight loads per MFMA (each
 // weight tile serves 128 rows) but needs 128 accumulators per lane and halves
 // the grid; it is taken for the large int4 shapes of long chunks (measured on
@@ -50,13 +51,15 @@ constexpr int DENSE_MAX_ROWS = 1024;
 
 // FMT W4: per 128-column step one 1 KiB tile and one scale dword per row
 // tile; W8: two 64-column tiles per row tile and the per-row scale applied to
-// the finished sum (as the stream kernel does).
+// the finished sum (as the stream kernel does); BF16: four 32-column tiles
+// per row tile, MFMA bf16 on the weights as stored (bf16 activations).
 template <int FMT, int EPI, int DENSE_MT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
                                                                                        int kt_per) {
-  static_assert(FMT == W_W4 || FMT == W_W8, "dense kernel: int4 or int8 weights");
+  static_assert(FMT == W_W4 || FMT == W_W8 || FMT == W_BF16, "dense kernel: int4, int8 or bf16 weights");
   static_assert(DENSE_MT == 4 || (DENSE_MT == 8 && FMT == W_W4), "dense kernel: 4 token blocks, or 8 for int4");
-  constexpr int WT = FMT == W_W4 ? 1 : 2;     // weight tiles per row tile and 128-column step
+  constexpr int WT = FMT == W_W4 ? 1 : (FMT == W_W8 ? 2 : 4);  // weight tiles per row tile and 128-column step
+  constexpr int WLOADS = FMT == W_BF16 ? 4 * DENSE_RW : 2 * DENSE_RW;  // register loads per step
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t xs1[DENSE_MT * 4 * 1024];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -105,15 +108,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       lds_dma16(src, (uint32_t)(uintptr_t)(lds_ptr)(xs + f * 1024));
     }
   };
-  // 2*DENSE_RW loads per step either way: W4 a tile and a scale dword, W8
-  // two tiles, per row tile
+  // WLOADS per step: per row tile W4 a tile and a scale dword, W8 two
+  // tiles, BF16 four tiles
   auto wload = [&](int t, uint4 (&w)[DENSE_RW][WT], uint32_t (&sc)[DENSE_RW]) {
 #pragma unroll
     for (int i = 0; i < DENSE_RW; ++i) {
       const size_t tile = (size_t)rtile[i] * a.ktiles + (size_t)t * WT;
-      w[i][0] = gload16_nt(a.w + tile * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < WT; ++j) w[i][j] = gload16_nt(a.w + (tile + j) * 1024 + lane * 16);
       if (FMT == W_W4) sc[i] = gload4(a.s + tile * 32 + lr * 2);
-      else w[i][WT - 1] = gload16_nt(a.w + (tile + 1) * 1024 + lane * 16);
     }
   };
   // Per 64-wide group: its two weight steps dequantised for the 4 row tiles,
@@ -122,6 +125,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // before their sums are scaled into the accumulators, so no MFMA waits on
   // the one before it and no FMA on an MFMA just issued.
   auto compute = [&](const uint8_t* xs, const uint4 (&w)[DENSE_RW][WT], const uint32_t (&sc)[DENSE_RW]) {
+    if (FMT == W_BF16) {
+      // step ks is tile ks of each row tile, an MFMA operand as stored
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < DENSE_MT; ++tb) {
+          const bf16x8 x = __builtin_bit_cast(bf16x8, *(const uint4*)(xs + (tb * 4 + ks) * 1024 + lane * 16));
+#pragma unroll
+          for (int i = 0; i < DENSE_RW; ++i)
+            acc[tb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, __builtin_bit_cast(bf16x8, w[i][ks & (WT - 1)]),
+                                                                 acc[tb][i], 0, 0, 0);
+        }
+      return;
+    }
     if (FMT == W_W8) {
       // 4 MFMA steps straight into the accumulators; step ks is dwords
       // 2(ks%2), 2(ks%2)+1 of tile ks/2
@@ -182,13 +199,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
     }
   };
-  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs, 4
-  // weight and 4 scale loads, the youngest) stay in flight; past the last
+  // Every tile's wait lets the next tile's loads (DENSE_MT fragment DMAs and
+  // WLOADS register loads, the youngest) stay in flight; past the last
   // tile the loads re-read it, so the wait is always the same.  It is kept
   // apart from the first use so that the compiler adds none there.
   auto wait_tile = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + 2 * DENSE_RW));
+    __builtin_amdgcn_s_waitcnt(vm_wait(DENSE_MT + WLOADS));
     asm volatile("s_nop 0");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();            // every wave's fragments of the tile are in LDS
@@ -282,7 +299,7 @@ int dense_splits(int fmt, int n, int k, int m, int epi) {
 }
 
 bool dense_ok(int fmt, int n, int k, int m, int epi) {
-  return (fmt == W_W4 || fmt == W_W8) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
+  return (fmt == W_W4 || fmt == W_W8 || fmt == W_BF16) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
          (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
 }
 
@@ -304,9 +321,12 @@ hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t 
   } else if (W.fmt == W_W4) {
     if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
     else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  } else {
+  } else if (W.fmt == W_W8) {
     if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
     else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
+  } else {
+    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_BF16, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
+    else hipLaunchKernelGGL((gemm_dense_kernel<W_BF16, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
   }
   if (splits) *splits = S;
   return hipGetLastError();

@@ -107,12 +107,13 @@ int dflash_pack_weight(int fmt, int n, int k, int gate_up, const void *d_src_cod
  *   d_ws     device workspace of dflash_linear_workspace_bytes(fmt,n,k,m)
  *            bytes, zero-filled once before first use (every call leaves its
  *            counters zero again).
- *   Prompt chunks: W4A16 and W8A16 (K % 128 == 0) with epilogue 0 also take
- *            m = 80, 96, ..., 1024 (multiples of 16 above 64).  These run the
- *            dense kernel prefill uses (activations staged in LDS and reused
- *            across 256 weight rows; same exact dequantisation: fp16 MFMA on
- *            the raw codes, one fp32 sum per 64-wide group times its scale for
- *            W4, the row scale on the finished sum for W8).
+ *   Prompt chunks: BF16, W8A16 and W4A16 (K % 128 == 0) with epilogue 0
+ *            also take m = 80, 96, ..., 1024 (multiples of 16 above 64).
+ *            These run the dense kernel prefill uses (activations staged in
+ *            LDS and reused across 256 weight rows; same exact
+ *            dequantisation: fp16 MFMA on the raw codes, one fp32 sum per
+ *            64-wide group times its scale for W4, the row scale on the
+ *            finished sum for W8; bf16 MFMA on the stored weights for BF16).
  * Errors: SHAPE for unsupported dims, INVALID for null pointers or an
  * undersized workspace. */
 size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m);
@@ -185,10 +186,10 @@ int dflash_state_init(dflash_state **out, const dflash_model *target,
 void dflash_state_destroy(dflash_state *st);
 
 /* Prefill P prompt tokens (target forward in chunks of B, causal; the
- * drafter's context rows for all P positions).  An int4 target of attention
- * layers runs the prompt up to its last whole block in chunks of up to 1024
- * rows (dense int4 GEMMs, one-pass causal attention), then the rest as one
- * block; other targets run every chunk as a block.  Writes the first generated
+ * drafter's context rows for all P positions).  An int4 or bf16 target of
+ * attention layers runs the prompt up to its last whole block in chunks of up
+ * to 1024 rows (dense GEMMs, one-pass causal attention), then the rest as one
+ * block; hybrid targets run every chunk as a block.  Writes the first generated
  * token (argmax of the last prompt row) to d_first_tok[0] and sets n = P.
  * The committed token log holds the prompt then every emitted token.
  * Not graph-capturable (host loop over chunks).  Errors: CAPACITY if

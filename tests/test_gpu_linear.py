@@ -202,6 +202,26 @@ def test_linear_dense_w8_parity(n, k, m):
     assert np.all(np.abs(y - ref) <= bound(x, w))
 
 
+@pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 2560, 1024), (2560, 12800, 96),
+                                   (19456, 2560, 528)])
+def test_linear_dense_bf16_parity(n, k, m):
+    # the bf16 dense path (4B-class targets and drafters): bf16 MFMA on the
+    # stored weights; the last shapes are the 4B drafter fc (sampled rows)
+    # and gate/up
+    g = synth.HostSynth(304)
+    w = g.weight(f"dense16_{n}x{k}", n, k, C.FMT_BF16)
+    x = x_values(np.random.default_rng(n + k + m + 2), m, k, C.FMT_BF16)
+    y, _, _ = run_linear(w, x, C.FMT_BF16)
+    assert np.all(np.isfinite(y))
+    if n * k > 4096 * 4096:
+        for r0 in (0, n // 2, n - 16):
+            ref = linear(x, w, rows=(r0, r0 + 16))
+            assert np.all(np.abs(y[:, r0:r0 + 16] - ref) <= bound(x, w, rows=(r0, r0 + 16)))
+        return
+    ref = linear(x, w)
+    assert np.all(np.abs(y - ref) <= bound(x, w))
+
+
 def test_linear_dense_w4_repeat_is_bitwise():
     g = synth.HostSynth(301)
     w = g.weight("dense_rep", 1024, 4096, C.FMT_W4A16)

@@ -247,6 +247,16 @@ def test_reduced_8b_dense_prompt_chunks_lockstep(P):
 
 
 
+@pytest.mark.parametrize("P", [1100, 530])
+def test_reduced_4b_dense_prompt_chunks_lockstep(P):
+    # bf16 target and drafter: 1100 prompt tokens run chunks of 1024 rows
+    # (the bf16 prompt GEMM, the one-pass prompt attention) and 64 rows (the
+    # block path), then a 12-token block; 530: one 528-row chunk, then 2
+    cfg = reduced("4b")
+    _, _, stats, _ = lockstep(cfg, P, [0, 15, 6])
+    assert stats["compared"] >= 3 * cfg.block
+
+
 def test_rollback_replays_identically():
     cfg = reduced("8b")
     ck = synth.make_pair(cfg)
