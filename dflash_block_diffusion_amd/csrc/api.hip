@@ -427,12 +427,11 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   s->capacity = s->pages * PAGE;
   s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
   if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
-  // dense prompt chunks: an int4 or bf16 target of attention layers (the
-  // projections have the dense kernel; GatedDeltaNet layers take B tokens at
-  // a time)
+  // dense prompt chunks: an int4 or bf16 target (the projections have the
+  // dense kernel; GatedDeltaNet layers run the chunk's recurrence B tokens
+  // at a time)
   s->pm = 0;
-  if ((t->d.fmt == DFLASH_FMT_W4A16 || t->d.fmt == DFLASH_FMT_BF16) && t->n_gdn == 0 && t->act == T_BF16 &&
-      max_ctx > 2 * block) {
+  if ((t->d.fmt == DFLASH_FMT_W4A16 || t->d.fmt == DFLASH_FMT_BF16) && t->act == T_BF16 && max_ctx > 2 * block) {
     bool ok = true;
     for (const Layer& L : t->layers)
       ok = ok && dense_ok(L.qkv.fmt, L.qkv.n, L.qkv.k, DENSE_PROMPT_ROWS, EPI_PARTIAL) &&
@@ -693,7 +692,24 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       gc.S = s->gdn_S + (size_t)g * gh * dvv * dkk;
       gc.tape = s->gdn_tape + (size_t)g * s->B * gh * gdn_rec(t);   // tape rows are laid out per B
       gc.out = s->ba; gc.otype = t->gin; gc.ldo = gh * dvv;
-      HIPCHK(launch_gdn_verify(gc, st));
+      if (B <= s->B) {
+        HIPCHK(launch_gdn_verify(gc, st));
+      } else {
+        // a prompt chunk (whole blocks, all committed): block after block,
+        // the block-path verify from the layer's state, then the pinned
+        // replay of all of the block's tokens into it, so that the state and
+        // outputs are the ones B-row prefill chunks give; the chunk's commit
+        // then skips the replay
+        for (int r0 = 0; r0 < B; r0 += s->B) {
+          GdnCall gj = gc;
+          gj.rows = s->B;
+          gj.proj.p = gc.proj.p + (size_t)r0 * gc.proj.ld;
+          gj.out = (char*)s->ba + (size_t)r0 * gc.ldo * elem_bytes(t->gin);
+          HIPCHK(launch_gdn_verify(gj, st));
+          HIPCHK(launch_gdn_replay(const_cast<float*>(gj.S), gj.tape, 1, s->B, gh, dkk, dvv, nullptr, s->B, s->scal,
+                                   s->capacity, st));
+        }
+      }
       RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_PARTIAL, st, &pend.in));
       ++g;
     }
@@ -723,9 +739,12 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
   return DFLASH_OK;
 }
 
-static int do_commit(dflash_state* s, const int32_t* d_acc, int host_count, const int32_t* emit, hipStream_t st) {
+// gdn_done: the GatedDeltaNet states already hold the committed tokens (a
+// prompt chunk replays them block by block in its forward pass)
+static int do_commit(dflash_state* s, const int32_t* d_acc, int host_count, const int32_t* emit, hipStream_t st,
+                     bool gdn_done = false) {
   const dflash_model* t = s->t;
-  if (t->n_gdn)
+  if (t->n_gdn && !gdn_done)
     HIPCHK(launch_gdn_replay(s->gdn_S, s->gdn_tape, t->n_gdn, s->B, t->d.gdn_heads, t->d.gdn_dk, t->d.gdn_dv,
                              d_acc, host_count, s->scal, s->capacity, st));
   HIPCHK(launch_commit(s->scal, d_acc, host_count, emit, s->tokens, s->acc_log, s->acc_log_len, s->capacity,
@@ -756,12 +775,13 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
     while (c0 < dense_end) {
       const int rows = std::min(s->pm, dense_end - c0);
       RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, rows, st, false));
+      const bool gdn_done = rows > s->B;
       if (s->pm_draft) {
-        RC(do_commit(s, nullptr, rows, nullptr, st));
+        RC(do_commit(s, nullptr, rows, nullptr, st, gdn_done));
         RC(draft_context_kv(s, st, 0, rows));
       } else {
         for (int j = 0; j < rows; j += s->B) {
-          RC(do_commit(s, nullptr, s->B, nullptr, st));
+          RC(do_commit(s, nullptr, s->B, nullptr, st, gdn_done));
           RC(draft_context_kv(s, st, j));
         }
       }

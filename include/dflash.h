@@ -186,10 +186,11 @@ int dflash_state_init(dflash_state **out, const dflash_model *target,
 void dflash_state_destroy(dflash_state *st);
 
 /* Prefill P prompt tokens (target forward in chunks of B, causal; the
- * drafter's context rows for all P positions).  An int4 or bf16 target of
- * attention layers runs the prompt up to its last whole block in chunks of up
- * to 1024 rows (dense GEMMs, one-pass causal attention), then the rest as one
- * block; hybrid targets run every chunk as a block.  Writes the first generated
+ * drafter's context rows for all P positions).  An int4 or bf16 target runs
+ * the prompt up to its last whole block in chunks of up to 1024 rows (dense
+ * GEMMs, one-pass causal attention, GatedDeltaNet layers B tokens at a time),
+ * then the rest as one block; an fp32 target runs every chunk as a block.
+ * Writes the first generated
  * token (argmax of the last prompt row) to d_first_tok[0] and sets n = P.
  * The committed token log holds the prompt then every emitted token.
  * Not graph-capturable (host loop over chunks).  Errors: CAPACITY if

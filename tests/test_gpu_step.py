@@ -294,8 +294,19 @@ def test_hybrid_gdn_replay_bitexact_vs_scratch_recompute():
 
 
 def test_hybrid_long_prompt_and_snapshot_rollback():
+    # 100 prompt tokens: one 96-row dense chunk (the GatedDeltaNet layers run
+    # its six blocks in turn), then a 4-token block
     cfg = reduced("hybrid", layers=4)
     lockstep(cfg, 100, [3, 15, 0])
+
+
+def test_hybrid_dense_prompt_chunks_lockstep():
+    # 1100 prompt tokens: chunks of 1024 rows (64 GatedDeltaNet blocks in
+    # turn, the bf16 prompt GEMM, the one-pass prompt attention) and 64 rows,
+    # then a 12-token block
+    cfg = reduced("hybrid", layers=4)
+    _, _, stats, _ = lockstep(cfg, 1100, [0, 15, 6])
+    assert stats["compared"] >= 3 * cfg.block
 
 
 def test_tiny_hybrid_lockstep():
