@@ -700,15 +700,7 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
         // replay of all of the block's tokens into it, so that the state and
         // outputs are the ones B-row prefill chunks give; the chunk's commit
         // then skips the replay
-        for (int r0 = 0; r0 < B; r0 += s->B) {
-          GdnCall gj = gc;
-          gj.rows = s->B;
-          gj.proj.p = gc.proj.p + (size_t)r0 * gc.proj.ld;
-          gj.out = (char*)s->ba + (size_t)r0 * gc.ldo * elem_bytes(t->gin);
-          HIPCHK(launch_gdn_verify(gj, st));
-          HIPCHK(launch_gdn_replay(const_cast<float*>(gj.S), gj.tape, 1, s->B, gh, dkk, dvv, nullptr, s->B, s->scal,
-                                   s->capacity, st));
-        }
+        HIPCHK(launch_gdn_prompt(gc, s->B, st));
       }
       RC(gemm(s, L.o, s->ba, gh * dvv, B, EPI_PARTIAL, st, &pend.in));
       ++g;

@@ -270,6 +270,9 @@ struct GdnCall {
   void* out; int otype; int ldo;             // o [B][gh*dv]
 };
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s);
+// a prompt chunk of c.rows = nblk * B committed tokens: verify and replay
+// block by block into c.S (updated in place); no tape
+hipError_t launch_gdn_prompt(const GdnCall& c, int B, hipStream_t s);
 // replays cnt = a+1 (or host_count) tape tokens into every GDN layer's state;
 // skipped when the matching commit will be refused for capacity
 hipError_t launch_gdn_replay(float* S_all, const float* tape_all, int n_layers, int B, int gh, int dk,

@@ -64,20 +64,28 @@ __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_l
 // The committed state is only read; the tape records (k_hat, v, alpha, beta)
 // per token for the commit's pinned replay.  One work-group per head,
 // 4*dv threads; thread (i, r) owns value row i and key columns r + 4m.
+constexpr int GDN_MAXT = 32;
 template <int DK, int DV>
-__global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
+struct GdnSmem {
+  float kq[GDN_MAXT][2 * DK + DV + 2];   // k_hat, q_hat, v, alpha, beta per token
+  float lga[GDN_MAXT];                   // log alpha, then log gamma
+  float KS[GDN_MAXT][DV + 1], QS[GDN_MAXT][DV + 1], U[GDN_MAXT][DV + 1];
+  float Am[GDN_MAXT][GDN_MAXT + 1], Mq[GDN_MAXT][GDN_MAXT + 1];
+};
+
+// The block of T tokens at projection / output rows row0..row0+T-1 against
+// the state S0 held in registers (thread (i, r): S0[i][r + 4m]); writes the
+// block's outputs and, if tape, its tape records.  Leaves the block's
+// k_hat, v, alpha, beta in sm.kq for a replay.
+template <int DK, int DV>
+__device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, const float (&S)[DK / 4], float* tape_base,
+                                             GdnSmem<DK, DV>& sm) {
   constexpr int NT = 4 * DV;
-  constexpr int MAXT = 32;
   constexpr int REC = DK + DV + 2;
-  __shared__ float kq[MAXT][2 * DK + DV + 2];   // k_hat, q_hat, v, alpha, beta per token
-  __shared__ float lga[MAXT];                   // log alpha, then log gamma
-  __shared__ float KS[MAXT][DV + 1], QS[MAXT][DV + 1], U[MAXT][DV + 1];
-  __shared__ float Am[MAXT][MAXT + 1], Mq[MAXT][MAXT + 1];
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid >> 2, r = tid & 3;
   const int gh = c.gh;
-  const int T = c.rows;
   const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
   const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
   const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   // 1. per-token preprocessing, one wave per token: L2 norms, gates, tape
   for (int t = wave; t < T; t += NT / 64) {
     // the projection is materialised in the activation format
-    auto proj = [&](size_t col) { return act_round(c.atype, parts_sum(c.proj, t, (int)col)); };
+    auto proj = [&](size_t col) { return act_round(c.atype, parts_sum(c.proj, row0 + t, (int)col)); };
     float qs = 0.f, ks = 0.f;
     for (int e = lane; e < DK; e += 64) {
       const float qv = proj(qo + e);
@@ -97,53 +105,49 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
     ks = wave_sum(ks);
     const float qn = 1.0f / sqrtf(qs + 1e-6f) * (1.0f / sqrtf((float)DK));
     const float kn = 1.0f / sqrtf(ks + 1e-6f);
-    float* tape = c.tape + ((size_t)t * gh + h) * REC;
+    float* tape = tape_base ? tape_base + ((size_t)t * gh + h) * REC : nullptr;
     for (int e = lane; e < DK; e += 64) {
       const float kh = proj(ko + e) * kn;
-      kq[t][e] = kh;
-      kq[t][DK + e] = proj(qo + e) * qn;
-      tape[e] = kh;
+      sm.kq[t][e] = kh;
+      sm.kq[t][DK + e] = proj(qo + e) * qn;
+      if (tape) tape[e] = kh;
     }
     for (int e = lane; e < DV; e += 64) {
       const float vv = proj(vo + e);
-      kq[t][2 * DK + e] = vv;
-      tape[DK + e] = vv;
+      sm.kq[t][2 * DK + e] = vv;
+      if (tape) tape[DK + e] = vv;
     }
     if (lane == 0) {
       const float av = proj(ao);
       const float bv = proj(bo);
       const float alpha = 1.0f / (1.0f + expf(av));
       const float beta = 1.0f / (1.0f + expf(-bv));
-      kq[t][2 * DK + DV] = alpha;
-      kq[t][2 * DK + DV + 1] = beta;
-      tape[DK + DV] = alpha;
-      tape[DK + DV + 1] = beta;
-      lga[t] = -(fmaxf(av, 0.f) + log1pf(expf(-fabsf(av))));   // log alpha = -softplus(a)
+      sm.kq[t][2 * DK + DV] = alpha;
+      sm.kq[t][2 * DK + DV + 1] = beta;
+      if (tape) {
+        tape[DK + DV] = alpha;
+        tape[DK + DV + 1] = beta;
+      }
+      sm.lga[t] = -(fmaxf(av, 0.f) + log1pf(expf(-fabsf(av))));   // log alpha = -softplus(a)
     }
   }
   __syncthreads();
   if (tid == 0)
-    for (int t = 1; t < T; ++t) lga[t] = lga[t - 1] + lga[t];   // log gamma_t
+    for (int t = 1; t < T; ++t) sm.lga[t] = sm.lga[t - 1] + sm.lga[t];   // log gamma_t
   // 2. KS, QS: row i of S0 against every k_hat_t, q_hat_t (4 lanes per row,
   //    partial dots over columns r + 4m, then the xor-2 / xor-1 exchanges)
-  {
-    float S[DK / 4];
-    const float* Sg = c.S + ((size_t)h * DV + i) * DK;
+  for (int t = 0; t < T; ++t) {
+    float dk_ = 0.f, dq_ = 0.f;
 #pragma unroll
-    for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
-    for (int t = 0; t < T; ++t) {
-      float dk_ = 0.f, dq_ = 0.f;
-#pragma unroll
-      for (int m = 0; m < DK / 4; ++m) {
-        dk_ = dk_ + S[m] * kq[t][r + 4 * m];
-        dq_ = dq_ + S[m] * kq[t][DK + r + 4 * m];
-      }
-      dk_ = dk_ + __shfl_xor(dk_, 2, 64);
-      dk_ = dk_ + __shfl_xor(dk_, 1, 64);
-      dq_ = dq_ + __shfl_xor(dq_, 2, 64);
-      dq_ = dq_ + __shfl_xor(dq_, 1, 64);
-      if (r == 0) { KS[t][i] = dk_; QS[t][i] = dq_; }
+    for (int m = 0; m < DK / 4; ++m) {
+      dk_ = dk_ + S[m] * sm.kq[t][r + 4 * m];
+      dq_ = dq_ + S[m] * sm.kq[t][DK + r + 4 * m];
     }
+    dk_ = dk_ + __shfl_xor(dk_, 2, 64);
+    dk_ = dk_ + __shfl_xor(dk_, 1, 64);
+    dq_ = dq_ + __shfl_xor(dq_, 2, 64);
+    dq_ = dq_ + __shfl_xor(dq_, 1, 64);
+    if (r == 0) { sm.KS[t][i] = dk_; sm.QS[t][i] = dq_; }
   }
   __syncthreads();
   // 3. A and M o QK^T (T x T each)
@@ -151,32 +155,67 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
     const int which = e / (T * T), t = (e / T) % T, s2 = e % T;
     float v = 0.f;
     if (which == 0 ? s2 < t : s2 <= t) {
-      const float* x = which == 0 ? &kq[t][0] : &kq[t][DK];
+      const float* x = which == 0 ? &sm.kq[t][0] : &sm.kq[t][DK];
       float d = 0.f;
-      for (int j = 0; j < DK; ++j) d = d + x[j] * kq[s2][j];
-      const float ratio = expf(lga[t] - lga[s2]);
-      v = which == 0 ? kq[t][2 * DK + DV + 1] * ratio * d : ratio * d;
+      for (int j = 0; j < DK; ++j) d = d + x[j] * sm.kq[s2][j];
+      const float ratio = expf(sm.lga[t] - sm.lga[s2]);
+      v = which == 0 ? sm.kq[t][2 * DK + DV + 1] * ratio * d : ratio * d;
     }
-    if (which == 0) Am[t][s2] = v; else Mq[t][s2] = v;
+    if (which == 0) sm.Am[t][s2] = v; else sm.Mq[t][s2] = v;
   }
   __syncthreads();
   // 4. U by forward substitution, one thread per value column
   if (tid < DV) {
     const int col = tid;
     for (int t = 0; t < T; ++t) {
-      const float beta = kq[t][2 * DK + DV + 1];
-      float u = beta * (kq[t][2 * DK + col] - expf(lga[t]) * KS[t][col]);
-      for (int s2 = 0; s2 < t; ++s2) u = u - Am[t][s2] * U[s2][col];
-      U[t][col] = u;
+      const float beta = sm.kq[t][2 * DK + DV + 1];
+      float u = beta * (sm.kq[t][2 * DK + col] - expf(sm.lga[t]) * sm.KS[t][col]);
+      for (int s2 = 0; s2 < t; ++s2) u = u - sm.Am[t][s2] * sm.U[s2][col];
+      sm.U[t][col] = u;
     }
   }
   __syncthreads();
   // 5. O = diag(gamma) QS + (M o QK^T) U; thread (i, r) takes tokens r, r+4, ...
   for (int t = r; t < T; t += 4) {
-    float o = expf(lga[t]) * QS[t][i];
-    for (int s2 = 0; s2 <= t; ++s2) o = o + Mq[t][s2] * U[s2][i];
-    store_act(c.out, act_index(t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
+    float o = expf(sm.lga[t]) * sm.QS[t][i];
+    for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][i];
+    store_act(c.out, act_index(row0 + t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
   }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
+  __shared__ GdnSmem<DK, DV> sm;
+  const int h = blockIdx.x, tid = threadIdx.x, i = tid >> 2, r = tid & 3;
+  float S[DK / 4];
+  const float* Sg = c.S + ((size_t)h * DV + i) * DK;
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+  verify_block<DK, DV>(c, 0, c.rows, S, c.tape, sm);
+}
+
+// A prompt chunk of nblk blocks of B tokens, all committed: per block the
+// verify above from the state in registers, then the commit's pinned replay
+// of the block's B tokens into that state (the tape records are the block's
+// sm.kq rows, bit for bit), so outputs and state are the ones separate verify
+// and replay launches per block give.  The state is written back at the end.
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk, int B) {
+  __shared__ GdnSmem<DK, DV> sm;
+  const int h = blockIdx.x, tid = threadIdx.x, i = tid >> 2, r = tid & 3;
+  float* Sg = const_cast<float*>(c.S) + ((size_t)h * DV + i) * DK;
+  float S[DK / 4];
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+  for (int j = 0; j < nblk; ++j) {
+    verify_block<DK, DV>(c, j * B, B, S, nullptr, sm);
+    __syncthreads();
+    for (int t = 0; t < B; ++t)
+      apply_token<DK>(S, &sm.kq[t][0], sm.kq[t][2 * DK + i], sm.kq[t][2 * DK + DV], sm.kq[t][2 * DK + DV + 1], r);
+    __syncthreads();                            // the next block overwrites sm
+  }
+#pragma unroll
+  for (int m = 0; m < DK / 4; ++m) Sg[r + 4 * m] = S[m];
 }
 
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
@@ -185,6 +224,18 @@ hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
     hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c);
   else if (c.dk == 32 && c.dv == 32)
     hipLaunchKernelGGL((gdn_verify_kernel<32, 32>), dim3(c.gh), dim3(128), 0, s, c);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_prompt(const GdnCall& c, int B, hipStream_t s) {
+  if (B < 1 || B > GDN_MAXT || c.rows < B || c.rows % B) return hipErrorInvalidValue;
+  const int nblk = c.rows / B;
+  if (c.dk == 128 && c.dv == 128)
+    hipLaunchKernelGGL((gdn_prompt_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
+  else if (c.dk == 32 && c.dv == 32)
+    hipLaunchKernelGGL((gdn_prompt_kernel<32, 32>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
