@@ -24,11 +24,20 @@
 
 namespace dfl {
 
+// Column j = r + 4m of a k (or q) row sits at kv[r + 4m] in the tape's
+// layout, or at kv[r * (dk/4 + 4) + m] in the lane-major LDS layout of the
+// verify (each lane's columns contiguous, the 4 lanes' runs 4 banks apart);
+// both give the same values, so the same results.
 template <int DK>
+constexpr int KRUN = DK / 4 + 4;
+template <int DK, bool LANE_MAJOR>
+__device__ __forceinline__ int kcol(int r, int m) { return LANE_MAJOR ? r * KRUN<DK> + m : r + 4 * m; }
+
+template <int DK, bool LANE_MAJOR = false>
 __device__ __forceinline__ float tree_dot(const float (&S)[DK / 4], const float* kv_lds, int r) {
   float p[DK / 4];
 #pragma unroll
-  for (int m = 0; m < DK / 4; ++m) p[m] = S[m] * kv_lds[r + 4 * m];
+  for (int m = 0; m < DK / 4; ++m) p[m] = S[m] * kv_lds[kcol<DK, LANE_MAJOR>(r, m)];
 #pragma unroll
   for (int w = DK / 8; w >= 1; w >>= 1)
 #pragma unroll
@@ -39,17 +48,17 @@ __device__ __forceinline__ float tree_dot(const float (&S)[DK / 4], const float*
   return x;
 }
 
-template <int DK>
+template <int DK, bool LANE_MAJOR = false>
 __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_lds, float v_i, float alpha,
                                             float beta, int r) {
-  const float acc = tree_dot<DK>(S, k_lds, r);
+  const float acc = tree_dot<DK, LANE_MAJOR>(S, k_lds, r);
   const float p = alpha * acc;
   const float rr = v_i - p;
   const float u = beta * rr;
 #pragma unroll
   for (int m = 0; m < DK / 4; ++m) {
     const float a = alpha * S[m];
-    const float b = u * k_lds[r + 4 * m];
+    const float b = u * k_lds[kcol<DK, LANE_MAJOR>(r, m)];
     S[m] = a + b;
   }
 }
@@ -67,7 +76,10 @@ __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_l
 constexpr int GDN_MAXT = 32;
 template <int DK, int DV>
 struct GdnSmem {
-  float kq[GDN_MAXT][2 * DK + DV + 2];   // k_hat, q_hat, v, alpha, beta per token
+  // per token: k_hat at [0, KB) and q_hat at [KB, 2 KB) (lane-major), v at
+  // [VO, VO + DV), alpha at AO, beta at BO
+  static constexpr int KB = 4 * KRUN<DK>, VO = 2 * KB, AO = VO + DV, BO = AO + 1, ROW = BO + 1;
+  float kq[GDN_MAXT][ROW];
   float lga[GDN_MAXT];                   // log alpha, then log gamma
   float KS[GDN_MAXT][DV + 1], QS[GDN_MAXT][DV + 1], U[GDN_MAXT][DV + 1];
   float Am[GDN_MAXT][GDN_MAXT + 1], Mq[GDN_MAXT][GDN_MAXT + 1];
@@ -77,11 +89,14 @@ struct GdnSmem {
 // the state S0 held in registers (thread (i, r): S0[i][r + 4m]); writes the
 // block's outputs and, if tape, its tape records.  Leaves the block's
 // k_hat, v, alpha, beta in sm.kq for a replay.
-template <int DK, int DV>
+// (TM: the most tokens a call passes, T <= TM <= GDN_MAXT)
+template <int DK, int DV, int TM>
 __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, const float (&S)[DK / 4], float* tape_base,
                                              GdnSmem<DK, DV>& sm) {
   constexpr int NT = 4 * DV;
   constexpr int REC = DK + DV + 2;
+  constexpr int KB = GdnSmem<DK, DV>::KB, VO = GdnSmem<DK, DV>::VO, AO = GdnSmem<DK, DV>::AO,
+                BO = GdnSmem<DK, DV>::BO;
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid >> 2, r = tid & 3;
@@ -90,14 +105,54 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
   const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
 
-  // 1. per-token preprocessing, one wave per token: L2 norms, gates, tape
+  // 1a. the block's projections (materialised in the activation format):
+  //     row t of kq takes k, q (lane-major), v, a, b.  The K splits are
+  //     added in their fixed order, one split's loads all in flight at once.
+  constexpr int NCOL = 2 * DK + DV + 2;
+  constexpr int PER = (TM * NCOL + NT - 1) / NT;
+  {
+    // offsets within one split (< 2^31 floats: at most 1024 rows of the
+    // projection); -1 past the block
+    float raw[PER];
+    int off[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + u * NT;
+      off[u] = -1;
+      if (idx < T * NCOL) {
+        const int t = idx / NCOL, e = idx % NCOL;
+        const size_t col = e < DK ? ko + e : e < 2 * DK ? qo + (e - DK) : e < 2 * DK + DV ? vo + (e - 2 * DK)
+                                                                                           : (e == 2 * DK + DV ? ao : bo);
+        off[u] = (row0 + t) * c.proj.ld + (int)col;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) raw[u] = off[u] >= 0 ? c.proj.p[off[u]] : 0.f;
+    for (int sp = 1; sp < c.proj.S; ++sp) {
+      const float* ps = c.proj.p + (size_t)sp * c.proj.stride;
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        if (off[u] >= 0) raw[u] = raw[u] + ps[off[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < T * NCOL) {
+        const int t = idx / NCOL, e = idx % NCOL;
+        const int pos = e < DK ? kcol<DK, true>(e & 3, e >> 2)
+                               : e < 2 * DK ? KB + kcol<DK, true>((e - DK) & 3, (e - DK) >> 2) : VO + (e - 2 * DK);
+        sm.kq[t][pos] = act_round(c.atype, raw[u]);
+      }
+    }
+  }
+  __syncthreads();
+  // 1b. per token, one wave per token: L2 norms, gates, tape
   for (int t = wave; t < T; t += NT / 64) {
-    // the projection is materialised in the activation format
-    auto proj = [&](size_t col) { return act_round(c.atype, parts_sum(c.proj, row0 + t, (int)col)); };
     float qs = 0.f, ks = 0.f;
     for (int e = lane; e < DK; e += 64) {
-      const float qv = proj(qo + e);
-      const float kv = proj(ko + e);
+      const int pe = kcol<DK, true>(e & 3, e >> 2);
+      const float qv = sm.kq[t][KB + pe];
+      const float kv = sm.kq[t][pe];
       qs += qv * qv;
       ks += kv * kv;
     }
@@ -107,23 +162,21 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     const float kn = 1.0f / sqrtf(ks + 1e-6f);
     float* tape = tape_base ? tape_base + ((size_t)t * gh + h) * REC : nullptr;
     for (int e = lane; e < DK; e += 64) {
-      const float kh = proj(ko + e) * kn;
-      sm.kq[t][e] = kh;
-      sm.kq[t][DK + e] = proj(qo + e) * qn;
+      const int pe = kcol<DK, true>(e & 3, e >> 2);
+      const float kh = sm.kq[t][pe] * kn;
+      sm.kq[t][pe] = kh;
+      sm.kq[t][KB + pe] = sm.kq[t][KB + pe] * qn;
       if (tape) tape[e] = kh;
     }
-    for (int e = lane; e < DV; e += 64) {
-      const float vv = proj(vo + e);
-      sm.kq[t][2 * DK + e] = vv;
-      if (tape) tape[DK + e] = vv;
-    }
+    if (tape)
+      for (int e = lane; e < DV; e += 64) tape[DK + e] = sm.kq[t][VO + e];
     if (lane == 0) {
-      const float av = proj(ao);
-      const float bv = proj(bo);
+      const float av = sm.kq[t][AO];
+      const float bv = sm.kq[t][BO];
       const float alpha = 1.0f / (1.0f + expf(av));
       const float beta = 1.0f / (1.0f + expf(-bv));
-      sm.kq[t][2 * DK + DV] = alpha;
-      sm.kq[t][2 * DK + DV + 1] = beta;
+      sm.kq[t][AO] = alpha;
+      sm.kq[t][BO] = beta;
       if (tape) {
         tape[DK + DV] = alpha;
         tape[DK + DV + 1] = beta;
@@ -135,18 +188,11 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   if (tid == 0)
     for (int t = 1; t < T; ++t) sm.lga[t] = sm.lga[t - 1] + sm.lga[t];   // log gamma_t
   // 2. KS, QS: row i of S0 against every k_hat_t, q_hat_t (4 lanes per row,
-  //    partial dots over columns r + 4m, then the xor-2 / xor-1 exchanges)
+  //    halving-tree partial dots over the lane's columns, then the xor-2 /
+  //    xor-1 exchanges)
   for (int t = 0; t < T; ++t) {
-    float dk_ = 0.f, dq_ = 0.f;
-#pragma unroll
-    for (int m = 0; m < DK / 4; ++m) {
-      dk_ = dk_ + S[m] * sm.kq[t][r + 4 * m];
-      dq_ = dq_ + S[m] * sm.kq[t][DK + r + 4 * m];
-    }
-    dk_ = dk_ + __shfl_xor(dk_, 2, 64);
-    dk_ = dk_ + __shfl_xor(dk_, 1, 64);
-    dq_ = dq_ + __shfl_xor(dq_, 2, 64);
-    dq_ = dq_ + __shfl_xor(dq_, 1, 64);
+    const float dk_ = tree_dot<DK, true>(S, &sm.kq[t][0], r);
+    const float dq_ = tree_dot<DK, true>(S, &sm.kq[t][KB], r);
     if (r == 0) { sm.KS[t][i] = dk_; sm.QS[t][i] = dq_; }
   }
   __syncthreads();
@@ -155,23 +201,33 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     const int which = e / (T * T), t = (e / T) % T, s2 = e % T;
     float v = 0.f;
     if (which == 0 ? s2 < t : s2 <= t) {
-      const float* x = which == 0 ? &sm.kq[t][0] : &sm.kq[t][DK];
+      const float* x = which == 0 ? &sm.kq[t][0] : &sm.kq[t][KB];
       float d = 0.f;
-      for (int j = 0; j < DK; ++j) d = d + x[j] * sm.kq[s2][j];
+#pragma unroll 1
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll 8
+        for (int m = 0; m < DK / 4; ++m) d = d + x[rr * KRUN<DK> + m] * sm.kq[s2][rr * KRUN<DK> + m];
       const float ratio = expf(sm.lga[t] - sm.lga[s2]);
-      v = which == 0 ? sm.kq[t][2 * DK + DV + 1] * ratio * d : ratio * d;
+      v = which == 0 ? sm.kq[t][BO] * ratio * d : ratio * d;
     }
     if (which == 0) sm.Am[t][s2] = v; else sm.Mq[t][s2] = v;
   }
   __syncthreads();
-  // 4. U by forward substitution, one thread per value column
+  // 4. U by forward substitution, one thread per value column (the column's
+  //    U values also kept in registers for the chain)
   if (tid < DV) {
     const int col = tid;
-    for (int t = 0; t < T; ++t) {
-      const float beta = sm.kq[t][2 * DK + DV + 1];
-      float u = beta * (sm.kq[t][2 * DK + col] - expf(sm.lga[t]) * sm.KS[t][col]);
-      for (int s2 = 0; s2 < t; ++s2) u = u - sm.Am[t][s2] * sm.U[s2][col];
-      sm.U[t][col] = u;
+    float uu[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        const float beta = sm.kq[t][BO];
+        float u = beta * (sm.kq[t][VO + col] - expf(sm.lga[t]) * sm.KS[t][col]);
+#pragma unroll
+        for (int s2 = 0; s2 < t; ++s2) u = u - sm.Am[t][s2] * uu[s2];
+        uu[t] = u;
+        sm.U[t][col] = u;
+      }
     }
   }
   __syncthreads();
@@ -191,7 +247,7 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
   for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
-  verify_block<DK, DV>(c, 0, c.rows, S, c.tape, sm);
+  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, S, c.tape, sm);
 }
 
 // A prompt chunk of nblk blocks of B tokens, all committed: per block the
@@ -199,7 +255,7 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
 // of the block's B tokens into that state (the tape records are the block's
 // sm.kq rows, bit for bit), so outputs and state are the ones separate verify
 // and replay launches per block give.  The state is written back at the end.
-template <int DK, int DV>
+template <int DK, int DV, int TM>
 __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk, int B) {
   __shared__ GdnSmem<DK, DV> sm;
   const int h = blockIdx.x, tid = threadIdx.x, i = tid >> 2, r = tid & 3;
@@ -208,10 +264,11 @@ __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk,
 #pragma unroll
   for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
   for (int j = 0; j < nblk; ++j) {
-    verify_block<DK, DV>(c, j * B, B, S, nullptr, sm);
+    verify_block<DK, DV, TM>(c, j * B, B, S, nullptr, sm);
     __syncthreads();
     for (int t = 0; t < B; ++t)
-      apply_token<DK>(S, &sm.kq[t][0], sm.kq[t][2 * DK + i], sm.kq[t][2 * DK + DV], sm.kq[t][2 * DK + DV + 1], r);
+      apply_token<DK, true>(S, &sm.kq[t][0], sm.kq[t][GdnSmem<DK, DV>::VO + i], sm.kq[t][GdnSmem<DK, DV>::AO],
+                            sm.kq[t][GdnSmem<DK, DV>::BO], r);
     __syncthreads();                            // the next block overwrites sm
   }
 #pragma unroll
@@ -232,12 +289,15 @@ hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
 hipError_t launch_gdn_prompt(const GdnCall& c, int B, hipStream_t s) {
   if (B < 1 || B > GDN_MAXT || c.rows < B || c.rows % B) return hipErrorInvalidValue;
   const int nblk = c.rows / B;
-  if (c.dk == 128 && c.dv == 128)
-    hipLaunchKernelGGL((gdn_prompt_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
-  else if (c.dk == 32 && c.dv == 32)
-    hipLaunchKernelGGL((gdn_prompt_kernel<32, 32>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
-  else
+  if (c.dk == 128 && c.dv == 128) {
+    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, 16>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
+    else hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, GDN_MAXT>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
+  } else if (c.dk == 32 && c.dv == 32) {
+    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, 16>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
+    else hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, GDN_MAXT>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
