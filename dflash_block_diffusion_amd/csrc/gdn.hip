@@ -78,28 +78,40 @@ template <int DK, int DV>
 struct GdnSmem {
   // per token: k_hat at [0, KB) and q_hat at [KB, 2 KB) (lane-major), v at
   // [VO, VO + DV), alpha at AO, beta at BO
-  static constexpr int KB = 4 * KRUN<DK>, VO = 2 * KB, AO = VO + DV, BO = AO + 1, ROW = BO + 1;
-  float kq[GDN_MAXT][ROW];
+  // (rows padded to 16 bytes, so that a lane's k or q run is read 16 bytes
+  // at a time)
+  static constexpr int KB = 4 * KRUN<DK>, VO = 2 * KB, AO = VO + DV, BO = AO + 1, ROW = (BO + 1 + 3) / 4 * 4;
+  float kq[GDN_MAXT][ROW] __attribute__((aligned(16)));
   float lga[GDN_MAXT];                   // log alpha, then log gamma
   float KS[GDN_MAXT][DV + 1], QS[GDN_MAXT][DV + 1], U[GDN_MAXT][DV + 1];
   float Am[GDN_MAXT][GDN_MAXT + 1], Mq[GDN_MAXT][GDN_MAXT + 1];
 };
 
+// Value rows per work-group: a head's dv rows go to dv / GDN_RW work-groups
+// (rows are independent in the rule), so the per-row work (K S0^T, Q S0^T,
+// O, the replay), which is VALU-bound, spreads over more CUs; every
+// work-group of a head repeats the per-token and T x T work.
+template <int DV>
+constexpr int GDN_RW = DV < 32 ? DV : 32;
+
 // The block of T tokens at projection / output rows row0..row0+T-1 against
-// the state S0 held in registers (thread (i, r): S0[i][r + 4m]); writes the
-// block's outputs and, if tape, its tape records.  Leaves the block's
-// k_hat, v, alpha, beta in sm.kq for a replay.
+// the state S0 held in registers: thread (i, r) with tid < 4 GDN_RW holds
+// row i = i0 + tid/4 (i0 = blockIdx.y GDN_RW), S0[i][r + 4m].  Writes the
+// block's outputs of the work-group's rows and, if tape, its tape records.
+// Leaves the block's k_hat, v, alpha, beta in sm.kq for a replay.
 // (TM: the most tokens a call passes, T <= TM <= GDN_MAXT)
 template <int DK, int DV, int TM>
 __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, const float (&S)[DK / 4], float* tape_base,
                                              GdnSmem<DK, DV>& sm) {
   constexpr int NT = 4 * DV;
+  constexpr int RW = GDN_RW<DV>;
   constexpr int REC = DK + DV + 2;
   constexpr int KB = GdnSmem<DK, DV>::KB, VO = GdnSmem<DK, DV>::VO, AO = GdnSmem<DK, DV>::AO,
                 BO = GdnSmem<DK, DV>::BO;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x, i0 = blockIdx.y * RW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = tid >> 2, r = tid & 3;
+  const bool owner = tid < 4 * RW;             // wave-uniform: RW is a multiple of 16
+  const int i = i0 + (tid >> 2), r = tid & 3;
   const int gh = c.gh;
   const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
   const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
@@ -190,11 +202,13 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   // 2. KS, QS: row i of S0 against every k_hat_t, q_hat_t (4 lanes per row,
   //    halving-tree partial dots over the lane's columns, then the xor-2 /
   //    xor-1 exchanges)
-  for (int t = 0; t < T; ++t) {
-    const float dk_ = tree_dot<DK, true>(S, &sm.kq[t][0], r);
-    const float dq_ = tree_dot<DK, true>(S, &sm.kq[t][KB], r);
-    if (r == 0) { sm.KS[t][i] = dk_; sm.QS[t][i] = dq_; }
-  }
+  if (owner)
+#pragma unroll 2
+    for (int t = 0; t < T; ++t) {
+      const float dk_ = tree_dot<DK, true>(S, &sm.kq[t][0], r);
+      const float dq_ = tree_dot<DK, true>(S, &sm.kq[t][KB], r);
+      if (r == 0) { sm.KS[t][i] = dk_; sm.QS[t][i] = dq_; }
+    }
   __syncthreads();
   // 3. A and M o QK^T (T x T each)
   for (int e = tid; e < 2 * T * T; e += NT) {
@@ -213,10 +227,11 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     if (which == 0) sm.Am[t][s2] = v; else sm.Mq[t][s2] = v;
   }
   __syncthreads();
-  // 4. U by forward substitution, one thread per value column (the column's
-  //    U values also kept in registers for the chain)
-  if (tid < DV) {
-    const int col = tid;
+  // 4. U by forward substitution, one thread per value column of the
+  //    work-group's rows (the column's U values also kept in registers for
+  //    the chain)
+  if (tid < RW) {
+    const int col = i0 + tid;
     float uu[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
@@ -232,22 +247,28 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   }
   __syncthreads();
   // 5. O = diag(gamma) QS + (M o QK^T) U; thread (i, r) takes tokens r, r+4, ...
-  for (int t = r; t < T; t += 4) {
-    float o = expf(sm.lga[t]) * sm.QS[t][i];
-    for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][i];
-    store_act(c.out, act_index(row0 + t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
+  if (owner) {
+    for (int t = r; t < T; t += 4) {
+      float o = expf(sm.lga[t]) * sm.QS[t][i];
+      for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][i];
+      store_act(c.out, act_index(row0 + t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
+    }
   }
 }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   __shared__ GdnSmem<DK, DV> sm;
-  const int h = blockIdx.x, tid = threadIdx.x, i = tid >> 2, r = tid & 3;
+  const int h = blockIdx.x, tid = threadIdx.x, r = tid & 3;
+  const int i = blockIdx.y * GDN_RW<DV> + (tid >> 2);
   float S[DK / 4];
-  const float* Sg = c.S + ((size_t)h * DV + i) * DK;
+  if (tid < 4 * GDN_RW<DV>) {
+    const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
-  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
-  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, S, c.tape, sm);
+    for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+  }
+  // the head's first work-group records the tape
+  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, S, blockIdx.y == 0 ? c.tape : nullptr, sm);
 }
 
 // A prompt chunk of nblk blocks of B tokens, all committed: per block the
@@ -258,29 +279,34 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
 template <int DK, int DV, int TM>
 __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk, int B) {
   __shared__ GdnSmem<DK, DV> sm;
-  const int h = blockIdx.x, tid = threadIdx.x, i = tid >> 2, r = tid & 3;
+  const int h = blockIdx.x, tid = threadIdx.x, r = tid & 3;
+  const int i = blockIdx.y * GDN_RW<DV> + (tid >> 2);
+  const bool owner = tid < 4 * GDN_RW<DV>;
   float* Sg = const_cast<float*>(c.S) + ((size_t)h * DV + i) * DK;
   float S[DK / 4];
+  if (owner)
 #pragma unroll
-  for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+    for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
   for (int j = 0; j < nblk; ++j) {
     verify_block<DK, DV, TM>(c, j * B, B, S, nullptr, sm);
     __syncthreads();
-    for (int t = 0; t < B; ++t)
-      apply_token<DK, true>(S, &sm.kq[t][0], sm.kq[t][GdnSmem<DK, DV>::VO + i], sm.kq[t][GdnSmem<DK, DV>::AO],
-                            sm.kq[t][GdnSmem<DK, DV>::BO], r);
+    if (owner)
+      for (int t = 0; t < B; ++t)
+        apply_token<DK, true>(S, &sm.kq[t][0], sm.kq[t][GdnSmem<DK, DV>::VO + i], sm.kq[t][GdnSmem<DK, DV>::AO],
+                              sm.kq[t][GdnSmem<DK, DV>::BO], r);
     __syncthreads();                            // the next block overwrites sm
   }
+  if (owner)
 #pragma unroll
-  for (int m = 0; m < DK / 4; ++m) Sg[r + 4 * m] = S[m];
+    for (int m = 0; m < DK / 4; ++m) Sg[r + 4 * m] = S[m];
 }
 
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
   if (c.rows < 1 || c.rows > 32) return hipErrorInvalidValue;    // one chunk of at most 32 tokens
   if (c.dk == 128 && c.dv == 128)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh), dim3(512), 0, s, c);
+    hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh, 128 / GDN_RW<128>), dim3(512), 0, s, c);
   else if (c.dk == 32 && c.dv == 32)
-    hipLaunchKernelGGL((gdn_verify_kernel<32, 32>), dim3(c.gh), dim3(128), 0, s, c);
+    hipLaunchKernelGGL((gdn_verify_kernel<32, 32>), dim3(c.gh, 32 / GDN_RW<32>), dim3(128), 0, s, c);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -290,11 +316,13 @@ hipError_t launch_gdn_prompt(const GdnCall& c, int B, hipStream_t s) {
   if (B < 1 || B > GDN_MAXT || c.rows < B || c.rows % B) return hipErrorInvalidValue;
   const int nblk = c.rows / B;
   if (c.dk == 128 && c.dv == 128) {
-    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, 16>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
-    else hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, GDN_MAXT>), dim3(c.gh), dim3(512), 0, s, c, nblk, B);
+    const dim3 grid(c.gh, 128 / GDN_RW<128>);
+    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, 16>), grid, dim3(512), 0, s, c, nblk, B);
+    else hipLaunchKernelGGL((gdn_prompt_kernel<128, 128, GDN_MAXT>), grid, dim3(512), 0, s, c, nblk, B);
   } else if (c.dk == 32 && c.dv == 32) {
-    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, 16>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
-    else hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, GDN_MAXT>), dim3(c.gh), dim3(128), 0, s, c, nblk, B);
+    const dim3 grid(c.gh, 32 / GDN_RW<32>);
+    if (B <= 16) hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, 16>), grid, dim3(128), 0, s, c, nblk, B);
+    else hipLaunchKernelGGL((gdn_prompt_kernel<32, 32, GDN_MAXT>), grid, dim3(128), 0, s, c, nblk, B);
   } else {
     return hipErrorInvalidValue;
   }
