@@ -30,6 +30,14 @@ namespace dfl {
 // both give the same values, so the same results.
 template <int DK>
 constexpr int KRUN = DK / 4 + 4;
+
+// x of lane l ^ X (X = 1 or 2) within each quad of lanes, by a DPP quad
+// permutation (the 4 lanes of a row are a quad)
+template <int X>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int sel = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), sel, 0xF, 0xF, true));
+}
 template <int DK, bool LANE_MAJOR>
 __device__ __forceinline__ int kcol(int r, int m) { return LANE_MAJOR ? r * KRUN<DK> + m : r + 4 * m; }
 
@@ -43,8 +51,8 @@ __device__ __forceinline__ float tree_dot(const float (&S)[DK / 4], const float*
 #pragma unroll
     for (int m = 0; m < w; ++m) p[m] = p[m] + p[m + w];
   float x = p[0];
-  x = x + __shfl_xor(x, 2, 64);
-  x = x + __shfl_xor(x, 1, 64);
+  x = x + quad_xor<2>(x);
+  x = x + quad_xor<1>(x);
   return x;
 }
 
@@ -74,6 +82,13 @@ __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_l
 // per token for the commit's pinned replay.  One work-group per head,
 // 4*dv threads; thread (i, r) owns value row i and key columns r + 4m.
 constexpr int GDN_MAXT = 32;
+// Value rows per work-group: a head's dv rows go to dv / GDN_RW work-groups
+// (rows are independent in the rule), so the per-row work (K S0^T, Q S0^T,
+// O, the replay), which is VALU-bound, spreads over more CUs; every
+// work-group of a head repeats the per-token and T x T work.
+template <int DV>
+constexpr int GDN_RW = DV < 32 ? DV : 32;
+
 template <int DK, int DV>
 struct GdnSmem {
   // per token: k_hat at [0, KB) and q_hat at [KB, 2 KB) (lane-major), v at
@@ -82,26 +97,23 @@ struct GdnSmem {
   // at a time)
   static constexpr int KB = 4 * KRUN<DK>, VO = 2 * KB, AO = VO + DV, BO = AO + 1, ROW = (BO + 1 + 3) / 4 * 4;
   float kq[GDN_MAXT][ROW] __attribute__((aligned(16)));
+  // the work-group's GDN_RW rows of the state S0, lane-major like k and q
+  float Sl[GDN_RW<DV>][4 * KRUN<DK>] __attribute__((aligned(16)));
   float lga[GDN_MAXT];                   // log alpha, then log gamma
   float KS[GDN_MAXT][DV + 1], QS[GDN_MAXT][DV + 1], U[GDN_MAXT][DV + 1];
   float Am[GDN_MAXT][GDN_MAXT + 1], Mq[GDN_MAXT][GDN_MAXT + 1];
 };
 
-// Value rows per work-group: a head's dv rows go to dv / GDN_RW work-groups
-// (rows are independent in the rule), so the per-row work (K S0^T, Q S0^T,
-// O, the replay), which is VALU-bound, spreads over more CUs; every
-// work-group of a head repeats the per-token and T x T work.
-template <int DV>
-constexpr int GDN_RW = DV < 32 ? DV : 32;
 
 // The block of T tokens at projection / output rows row0..row0+T-1 against
-// the state S0 held in registers: thread (i, r) with tid < 4 GDN_RW holds
-// row i = i0 + tid/4 (i0 = blockIdx.y GDN_RW), S0[i][r + 4m].  Writes the
-// block's outputs of the work-group's rows and, if tape, its tape records.
-// Leaves the block's k_hat, v, alpha, beta in sm.kq for a replay.
+// the work-group's rows i0..i0+GDN_RW-1 of the state S0 in sm.Sl (i0 =
+// blockIdx.y GDN_RW; written by the caller before the call); thread (i, r)
+// with tid < 4 GDN_RW is row i = i0 + tid/4.  Writes the block's outputs of
+// the work-group's rows and, if tape, its tape records.  Leaves the block's
+// k_hat, v, alpha, beta in sm.kq for a replay.
 // (TM: the most tokens a call passes, T <= TM <= GDN_MAXT)
 template <int DK, int DV, int TM>
-__device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, const float (&S)[DK / 4], float* tape_base,
+__device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, float* tape_base,
                                              GdnSmem<DK, DV>& sm) {
   constexpr int NT = 4 * DV;
   constexpr int RW = GDN_RW<DV>;
@@ -202,13 +214,19 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   // 2. KS, QS: row i of S0 against every k_hat_t, q_hat_t (4 lanes per row,
   //    halving-tree partial dots over the lane's columns, then the xor-2 /
   //    xor-1 exchanges)
-  if (owner)
-#pragma unroll 2
-    for (int t = 0; t < T; ++t) {
-      const float dk_ = tree_dot<DK, true>(S, &sm.kq[t][0], r);
-      const float dq_ = tree_dot<DK, true>(S, &sm.kq[t][KB], r);
-      if (r == 0) { sm.KS[t][i] = dk_; sm.QS[t][i] = dq_; }
+  //    every thread group of 4 GDN_RW threads takes every G-th token
+  {
+    constexpr int G = NT / (4 * RW);
+    const int lt = tid % (4 * RW), il = lt >> 2;
+    float Sr[DK / 4];
+#pragma unroll
+    for (int m = 0; m < DK / 4; ++m) Sr[m] = sm.Sl[il][kcol<DK, true>(r, m)];
+    for (int t = tid / (4 * RW); t < T; t += G) {
+      const float dk_ = tree_dot<DK, true>(Sr, &sm.kq[t][0], r);
+      const float dq_ = tree_dot<DK, true>(Sr, &sm.kq[t][KB], r);
+      if (r == 0) { sm.KS[t][i0 + il] = dk_; sm.QS[t][i0 + il] = dq_; }
     }
+  }
   __syncthreads();
   // 3. A and M o QK^T (T x T each)
   for (int e = tid; e < 2 * T * T; e += NT) {
@@ -261,14 +279,14 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   __shared__ GdnSmem<DK, DV> sm;
   const int h = blockIdx.x, tid = threadIdx.x, r = tid & 3;
   const int i = blockIdx.y * GDN_RW<DV> + (tid >> 2);
-  float S[DK / 4];
   if (tid < 4 * GDN_RW<DV>) {
     const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
-    for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+    for (int m = 0; m < DK / 4; ++m) sm.Sl[tid >> 2][kcol<DK, true>(r, m)] = Sg[r + 4 * m];
   }
+  // (verify_block's first barrier orders these stores before their reads);
   // the head's first work-group records the tape
-  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, S, blockIdx.y == 0 ? c.tape : nullptr, sm);
+  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm);
 }
 
 // A prompt chunk of nblk blocks of B tokens, all committed: per block the
@@ -288,7 +306,10 @@ __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk,
 #pragma unroll
     for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
   for (int j = 0; j < nblk; ++j) {
-    verify_block<DK, DV, TM>(c, j * B, B, S, nullptr, sm);
+    if (owner)
+#pragma unroll
+      for (int m = 0; m < DK / 4; ++m) sm.Sl[tid >> 2][kcol<DK, true>(r, m)] = S[m];
+    verify_block<DK, DV, TM>(c, j * B, B, nullptr, sm);
     __syncthreads();
     if (owner)
       for (int t = 0; t < B; ++t)
