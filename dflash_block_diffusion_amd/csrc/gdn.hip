@@ -100,21 +100,62 @@ struct GdnSmem {
   // the work-group's GDN_RW rows of the state S0, lane-major like k and q
   float Sl[GDN_RW<DV>][4 * KRUN<DK>] __attribute__((aligned(16)));
   float lga[GDN_MAXT];                   // log alpha, then log gamma
+  float ga[GDN_MAXT];                    // gamma = exp(log gamma)
   float KS[GDN_MAXT][DV + 1], QS[GDN_MAXT][DV + 1], U[GDN_MAXT][DV + 1];
   float Am[GDN_MAXT][GDN_MAXT + 1], Mq[GDN_MAXT][GDN_MAXT + 1];
 };
 
 
+// The projections of the T tokens at rows row0.. of a block (materialised in
+// the activation format later, at the LDS store): element idx = tid + u NT of
+// the block's T x (k, q, v, a, b) values.  The K splits are added in their
+// fixed order, one split's loads all in flight at once.
+template <int DK, int DV, int TM>
+__device__ __forceinline__ void gdn_load_block(const GdnCall& c, int row0, int T,
+                                               float (&raw)[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)]) {
+  constexpr int NT = 4 * DV, NCOL = 2 * DK + DV + 2, PER = (TM * NCOL + NT - 1) / NT;
+  const int h = blockIdx.x, tid = threadIdx.x, gh = c.gh;
+  const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
+  const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
+  const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
+  // offsets within one split (< 2^31 floats: at most 1024 rows of the
+  // projection); -1 past the block
+  int off[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = tid + u * NT;
+    off[u] = -1;
+    if (idx < T * NCOL) {
+      const int t = idx / NCOL, e = idx % NCOL;
+      const size_t col = e < DK ? ko + e : e < 2 * DK ? qo + (e - DK) : e < 2 * DK + DV ? vo + (e - 2 * DK)
+                                                                                         : (e == 2 * DK + DV ? ao : bo);
+      off[u] = (row0 + t) * c.proj.ld + (int)col;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) raw[u] = off[u] >= 0 ? c.proj.p[off[u]] : 0.f;
+  for (int sp = 1; sp < c.proj.S; ++sp) {
+    const float* ps = c.proj.p + (size_t)sp * c.proj.stride;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (off[u] >= 0) raw[u] = raw[u] + ps[off[u]];
+  }
+}
+
 // The block of T tokens at projection / output rows row0..row0+T-1 against
 // the work-group's rows i0..i0+GDN_RW-1 of the state S0 in sm.Sl (i0 =
 // blockIdx.y GDN_RW; written by the caller before the call); thread (i, r)
-// with tid < 4 GDN_RW is row i = i0 + tid/4.  Writes the block's outputs of
-// the work-group's rows and, if tape, its tape records.  Leaves the block's
-// k_hat, v, alpha, beta in sm.kq for a replay.
-// (TM: the most tokens a call passes, T <= TM <= GDN_MAXT)
+// with tid < 4 GDN_RW is row i = i0 + tid/4.  raw holds the block's
+// projections (gdn_load_block); once they are in LDS, the loads of the
+// block at next_row0 (if >= 0, next_T tokens) go into raw, in flight during
+// the rest.  Writes the block's outputs of the work-group's rows and, if
+// tape, its tape records.  Leaves the block's k_hat, v, alpha, beta in sm.kq
+// for a replay.  (TM: the most tokens a call passes, T <= TM <= GDN_MAXT)
 template <int DK, int DV, int TM>
 __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, float* tape_base,
-                                             GdnSmem<DK, DV>& sm) {
+                                             GdnSmem<DK, DV>& sm,
+                                             float (&raw)[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)],
+                                             int next_row0, int next_T) {
   constexpr int NT = 4 * DV;
   constexpr int RW = GDN_RW<DV>;
   constexpr int REC = DK + DV + 2;
@@ -125,39 +166,12 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   const bool owner = tid < 4 * RW;             // wave-uniform: RW is a multiple of 16
   const int i = i0 + (tid >> 2), r = tid & 3;
   const int gh = c.gh;
-  const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
-  const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
-  const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
 
-  // 1a. the block's projections (materialised in the activation format):
-  //     row t of kq takes k, q (lane-major), v, a, b.  The K splits are
-  //     added in their fixed order, one split's loads all in flight at once.
+  // 1a. the block's projections, materialised in the activation format:
+  //     row t of kq takes k, q (lane-major), v, a, b
   constexpr int NCOL = 2 * DK + DV + 2;
   constexpr int PER = (TM * NCOL + NT - 1) / NT;
   {
-    // offsets within one split (< 2^31 floats: at most 1024 rows of the
-    // projection); -1 past the block
-    float raw[PER];
-    int off[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + u * NT;
-      off[u] = -1;
-      if (idx < T * NCOL) {
-        const int t = idx / NCOL, e = idx % NCOL;
-        const size_t col = e < DK ? ko + e : e < 2 * DK ? qo + (e - DK) : e < 2 * DK + DV ? vo + (e - 2 * DK)
-                                                                                           : (e == 2 * DK + DV ? ao : bo);
-        off[u] = (row0 + t) * c.proj.ld + (int)col;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) raw[u] = off[u] >= 0 ? c.proj.p[off[u]] : 0.f;
-    for (int sp = 1; sp < c.proj.S; ++sp) {
-      const float* ps = c.proj.p + (size_t)sp * c.proj.stride;
-#pragma unroll
-      for (int u = 0; u < PER; ++u)
-        if (off[u] >= 0) raw[u] = raw[u] + ps[off[u]];
-    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = tid + u * NT;
@@ -169,6 +183,7 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
       }
     }
   }
+  if (next_row0 >= 0) gdn_load_block<DK, DV, TM>(c, next_row0, next_T, raw);
   __syncthreads();
   // 1b. per token, one wave per token: L2 norms, gates, tape
   for (int t = wave; t < T; t += NT / 64) {
@@ -228,7 +243,8 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     }
   }
   __syncthreads();
-  // 3. A and M o QK^T (T x T each)
+  // 3. A and M o QK^T (T x T each); gamma_t once per token
+  if (tid < T) sm.ga[tid] = expf(sm.lga[tid]);
   for (int e = tid; e < 2 * T * T; e += NT) {
     const int which = e / (T * T), t = (e / T) % T, s2 = e % T;
     float v = 0.f;
@@ -255,7 +271,7 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     for (int t = 0; t < TM; ++t) {
       if (t < T) {
         const float beta = sm.kq[t][BO];
-        float u = beta * (sm.kq[t][VO + col] - expf(sm.lga[t]) * sm.KS[t][col]);
+        float u = beta * (sm.kq[t][VO + col] - sm.ga[t] * sm.KS[t][col]);
 #pragma unroll
         for (int s2 = 0; s2 < t; ++s2) u = u - sm.Am[t][s2] * uu[s2];
         uu[t] = u;
@@ -267,7 +283,7 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   // 5. O = diag(gamma) QS + (M o QK^T) U; thread (i, r) takes tokens r, r+4, ...
   if (owner) {
     for (int t = r; t < T; t += 4) {
-      float o = expf(sm.lga[t]) * sm.QS[t][i];
+      float o = sm.ga[t] * sm.QS[t][i];
       for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][i];
       store_act(c.out, act_index(row0 + t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
     }
@@ -286,7 +302,9 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   }
   // (verify_block's first barrier orders these stores before their reads);
   // the head's first work-group records the tape
-  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm);
+  float raw[(GDN_MAXT * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)];
+  gdn_load_block<DK, DV, GDN_MAXT>(c, 0, c.rows, raw);
+  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm, raw, -1, 0);
 }
 
 // A prompt chunk of nblk blocks of B tokens, all committed: per block the
@@ -305,11 +323,14 @@ __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk,
   if (owner)
 #pragma unroll
     for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
+  // block j + 1's projections load while block j is worked on
+  float raw[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)];
+  gdn_load_block<DK, DV, TM>(c, 0, B, raw);
   for (int j = 0; j < nblk; ++j) {
     if (owner)
 #pragma unroll
       for (int m = 0; m < DK / 4; ++m) sm.Sl[tid >> 2][kcol<DK, true>(r, m)] = S[m];
-    verify_block<DK, DV, TM>(c, j * B, B, nullptr, sm);
+    verify_block<DK, DV, TM>(c, j * B, B, nullptr, sm, raw, j + 1 < nblk ? (j + 1) * B : -1, B);
     __syncthreads();
     if (owner)
       for (int t = 0; t < B; ++t)
