@@ -21,6 +21,10 @@
 // two-pass structure of the long-context verify attention in the dflash-mlx
 // note ("Technical challenges", JIT SDPA 2-pass for N >= 1024), here used at
 // every length so the graph of a step is length-independent.
+//
+// attn_prefill_kernel: the causal attention of a prompt chunk (more than 64
+// rows) in one pass with an online softmax: enough query rows per KV head
+// fill the chip without splitting the keys, so no partials and no combine.
 #include "common.h"
 
 namespace dfl {
@@ -351,7 +355,8 @@ constexpr int PF_PAGES = 1;                            // pages per stage
 constexpr int PF_KEYS = PF_PAGES * PAGE;               // 64 keys
 constexpr int PF_DMAS = 4 * PF_PAGES;                  // K (or V^T) DMAs per wave and stage
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_prefill_kernel(AttnArgs a, void* out, int otype, int ldo) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_prefill_kernel(AttnArgs a, void* out,
+                                                                                           int otype, int ldo) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ldsK0[PF_PAGES * 16384];
   __shared__ __attribute__((aligned(16))) uint8_t ldsV0[PF_PAGES * 16384];

@@ -299,8 +299,14 @@ int dense_splits(int fmt, int n, int k, int m, int epi) {
 }
 
 bool dense_ok(int fmt, int n, int k, int m, int epi) {
-  return (fmt == W_W4 || fmt == W_W8 || fmt == W_BF16) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 && n % 16 == 0 && k % 128 == 0 &&
-         (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
+  return (fmt == W_W4 || fmt == W_W8 || fmt == W_BF16) && m > MAX_ROWS && m <= DENSE_MAX_ROWS && m % 16 == 0 &&
+         n % 16 == 0 && k % 128 == 0 && (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
+}
+
+template <int FMT, int MT>
+static void launch_dense(int epi, dim3 grid, hipStream_t s, const GemmArgs& a, int kt_per) {
+  if (epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_PARTIAL, MT>), grid, dim3(256), 0, s, a, kt_per);
+  else hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_SILU, MT>), grid, dim3(256), 0, s, a, kt_per);
 }
 
 hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t s, int* splits) {
@@ -315,19 +321,10 @@ hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t 
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   const int kt_per = (W.k / 128 + S - 1) / S;
   const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + mt - 1) / mt), 1, S);
-  if (W.fmt == W_W4 && mt == 8) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 8>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 8>), grid, dim3(256), 0, s, a, kt_per);
-  } else if (W.fmt == W_W4) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W4, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  } else if (W.fmt == W_W8) {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_W8, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  } else {
-    if (c.epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<W_BF16, EPI_PARTIAL, 4>), grid, dim3(256), 0, s, a, kt_per);
-    else hipLaunchKernelGGL((gemm_dense_kernel<W_BF16, EPI_SILU, 4>), grid, dim3(256), 0, s, a, kt_per);
-  }
+  if (W.fmt == W_W4 && mt == 8) launch_dense<W_W4, 8>(c.epi, grid, s, a, kt_per);
+  else if (W.fmt == W_W4) launch_dense<W_W4, 4>(c.epi, grid, s, a, kt_per);
+  else if (W.fmt == W_W8) launch_dense<W_W8, 4>(c.epi, grid, s, a, kt_per);
+  else launch_dense<W_BF16, 4>(c.epi, grid, s, a, kt_per);
   if (splits) *splits = S;
   return hipGetLastError();
 }

@@ -123,12 +123,14 @@ def test_model_create_rejects_bad_head_dim_and_sel():
 
 
 def test_linear_rows_beyond_the_limits_are_refused():
-    # prompt chunks: W4A16 only, multiples of 16 up to 1024 rows
+    # prompt chunks: BF16, W8A16 and W4A16, multiples of 16 up to 1024 rows
     from dflash_block_diffusion_amd import configs as C
     L = bn.lib()
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 72) == 0      # not a multiple of 16
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 1040) == 0    # above 1024
-    assert L.dflash_linear_workspace_bytes(C.FMT_BF16, 256, 512, 128) == 0      # dense path: W4 and W8 only
+    assert L.dflash_linear_workspace_bytes(C.FMT_F32, 256, 512, 128) == 0       # no fp32 dense path
+    assert L.dflash_linear_workspace_bytes(C.FMT_BF16, 256, 480, 128) == 0      # dense needs K % 128
+    assert L.dflash_linear_workspace_bytes(C.FMT_BF16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 448, 128) == 0     # W8 dense needs K % 128
     assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 128) > 0
