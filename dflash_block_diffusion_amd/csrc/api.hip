@@ -759,7 +759,43 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
     HIPCHK(launch_fill_i32((int32_t*)s->gdn_S,
                            (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk, 0, st));
   int last = 0, c0 = 0;
-  if (s->pm > 0) {
+  // Without GatedDeltaNet layers and with a dense drafter pass, the whole
+  // prompt runs as chunks (the last one padded to a whole 16-row group); the
+  // first token is the argmax of the last row, from the lm-head over its
+  // 16-row group, and the drafter's context rows are committed in two parts
+  // (up to that group, then the group's valid rows), as B-row chunks would.
+  // Otherwise the whole blocks before the one holding the last token run as
+  // chunks and that block takes the block path.
+  const bool fold = s->pm > 0 && s->pm_draft && t->n_gdn == 0;
+  if (fold) {
+    const int H = t->d.hidden;
+    while (c0 < n_tokens) {
+      const int valid = std::min(s->pm, n_tokens - c0);
+      if (c0 + valid < n_tokens) {           // a full chunk (pm rows, a multiple of B)
+        RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, valid, st, false));
+        RC(do_commit(s, nullptr, valid, nullptr, st));
+        RC(draft_context_kv(s, st, 0, valid));
+        c0 += valid;
+        continue;
+      }
+      const int rows = (valid + 15) / 16 * 16, tail0 = (valid - 1) / 16 * 16;
+      last = valid - tail0;
+      RC(do_verify(s, s->tokens + c0, s->ybuf, nullptr, rows, st, false));
+      // the last row's logits: lm-head over its 16-row group of the final norm
+      const void* xh = (const char*)s->bu + (size_t)tail0 * H * elem_bytes(t->gin);
+      RC(gemm(s, t->lm, xh, H, 16, EPI_ARGMAX, st, nullptr, nullptr, 0, s->temp > 0.f ? s->vlog : nullptr,
+              t->d.vocab, 0, s->ybuf));
+      if (tail0 > 0) {
+        RC(do_commit(s, nullptr, tail0, nullptr, st));
+        RC(draft_context_kv(s, st, 0, tail0));
+      }
+      RC(do_commit(s, nullptr, last, nullptr, st));
+      // the group's context rows (rows past the prompt go to slots past n,
+      // which the next rows overwrite before any read)
+      RC(draft_context_kv(s, st, tail0, 16));
+      c0 = n_tokens;
+    }
+  } else if (s->pm > 0) {
     // the whole blocks before the one holding the last token run as dense
     // chunks of up to pm rows; their drafter context rows then go in B at a
     // time (the commit of each block makes it the pending context)

@@ -187,10 +187,11 @@ void dflash_state_destroy(dflash_state *st);
 
 /* Prefill P prompt tokens (target forward in chunks of B, causal; the
  * drafter's context rows for all P positions).  An int4 or bf16 target runs
- * the prompt up to its last whole block in chunks of up to 1024 rows (dense
- * GEMMs, one-pass causal attention, GatedDeltaNet layers B tokens at a time),
- * then the rest as one block; an fp32 target runs every chunk as a block.
- * Writes the first generated
+ * the prompt in chunks of up to 1024 rows (dense GEMMs, one-pass causal
+ * attention); with GatedDeltaNet layers (run B tokens at a time) or a drafter
+ * without the dense path, the chunks stop at the last whole block before the
+ * last token and that block runs as a block.  An fp32 target runs every
+ * chunk as a block.  Writes the first generated
  * token (argmax of the last prompt row) to d_first_tok[0] and sets n = P.
  * The committed token log holds the prompt then every emitted token.
  * Not graph-capturable (host loop over chunks).  Errors: CAPACITY if

@@ -235,12 +235,13 @@ def test_reduced_lockstep(name, P):
 
 @pytest.mark.parametrize("P", [1200, 700, 545, 96, 33])
 def test_reduced_8b_dense_prompt_chunks_lockstep(P):
-    # 1200 prompt tokens: dense chunks of 1024 and 160 rows (the int4 prompt
-    # GEMM and the one-pass prompt attention; the second chunk attends over
-    # the first), then the last 16 tokens as a block; 700: one 672-row chunk,
-    # then 28 tokens; 545: one 544-row chunk, then a 1-token block; 96: one
-    # 64-row chunk on the block GEMMs and split-KV attention; 33: one 32-row
-    # chunk
+    # the whole prompt runs as chunks, the last padded to 16 rows, whose
+    # last 16-row group gives the first token and the pending context rows.
+    # 1200 prompt tokens: chunks of 1024 and 176 rows (the int4 prompt GEMM
+    # and the one-pass prompt attention; the second chunk attends over the
+    # first); 700: one 704-row chunk (4 padding rows); 545: one 560-row chunk,
+    # a 1-row last group; 96: one 96-row chunk; 33: one 48-row chunk on the
+    # block GEMMs and split-KV attention
     cfg = reduced("8b")
     _, _, stats, _ = lockstep(cfg, P, [0, 31, 9])
     assert stats["compared"] >= 3 * cfg.block
@@ -250,8 +251,8 @@ def test_reduced_8b_dense_prompt_chunks_lockstep(P):
 @pytest.mark.parametrize("P", [1100, 530])
 def test_reduced_4b_dense_prompt_chunks_lockstep(P):
     # bf16 target and drafter: 1100 prompt tokens run chunks of 1024 rows
-    # (the bf16 prompt GEMM, the one-pass prompt attention) and 64 rows (the
-    # block path), then a 12-token block; 530: one 528-row chunk, then 2
+    # (the bf16 prompt GEMM, the one-pass prompt attention) and 80 rows (76
+    # valid); 530: one 544-row chunk, a 2-row last group
     cfg = reduced("4b")
     _, _, stats, _ = lockstep(cfg, P, [0, 15, 6])
     assert stats["compared"] >= 3 * cfg.block
