@@ -164,8 +164,16 @@ def prefill_gemm_rate(pair, prompt, cfg, ctx):
     between two HIP events on the launch stream.  FLOPs = 2 * rows * the
     target's projection parameters over the rows that run as dense chunks."""
     import torch
+    from dflash_block_diffusion_amd import configs
     B = cfg.block
-    dense_rows = ((ctx - 1) // B) * B
+    # rows the dense chunks run (chunks of up to 1024 rows): the whole prompt,
+    # the last chunk padded to 16 rows, or, with GatedDeltaNet layers, the
+    # whole blocks before the one holding the last token
+    if any(k != configs.LAYER_ATTN for k in cfg.target.layer_kinds or ()):
+        dense_rows = ((ctx - 1) // B) * B
+    else:
+        full = (ctx - 1) // 1024
+        dense_rows = full * 1024 + (ctx - full * 1024 + 15) // 16 * 16
     pair.prof(True)
     pair.prefill(prompt)
     torch.cuda.synchronize()
