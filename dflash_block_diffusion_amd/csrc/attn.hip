@@ -32,11 +32,11 @@ namespace dfl {
 static constexpr float LOG2E = 1.4426950408889634f;
 
 // ------------------------------------------------------------ QK norm + RoPE
-// One wave per (row, head); a work-group takes QK_ROWS consecutive rows of
-// one head when the launch has many rows (a prompt chunk), one otherwise.
-constexpr int QK_ROWS = 4;
-__global__ __launch_bounds__(64 * QK_ROWS) void qk_rope_kernel(RopeCall c) {
-  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), head = blockIdx.y, lane = threadIdx.x & 63;
+// One wave per (row, head); a work-group takes R consecutive rows of one
+// head: 4 when the launch has many rows (a prompt chunk), 1 otherwise.
+template <int R>
+__global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
+  const int row = blockIdx.x * R + (threadIdx.x >> 6), head = blockIdx.y, lane = threadIdx.x & 63;
   if (row >= c.block_rows + c.ctx_rows) return;       // past the launch's rows (whole waves)
   if (row >= c.block_rows && head < c.hq) return;      // context rows only carry k/v
   const int d = c.d, half = d >> 1;
@@ -88,9 +88,11 @@ __global__ __launch_bounds__(64 * QK_ROWS) void qk_rope_kernel(RopeCall c) {
 }
 
 hipError_t launch_qk_rope(const RopeCall& c, hipStream_t s) {
-  const int rows = c.block_rows + c.ctx_rows, per = rows > 64 ? QK_ROWS : 1;
-  dim3 grid((rows + per - 1) / per, c.hq + c.hkv);
-  hipLaunchKernelGGL(qk_rope_kernel, grid, dim3(64 * per), 0, s, c);
+  const int rows = c.block_rows + c.ctx_rows;
+  if (rows > 64)
+    hipLaunchKernelGGL(qk_rope_kernel<4>, dim3((rows + 3) / 4, c.hq + c.hkv), dim3(256), 0, s, c);
+  else
+    hipLaunchKernelGGL(qk_rope_kernel<1>, dim3(rows, c.hq + c.hkv), dim3(64), 0, s, c);
   return hipGetLastError();
 }
 
