@@ -46,18 +46,20 @@ __device__ __forceinline__ uint32_t gload4(const void* p) {
   asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
   return r;
 }
-constexpr int DENSE_RW = 4;                  // row tiles per wave
 constexpr int DENSE_MAX_ROWS = 1024;
 
 // FMT W4: per 128-column step one 1 KiB tile and one scale dword per row
 // tile; W8: two 64-column tiles per row tile and the per-row scale applied to
 // the finished sum (as the stream kernel does); BF16: four 32-column tiles
 // per row tile, MFMA bf16 on the weights as stored (bf16 activations).
-template <int FMT, int EPI, int DENSE_MT>
+// DENSE_RW: row tiles per wave (4; 2 for the 128-row bf16 shape)
+template <int FMT, int EPI, int DENSE_MT, int DENSE_RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
                                                                                        int kt_per) {
   static_assert(FMT == W_W4 || FMT == W_W8 || FMT == W_BF16, "dense kernel: int4, int8 or bf16 weights");
-  static_assert(DENSE_MT == 4 || (DENSE_MT == 8 && FMT == W_W4), "dense kernel: 4 token blocks, or 8 for int4");
+  static_assert((DENSE_MT == 4 && DENSE_RW == 4) || (DENSE_MT == 8 && DENSE_RW == 4 && FMT == W_W4) ||
+                    (DENSE_MT == 8 && DENSE_RW == 2 && FMT == W_BF16),
+                "dense kernel: 64 rows x 4 row tiles, or 128 rows x 4 (int4) / x 2 (bf16)");
   constexpr int WT = FMT == W_W4 ? 1 : (FMT == W_W8 ? 2 : 4);  // weight tiles per row tile and 128-column step
   constexpr int WLOADS = FMT == W_BF16 ? 4 * DENSE_RW : 2 * DENSE_RW;  // register loads per step
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
@@ -282,17 +284,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 }
 
 // token blocks per work-group: 8 for int4 chunks of more than 512 rows with
-// a wide N (gate/up) or a deep K (down), else 4
+// a wide N (gate/up) or a deep K (down), and for bf16 chunks of more than 512
+// rows (whose weights, 4x the bytes of int4 ones, would otherwise load
+// faster than a CU's vector-memory path moves them), else 4; row tiles per
+// wave: 2 for that bf16 shape (registers), else 4
 static int dense_mt(int fmt, int n, int k, int m) {
+  if (fmt == W_BF16) return m > 512 ? 8 : 4;
   return fmt == W_W4 && m > 512 && (n >= 16384 || k >= 8192) ? 8 : 4;
 }
+static int dense_rw(int fmt, int n, int k, int m) { return fmt == W_BF16 && dense_mt(fmt, n, k, m) == 8 ? 2 : 4; }
 
 // K splits of a dense launch: partial sums go to S slices so that the grid
 // reaches the chip's 256 CUs, each split keeping at least 4 K tiles
 int dense_splits(int fmt, int n, int k, int m, int epi) {
   if (epi != EPI_PARTIAL) return 1;
-  const int ktiles = k / 128, mt = dense_mt(fmt, n, k, m);
-  const int base = ((n / 16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((m / 16 + mt - 1) / mt);
+  const int ktiles = k / 128, mt = dense_mt(fmt, n, k, m), rw = dense_rw(fmt, n, k, m);
+  const int base = ((n / 16 + 4 * rw - 1) / (4 * rw)) * ((m / 16 + mt - 1) / mt);
   int S = 1;
   while (S < MAX_SPLITS && base * S < 256 && ktiles / (2 * S) >= 4) S *= 2;
   return S;
@@ -303,16 +310,19 @@ bool dense_ok(int fmt, int n, int k, int m, int epi) {
          n % 16 == 0 && k % 128 == 0 && (epi == EPI_PARTIAL || (epi == EPI_SILU && n % 32 == 0));
 }
 
-template <int FMT, int MT>
+template <int FMT, int MT, int RW = 4>
 static void launch_dense(int epi, dim3 grid, hipStream_t s, const GemmArgs& a, int kt_per) {
-  if (epi == EPI_PARTIAL) hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_PARTIAL, MT>), grid, dim3(256), 0, s, a, kt_per);
-  else hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_SILU, MT>), grid, dim3(256), 0, s, a, kt_per);
+  if (epi == EPI_PARTIAL)
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_PARTIAL, MT, RW>), grid, dim3(256), 0, s, a, kt_per);
+  else
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, EPI_SILU, MT, RW>), grid, dim3(256), 0, s, a, kt_per);
 }
 
 hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t s, int* splits) {
   const GemmW& W = *c.W;
   if (!dense_ok(W.fmt, W.n, W.k, c.m, c.epi)) return hipErrorInvalidValue;
-  const int S = dense_splits(W.fmt, W.n, W.k, c.m, c.epi), mt = dense_mt(W.fmt, W.n, W.k, c.m);
+  const int S = dense_splits(W.fmt, W.n, W.k, c.m, c.epi), mt = dense_mt(W.fmt, W.n, W.k, c.m),
+            rw = dense_rw(W.fmt, W.n, W.k, c.m);
   if (c.epi == EPI_PARTIAL && (size_t)S * c.m * W.n > w.part_floats) return hipErrorInvalidValue;
   GemmArgs a{};
   a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
@@ -320,10 +330,11 @@ hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t 
   a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   const int kt_per = (W.k / 128 + S - 1) / S;
-  const dim3 grid(((a.ntile16 + 4 * DENSE_RW - 1) / (4 * DENSE_RW)) * ((c.m / 16 + mt - 1) / mt), 1, S);
+  const dim3 grid(((a.ntile16 + 4 * rw - 1) / (4 * rw)) * ((c.m / 16 + mt - 1) / mt), 1, S);
   if (W.fmt == W_W4 && mt == 8) launch_dense<W_W4, 8>(c.epi, grid, s, a, kt_per);
   else if (W.fmt == W_W4) launch_dense<W_W4, 4>(c.epi, grid, s, a, kt_per);
   else if (W.fmt == W_W8) launch_dense<W_W8, 4>(c.epi, grid, s, a, kt_per);
+  else if (mt == 8) launch_dense<W_BF16, 8, 2>(c.epi, grid, s, a, kt_per);
   else launch_dense<W_BF16, 4>(c.epi, grid, s, a, kt_per);
   if (splits) *splits = S;
   return hipGetLastError();
