@@ -36,8 +36,9 @@ static constexpr float LOG2E = 1.4426950408889634f;
 // head: 4 when the launch has many rows (a prompt chunk), 1 otherwise.
 template <int R>
 __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
-  const int row = blockIdx.x * R + (threadIdx.x >> 6), head = blockIdx.y, lane = threadIdx.x & 63;
-  if (row >= c.block_rows + c.ctx_rows) return;       // past the launch's rows (whole waves)
+  const int row = R == 1 ? (int)blockIdx.x : (int)blockIdx.x * R + (int)(threadIdx.x >> 6);
+  const int head = blockIdx.y, lane = R == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+  if (R > 1 && row >= c.block_rows + c.ctx_rows) return;   // past the launch's rows (whole waves)
   if (row >= c.block_rows && head < c.hq) return;      // context rows only carry k/v
   const int d = c.d, half = d >> 1;
   const bool act = lane < half;
