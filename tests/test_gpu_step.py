@@ -233,13 +233,14 @@ def test_reduced_lockstep(name, P):
     assert stats["compared"] >= len(forced) * cfg.block
 
 
-@pytest.mark.parametrize("P", [1200, 700, 545, 96, 33])
+@pytest.mark.parametrize("P", [1200, 1025, 700, 545, 96, 33])
 def test_reduced_8b_dense_prompt_chunks_lockstep(P):
     # the whole prompt runs as chunks, the last padded to 16 rows, whose
     # last 16-row group gives the first token and the pending context rows.
     # 1200 prompt tokens: chunks of 1024 and 176 rows (the int4 prompt GEMM
     # and the one-pass prompt attention; the second chunk attends over the
-    # first); 700: one 704-row chunk (4 padding rows); 545: one 560-row chunk,
+    # first); 1025: a 1024-row chunk, then a 16-row chunk holding the last
+    # token alone; 700: one 704-row chunk (4 padding rows); 545: one 560-row chunk,
     # a 1-row last group; 96: one 96-row chunk; 33: one 48-row chunk on the
     # block GEMMs and split-KV attention
     cfg = reduced("8b")
