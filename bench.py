@@ -217,7 +217,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the draft+verify step of one sequence runs on a single "
-              f"MI355X here (requested --gpus {args.gpus}); nothing in this build uses a second GPU.",
+              f"MI355X (requested --gpus {args.gpus}); the library uses no second GPU.",
               file=sys.stderr)
         sys.exit(2)
 

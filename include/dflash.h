@@ -48,7 +48,7 @@ enum {
   DFLASH_E_SHAPE = -2,       /* dimensions the kernels do not support */
   DFLASH_E_CAPACITY = -3,    /* arena too small / context capacity exceeded */
   DFLASH_E_DEVICE = -4,      /* HIP error (no device, launch failure) */
-  DFLASH_E_UNSUPPORTED = -5  /* valid request this build does not implement */
+  DFLASH_E_UNSUPPORTED = -5  /* valid request the library does not implement */
 };
 
 /* Weight formats. Activations are fp32 for DFLASH_FMT_F32 models and bf16
