@@ -38,6 +38,19 @@ __device__ __forceinline__ float quad_xor(float x) {
   constexpr int sel = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), sel, 0xF, 0xF, true));
 }
+// x of the lane R places further round its DPP row of 16 lanes
+template <int R>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
+}
+// the sum over each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ float row16_sum(float x) {
+  x = x + quad_xor<1>(x);
+  x = x + quad_xor<2>(x);
+  x = x + row_ror<4>(x);
+  x = x + row_ror<8>(x);
+  return x;
+}
 template <int DK, bool LANE_MAJOR>
 __device__ __forceinline__ int kcol(int r, int m) { return LANE_MAJOR ? r * KRUN<DK> + m : r + 4 * m; }
 
@@ -185,22 +198,27 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   }
   if (next_row0 >= 0) gdn_load_block<DK, DV, TM>(c, next_row0, next_T, raw);
   __syncthreads();
-  // 1b. per token, one wave per token: L2 norms, gates, tape
-  for (int t = wave; t < T; t += NT / 64) {
+  // 1b. per token, 16 lanes per token (4 tokens per wave): L2 norms (sums
+  //     over the 16 lanes by DPP), gates, tape
+  for (int t0 = 0; t0 < T; t0 += 4 * (NT / 64)) {
+    const int t = t0 + 4 * wave + (lane >> 4), l16 = lane & 15;
+    const bool tok = t < T;
     float qs = 0.f, ks = 0.f;
-    for (int e = lane; e < DK; e += 64) {
-      const int pe = kcol<DK, true>(e & 3, e >> 2);
-      const float qv = sm.kq[t][KB + pe];
-      const float kv = sm.kq[t][pe];
-      qs += qv * qv;
-      ks += kv * kv;
-    }
-    qs = wave_sum(qs);
-    ks = wave_sum(ks);
+    if (tok)
+      for (int e = l16; e < DK; e += 16) {
+        const int pe = kcol<DK, true>(e & 3, e >> 2);
+        const float qv = sm.kq[t][KB + pe];
+        const float kv = sm.kq[t][pe];
+        qs += qv * qv;
+        ks += kv * kv;
+      }
+    qs = row16_sum(qs);                        // every lane takes part in the exchanges
+    ks = row16_sum(ks);
+    if (!tok) continue;
     const float qn = 1.0f / sqrtf(qs + 1e-6f) * (1.0f / sqrtf((float)DK));
     const float kn = 1.0f / sqrtf(ks + 1e-6f);
     float* tape = tape_base ? tape_base + ((size_t)t * gh + h) * REC : nullptr;
-    for (int e = lane; e < DK; e += 64) {
+    for (int e = l16; e < DK; e += 16) {
       const int pe = kcol<DK, true>(e & 3, e >> 2);
       const float kh = sm.kq[t][pe] * kn;
       sm.kq[t][pe] = kh;
@@ -208,8 +226,8 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
       if (tape) tape[e] = kh;
     }
     if (tape)
-      for (int e = lane; e < DV; e += 64) tape[DK + e] = sm.kq[t][VO + e];
-    if (lane == 0) {
+      for (int e = l16; e < DV; e += 16) tape[DK + e] = sm.kq[t][VO + e];
+    if (l16 == 0) {
       const float av = sm.kq[t][AO];
       const float bv = sm.kq[t][BO];
       const float alpha = 1.0f / (1.0f + expf(av));
