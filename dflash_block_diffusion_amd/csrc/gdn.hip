@@ -92,8 +92,9 @@ __device__ __forceinline__ void apply_token(float (&S)[DK / 4], const float* k_l
 //   (I + A) U = diag(beta)(V - diag(gamma) KS)   (forward substitution)
 //   O = diag(gamma) QS + (M o Q K^T) U,  M[t][s] = gamma_t/gamma_s (s <= t).
 // The committed state is only read; the tape records (k_hat, v, alpha, beta)
-// per token for the commit's pinned replay.  One work-group per head,
-// 4*dv threads; thread (i, r) owns value row i and key columns r + 4m.
+// per token for the commit's pinned replay.  dv / GDN_RW work-groups of 4*dv
+// threads per head, each for GDN_RW value rows; in the state's register
+// layout thread (i, r) holds value row i, key columns r + 4m.
 constexpr int GDN_MAXT = 32;
 // Value rows per work-group: a head's dv rows go to dv / GDN_RW work-groups
 // (rows are independent in the rule), so the per-row work (K S0^T, Q S0^T,
@@ -157,8 +158,7 @@ __device__ __forceinline__ void gdn_load_block(const GdnCall& c, int row0, int T
 
 // The block of T tokens at projection / output rows row0..row0+T-1 against
 // the work-group's rows i0..i0+GDN_RW-1 of the state S0 in sm.Sl (i0 =
-// blockIdx.y GDN_RW; written by the caller before the call); thread (i, r)
-// with tid < 4 GDN_RW is row i = i0 + tid/4.  raw holds the block's
+// blockIdx.y GDN_RW; written by the caller before the call).  raw holds the block's
 // projections (gdn_load_block); once they are in LDS, the loads of the
 // block at next_row0 (if >= 0, next_T tokens) go into raw, in flight during
 // the rest.  Writes the block's outputs of the work-group's rows and, if
@@ -176,8 +176,7 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
                 BO = GdnSmem<DK, DV>::BO;
   const int h = blockIdx.x, i0 = blockIdx.y * RW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool owner = tid < 4 * RW;             // wave-uniform: RW is a multiple of 16
-  const int i = i0 + (tid >> 2), r = tid & 3;
+  const int r = tid & 3;
   const int gh = c.gh;
 
   // 1a. the block's projections, materialised in the activation format:
@@ -298,13 +297,13 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     }
   }
   __syncthreads();
-  // 5. O = diag(gamma) QS + (M o QK^T) U; thread (i, r) takes tokens r, r+4, ...
-  if (owner) {
-    for (int t = r; t < T; t += 4) {
-      float o = sm.ga[t] * sm.QS[t][i];
-      for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][i];
-      store_act(c.out, act_index(row0 + t, h * DV + i, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
-    }
+  // 5. O = diag(gamma) QS + (M o QK^T) U over the work-group's rows; every
+  //    thread takes (token, row) pairs
+  for (int e = tid; e < T * RW; e += NT) {
+    const int t = e / RW, il = i0 + e % RW;
+    float o = sm.ga[t] * sm.QS[t][il];
+    for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][il];
+    store_act(c.out, act_index(row0 + t, h * DV + il, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
   }
 }
 
