@@ -57,9 +57,9 @@ template <int FMT, int EPI, int DENSE_MT, int DENSE_RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dense_kernel(GemmArgs a,
                                                                                        int kt_per) {
   static_assert(FMT == W_W4 || FMT == W_W8 || FMT == W_BF16, "dense kernel: int4, int8 or bf16 weights");
-  static_assert((DENSE_MT == 4 && DENSE_RW == 4) || (DENSE_MT == 8 && DENSE_RW == 4 && FMT == W_W4) ||
+  static_assert((DENSE_MT == 4 && DENSE_RW == 4) || (DENSE_MT == 8 && DENSE_RW == 4 && FMT != W_BF16) ||
                     (DENSE_MT == 8 && DENSE_RW == 2 && FMT == W_BF16),
-                "dense kernel: 64 rows x 4 row tiles, or 128 rows x 4 (int4) / x 2 (bf16)");
+                "dense kernel: 64 rows x 4 row tiles, or 128 rows x 4 (int4, int8) / x 2 (bf16)");
   constexpr int WT = FMT == W_W4 ? 1 : (FMT == W_W8 ? 2 : 4);  // weight tiles per row tile and 128-column step
   constexpr int WLOADS = FMT == W_BF16 ? 4 * DENSE_RW : 2 * DENSE_RW;  // register loads per step
   __shared__ __attribute__((aligned(16))) uint8_t xs0[DENSE_MT * 4 * 1024];
@@ -289,8 +289,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // faster than a CU's vector-memory path moves them), else 4; row tiles per
 // wave: 2 for that bf16 shape (registers), else 4
 static int dense_mt(int fmt, int n, int k, int m) {
-  if (fmt == W_BF16) return m > 512 ? 8 : 4;
-  return fmt == W_W4 && m > 512 && (n >= 16384 || k >= 8192) ? 8 : 4;
+  if (fmt == W_BF16 || fmt == W_W8) return m > 512 ? 8 : 4;
+  return m > 512 && (n >= 16384 || k >= 8192) ? 8 : 4;
 }
 static int dense_rw(int fmt, int n, int k, int m) { return fmt == W_BF16 && dense_mt(fmt, n, k, m) == 8 ? 2 : 4; }
 
@@ -333,6 +333,7 @@ hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t 
   const dim3 grid(((a.ntile16 + 4 * rw - 1) / (4 * rw)) * ((c.m / 16 + mt - 1) / mt), 1, S);
   if (W.fmt == W_W4 && mt == 8) launch_dense<W_W4, 8>(c.epi, grid, s, a, kt_per);
   else if (W.fmt == W_W4) launch_dense<W_W4, 4>(c.epi, grid, s, a, kt_per);
+  else if (W.fmt == W_W8 && mt == 8) launch_dense<W_W8, 8>(c.epi, grid, s, a, kt_per);
   else if (W.fmt == W_W8) launch_dense<W_W8, 4>(c.epi, grid, s, a, kt_per);
   else if (mt == 8) launch_dense<W_BF16, 8, 2>(c.epi, grid, s, a, kt_per);
   else launch_dense<W_BF16, 4>(c.epi, grid, s, a, kt_per);

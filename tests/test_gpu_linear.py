@@ -184,10 +184,11 @@ def test_linear_dense_w4_parity(n, k, m):
     assert np.all(np.abs(y - ref) <= bound(x, w))
 
 
-@pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 4096, 512), (4096, 20480, 96)])
+@pytest.mark.parametrize("n,k,m", [(48, 256, 80), (1040, 1024, 128), (272, 4096, 512), (4096, 20480, 96),
+                                   (272, 4096, 784), (4096, 20480, 1024)])
 def test_linear_dense_w8_parity(n, k, m):
     # the int8 dense path (the drafter's context pass of a prompt chunk):
-    # the row scale on the finished sum
+    # the row scale on the finished sum; past 512 rows the 128-row shape
     g = synth.HostSynth(303)
     w = g.weight(f"dense8_{n}x{k}", n, k, C.FMT_W8A16)
     x = x_values(np.random.default_rng(n + k + m + 1), m, k, C.FMT_W8A16)
