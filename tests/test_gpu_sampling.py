@@ -231,3 +231,23 @@ def test_sampled_generation_is_seeded_and_well_formed():
     assert outs[0] == outs[1]
     assert outs[0] != outs[2]
     assert all(0 <= t < cfg.target.vocab for t in outs[0])
+
+
+@pytest.mark.parametrize("P", [700, 1025, 33])
+def test_prompt_chunk_first_draw_at_low_temperature_is_the_greedy_token(P):
+    # the dense prompt pass keeps the last prompt row's logits for the first
+    # draw (the lm-head over that row's 16-row group): at T = 1e-4 the draw
+    # is the argmax, so it equals the greedy first token of the same prompt
+    from dataclasses import replace
+    cfg = C.get("8b").reduced(2, 1)
+    cfg = replace(cfg, target=replace(cfg.target, vocab=32768), drafter=replace(cfg.drafter, vocab=32768))
+    ck = synth.make_pair(cfg)
+    prompt = synth.prompt(cfg, P)
+    greedy = Pair(cfg, ck, max_ctx=P + 256)
+    first0 = greedy.prefill(prompt)
+    del greedy
+    samp = Pair(cfg, ck, max_ctx=P + 256)
+    samp.set_sampling(1e-4, 5)
+    first1 = samp.prefill(prompt)
+    assert 0 <= first0 < cfg.target.vocab
+    assert first1 == first0
