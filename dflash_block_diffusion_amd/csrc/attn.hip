@@ -106,7 +106,6 @@ struct AttnArgs {
 };
 
 constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
-constexpr int ATTN_DMAS = 4 * ATTN_PAGES;            // K (or V^T) page DMAs per wave
 
 
 
@@ -121,7 +120,7 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 }
 
 // head_dim 128, bf16 q/k/v.  Work-group = (split of 256 keys, KV head, group
-// of 4 row blocks), one wave per 16-row block of the head's G*B query rows
+// of NW row blocks), one wave per 16-row block of the head's G*B query rows
 // (row r = token r/G, query head h*G + r%G).
 //  1. Every wave issues its share of the 4 K pages and 4 V^T pages as
 //     direct global->LDS 16-byte loads (128 KiB in flight per work-group, no
@@ -135,8 +134,14 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 //     p_hi + p_lo, two bf16 values whose sum carries 16 significant bits.
 //  3. Unnormalised partial (o, max, sum) per row; attn_combine merges the
 //     splits.
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+// NW waves per work-group (4 or 8): with 8, one staging of a split's K / V^T
+// serves all 8 row blocks of a 32-token block's 128 query rows per KV head
+// (G = 4), so each split is read from HBM once, not once per 4 row blocks.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
+  constexpr int BPW = 16 / NW;                 // 1 KiB DMA blocks per page and wave
+  constexpr int DMAS = BPW * ATTN_PAGES;       // V^T DMAs per wave (and K DMAs)
   // K and V^T staging as two LDS objects, so that waiting for the K loads
   // does not also wait for the V^T loads
   __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int p = 0; p < ATTN_PAGES; ++p)
     pbase[p] = ((size_t)__builtin_amdgcn_readlane(my_page, p) * a.hkv + h) * PAGE * D;
-  const int rbi = blockIdx.z * 4 + wave;      // this wave's 16-row block
+  const int rbi = blockIdx.z * NW + wave;     // this wave's 16-row block
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
   const int r = rb * 16 + lr;
@@ -174,15 +179,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int kv_len = n + a.B;
   if (key0 >= kv_len) return;                 // uniform over the work-group
   // K pages first, then V^T pages: the scores and the softmax run while the
-  // V^T loads are still in flight.  Each of the 4 waves issues ATTN_DMAS K
-  // and then ATTN_DMAS V^T 1 KiB blocks.
+  // V^T loads are still in flight.  Each of the NW waves issues DMAS K and
+  // then DMAS V^T 1 KiB blocks (16 blocks per 16 KiB page).
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int p = 0; p < ATTN_PAGES; ++p) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int blk = wave + 4 * j;
+      for (int j = 0; j < BPW; ++j) {
+        const int blk = wave + NW * j;
         const int q = blk * 64 + lane;         // 16-byte granule of the 16 KiB region
         const uint16_t* src;
         if (half == 0) {
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   }
   // this wave's q and K loads are done once at most its V^T loads are
   // outstanding
-  __builtin_amdgcn_s_waitcnt(vm_wait(ATTN_DMAS));
+  __builtin_amdgcn_s_waitcnt(vm_wait(DMAS));
   __builtin_amdgcn_s_barrier();
 
   // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr),
@@ -643,7 +648,16 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
       hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4 * c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+    // One work-group fits a CU (128 KiB of LDS).  Eight waves share one K / V^T
+    // staging only when the four-wave grid would spill past the 256 CUs and
+    // the row blocks fill whole groups of eight: with fewer splits, four-wave
+    // work-groups spread the score and P.V work over twice the CUs and are
+    // faster (8B shapes, block 32: 3.38 vs 3.53 ms a step at ctx 64, 4.02 vs
+    // 3.88 ms at ctx 4096).
+    if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > 256)
+      hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

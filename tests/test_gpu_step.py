@@ -67,13 +67,13 @@ def compare_tokens(got, ref, margin, stats, floor=0.0):
     assert np.array_equal(np.asarray(got)[ok], np.asarray(ref)[ok]), (got, ref, margin)
 
 
-def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0):
+def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
     """Run len(forced) injected steps on GPU and oracle in lockstep; with
     max_draft > 0 both sides verify only the first max_draft drafts."""
     B, V = cfg.block, cfg.target.vocab
     ck = synth.make_pair(cfg)
     prompt = synth.prompt(cfg, P)
-    max_ctx = P + (len(forced) + 4) * B + 64
+    max_ctx = max_ctx or P + (len(forced) + 4) * B + 64
     pair = Pair(cfg, ck, max_ctx=max_ctx)
     if max_draft:
         rows = pair.set_max_draft(max_draft)
@@ -231,6 +231,16 @@ def test_reduced_lockstep(name, P):
     forced = [0, cfg.block - 1, 5, 11]
     _, _, stats, _ = lockstep(cfg, P, forced)
     assert stats["compared"] >= len(forced) * cfg.block
+
+
+def test_reduced_8b_lockstep_long_cache_eight_wave_attention():
+    # a 4400-token cache gives 18 key splits: 18 x 8 KV heads x 2 four-wave
+    # groups exceed 256 work-groups, so the block attention runs eight waves
+    # per work-group (the 128 query rows of a KV head share one K / V staging);
+    # splits past the committed keys leave at once
+    cfg = reduced("8b")
+    _, _, stats, _ = lockstep(cfg, 300, [0, 31, 5, 11], max_ctx=4400)
+    assert stats["compared"] >= 4 * cfg.block
 
 
 @pytest.mark.parametrize("P", [1200, 1025, 700, 545, 96, 33])
