@@ -28,8 +28,13 @@ the order the pages describe it:
 
 Pinned against the pages and the mathematics by ``tests/test_oracle_*.py``.
 
-Parity unpinned: the drafter's internal wiring (mask token id, which slot
-predicts which position, how the projected hidden states enter each drafter
-layer) follows stated readings; the pages give no worked example of it, so
-only its component pieces and the end-to-end losslessness invariant pin it.
+The way the pieces are assembled -- decoder-layer wiring, the causal verify
+and its hidden side-write, the drafter's view of the whole context and the
+whole block, context keys normed and rotated at their own positions, the
+GatedDeltaNet gates and query scale -- is pinned by constructed-weight closed
+forms and exact invariants (tests/test_oracle_assembly.py).  The choices that
+remain readings (mask token id, which slot predicts which position, that the
+projected hidden states enter each drafter layer as extra keys/values) are
+pinned to their stated definition, not to a worked example on the pages,
+which give none.
 """
