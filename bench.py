@@ -99,63 +99,86 @@ def committed_traffic(kernel):
     return None
 
 
-def cpu_baseline(cfg, ctx, budget_s=30.0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    one target layer, one drafter layer, the fc projection and the lm-head
-    at the benchmark's widths, formats, block and context (the KV caches of
-    the ctx committed positions are seeded random values instead of a host
-    prefill); the full step time is extrapolated by the layer counts."""
+def host_checkpoint(ck):
+    """Copy a device checkpoint (torch tensors) to host numpy arrays in the
+    layout the oracle reads: the oracle then runs on the very weights the
+    GPU model was packed from."""
     import numpy as np
-    from dataclasses import replace
+    from dflash_block_diffusion_amd.synth import Weight
+
+    def cv(t):
+        if t is None:
+            return None
+        return t.detach().cpu().numpy() if hasattr(t, "detach") else np.asarray(t)
+
+    def walk(v):
+        if isinstance(v, Weight):
+            return Weight(v.fmt, v.n, v.k, values=cv(v.values), codes=cv(v.codes), scales=cv(v.scales))
+        if isinstance(v, dict):
+            return {k: walk(x) for k, x in v.items()}
+        if isinstance(v, list):
+            return [walk(x) for x in v]
+        return cv(v) if hasattr(v, "detach") else v
+    return walk(ck)
+
+
+def cpu_baseline(cfg, ctx, host_ck):
+    """The oracle, as it stands, timed on one whole draft+verify step of the
+    benchmark workload: the drafter's pass over the block (all its layers,
+    the shared lm-head), the target's verify of the block (all its layers,
+    the lm-head), the acceptance and the commit with the drafter's context
+    rows for the accepted tokens.  Same weights as the GPU model; the KV
+    caches of the ctx committed positions (and GatedDeltaNet states) are
+    seeded random values instead of a host prefill of the prompt, which
+    would take minutes.  Weight copying is not timed."""
+    import numpy as np
     from dflash_block_diffusion_amd import synth
-    from oracle.spec import OracleDrafter, OracleTarget
+    from oracle.spec import OracleDrafter, OracleTarget, accept_length
+    from oracle.model import argmax_first
     B = cfg.block
-    one = replace(cfg, target=replace(cfg.target, n_layers=1, layer_kinds=cfg.target.kinds()[-1:]),
-                  drafter=replace(cfg.drafter, n_layers=1), sel_layers=(0,))
-    g = synth.HostSynth(cfg.seed)
-    t0 = time.time()
-    ck = synth.make_pair(one, g)
-    fc_full = g.weight("w_fc_full", cfg.drafter.hidden, len(cfg.sel_layers) * cfg.target.hidden, cfg.drafter.fmt)
-    gen_s = time.time() - t0
     cap = ctx + 2 * B
-    tgt = OracleTarget(one.target, ck["target"], one.sel_layers, cap)
-    drf = OracleDrafter(one.drafter, ck["drafter"], ck["target"], one.mask_token, B, cap)
+    tgt = OracleTarget(cfg.target, host_ck["target"], cfg.sel_layers, cap)
+    drf = OracleDrafter(cfg.drafter, host_ck["drafter"], host_ck["target"], cfg.mask_token, B, cap)
     rng = np.random.default_rng(5)
     for l in tgt.K:
         tgt.K[l][:ctx] = rng.standard_normal(tgt.K[l][:ctx].shape)
-        tgt.V[l][:ctx] = rng.standard_normal(tgt.V[l][:ctx].shape)
+        tgt.V[l][:ctx] = rng.standard_normal(tgt.V[l][:ctx].shape) * 0.5
     for l in tgt.S:
         tgt.S[l] = rng.standard_normal(tgt.S[l].shape) * 0.1
     for l in range(len(drf.K)):
         drf.K[l][:ctx] = rng.standard_normal(drf.K[l][:ctx].shape)
-        drf.V[l][:ctx] = rng.standard_normal(drf.V[l][:ctx].shape)
+        drf.V[l][:ctx] = rng.standard_normal(drf.V[l][:ctx].shape) * 0.5
     tgt.n = ctx
-    block = list(synth.prompt(cfg, B, seed=9))
-    from oracle.numerics import linear
-    from oracle.model import rmsnorm
+    drf.n_ctx = ctx
+    anchor = int(synth.prompt(cfg, 1, seed=9)[0])
+    t0 = time.time()
+    drafts, _ = drf.draft(anchor, ctx)
+    t_draft = time.time() - t0
+    block = [anchor] + [int(t) for t in drafts]
     t1 = time.time()
-    fwd = tgt.forward(block, layers=1)
-    t_layer = time.time() - t1
-    t1 = time.time()
-    logits = linear(rmsnorm(fwd["x"], ck["target"]["final_norm"], 1e-6), ck["target"]["w_lm"])
-    t_lm = time.time() - t1
-    t1 = time.time()
-    hid = np.tile(fwd["x"], (1, len(cfg.sel_layers)))
-    linear(hid, fc_full)
-    t_fc = time.time() - t1
-    t1 = time.time()
-    drf.draft(int(block[0]), ctx)
-    t_draft1 = time.time() - t1 - t_lm * (B - 1) / B       # draft() includes one lm-head pass
-    step_s = cfg.target.n_layers * t_layer + cfg.drafter.n_layers * max(t_draft1, 0.0) + t_fc + 2 * t_lm
-    import numpy as _np
-    cores = os.cpu_count()
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": (f"1 target layer ({t_layer:.2f} s), 1 drafter pass ({max(t_draft1, 0):.2f} s), fc "
-                       f"({t_fc:.2f} s) and lm-head ({t_lm:.2f} s) of the benchmark step at ctx {ctx} with "
-                       f"seeded random KV, extrapolated to {cfg.target.n_layers}+{cfg.drafter.n_layers} layers; "
-                       f"float64 NumPy, BLAS threads = host cores ({cores}); weight synthesis {gen_s:.1f} s "
-                       f"not timed"),
-            "step_seconds": step_s}
+    fwd = tgt.forward(block)
+    y = argmax_first(fwd["logits"])
+    a = accept_length(drafts, y)
+    tgt.commit(fwd, a)
+    t_verify = time.time() - t1
+    t2 = time.time()
+    drf.ctx_append(fwd["hidden"][: a + 1], ctx + np.arange(a + 1))
+    t_commit = time.time() - t2
+    step_s = time.time() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": round(1.0 / step_s, 5), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": (f"one whole step of the benchmark workload at ctx {ctx} ({step_s:.1f} s: draft "
+                       f"{t_draft:.1f} s, verify + accept {t_verify:.1f} s, commit {t_commit:.1f} s; "
+                       f"a = {a}), float64 NumPy on the GPU model's weights, KV of the committed "
+                       f"context seeded random; BLAS threads {threads}, host cpu_count "
+                       f"{os.cpu_count()}, affinity {len(os.sched_getaffinity(0))}"),
+            "tok_per_s": round((a + 1) / step_s, 4), "step_seconds": round(step_s, 2)}
 
 
 def prefill_gemm_rate(pair, prompt, cfg, ctx):
@@ -238,6 +261,7 @@ def main():
     if args.max_draft:
         pair.set_max_draft(args.max_draft)
         n_drafts = pair.accept_block - 1
+    host_ck = None if args.no_cpu_baseline else host_checkpoint(ck)
     del ck
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -341,7 +365,8 @@ def main():
         gem_ms = sum(r["ms"] for r in kernels)
         gem_bytes = sum(r["bytes"] for r in kernels)
         top = kernels[0]
-        per_launch_bytes = top["bytes"] / top["launches"]
+        per_launch_bytes = top["bytes"] / top["launches"]       # packed weights + scales
+        per_launch_io = top["io_bytes"] / top["launches"]       # activations in, product out
         # the per-launch events above carry a marker gap each; the kernel's own
         # average comes from its recorded launches replayed back to back
         # (weights of every layer in turn, so no cache holds them)
@@ -351,7 +376,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(top["kernel"]),
                 "kernel": top["kernel"], "launches_per_step": top["launches"] / K,
-                "bytes_per_launch": per_launch_bytes, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "bytes_per_launch": per_launch_bytes, "io_bytes_per_launch": per_launch_io,
+                "avg_launch_us": round(avg_ms * 1e3, 2),
                 "avg_launch_us_with_event_markers": round(top["ms"] / top["launches"] * 1e3, 2),
                 "all_gemms_GBps": round(gem_bytes / (gem_ms / 1e3) / 1e9, 1),
                 "gemm_ms_per_step_eager": round(gem_ms / K, 4)}
@@ -363,9 +389,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(cfg, ctx)
+        cpu = cpu_baseline(cfg, ctx, host_ck)
+        del host_ck
         log(f"cpu baseline in {time.time() - t0:.1f} s: {cpu['value']:.5f} steps/s")
-        cpu.pop("step_seconds", None)
 
     fmt_name = {0: "f32", 1: "bf16", 2: "w8a16", 3: "w4a16"}
     out = {

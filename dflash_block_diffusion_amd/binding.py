@@ -19,7 +19,7 @@ DFLASH_OK = 0
 ERRORS = {-1: "INVALID", -2: "SHAPE", -3: "CAPACITY", -4: "DEVICE", -5: "UNSUPPORTED"}
 FMT_F32, FMT_BF16, FMT_W8A16, FMT_W4A16 = 0, 1, 2, 3
 LAYER_ATTN, LAYER_GDN = 0, 1
-STATUS_CAPACITY, STATUS_TOKEN_RANGE = 1, 2
+STATUS_CAPACITY, STATUS_TOKEN_RANGE, STATUS_ACT_RANGE = 1, 2, 4
 
 
 class LayerDesc(Structure):
@@ -81,7 +81,7 @@ SIGNATURES = {
     "dflash_prof_enable": (c_int, [c_void_p, c_int]),
     "dflash_prof_replay": (c_int, [c_void_p, c_char_p, c_int, c_void_p, POINTER(c_double), POINTER(c_int64)]),
     "dflash_prof_read": (c_int, [c_void_p, POINTER(c_char_p), POINTER(c_int64), POINTER(c_double),
-                                 POINTER(c_double), c_int, POINTER(c_int)]),
+                                 POINTER(c_double), POINTER(c_double), c_int, POINTER(c_int)]),
 }
 
 _LIB = None

@@ -263,7 +263,7 @@ extern "C" int dflash_drafter_bind(dflash_model* drafter, const dflash_model* ta
 }
 
 // ------------------------------------------------------------------ state
-struct ProfRec { const char* name; double bytes; hipEvent_t a, b; GemmCall call; };
+struct ProfRec { const char* name; double bytes, io_bytes; hipEvent_t a, b; GemmCall call; };
 
 // Partial sums a GEMM left for the next residual/norm kernel, and where the
 // new residual is to be copied (conditioning layers feed the drafter).
@@ -527,13 +527,14 @@ static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, 
   c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi;
   c.part = s->ws.part; c.out = out; c.otype = otype;
   c.logits = logits; c.ldl = ldl; c.row0 = row0; c.am_out = am_out;
+  c.status = s->scal + SC_STATUS;
   const char* name = nullptr;
-  double bytes = 0;
+  double bytes = 0, io = 0;
   int S = 1;
   hipEvent_t ea = nullptr, eb = nullptr;
   if (s->prof) { ea = take_event(s); eb = take_event(s); hipEventRecord(ea, st); }
-  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes, &S);
-  if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, ea, eb, c}); }
+  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes, &S, &io);
+  if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, io, ea, eb, c}); }
   if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm: ") + hipGetErrorString(e));
   if (parts) *parts = Parts{s->ws.part, S, (size_t)m * W.n, W.n};
   return DFLASH_OK;
@@ -551,6 +552,7 @@ static int norm(dflash_state* s, const dflash_model* m, Pending& pend, const flo
   c.side = pend.side; c.side_type = pend.side_type; c.ld_side = pend.ld_side; c.side_col0 = pend.side_col0;
   c.gain = gain; c.eps = m->d.eps; c.h = m->d.hidden; c.rows = rows;
   c.out = out; c.otype = otype; c.ldo = m->d.hidden; c.tiled = 1;
+  c.status = s->scal + SC_STATUS;
   HIPCHK(launch_norm(c, st));
   pend = Pending{};
   return DFLASH_OK;
@@ -579,6 +581,7 @@ static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer
   ac.dev_n = s->scal + SC_N; ac.block_rows = B; ac.causal = draft ? 0 : 1;
   ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits; ac.npages = s->pages;
   ac.o_part = s->o_part; ac.ml_part = s->ml_part; ac.out = s->ba; ac.otype = m->gin; ac.ldo = hq * hd;
+  ac.status = s->scal + SC_STATUS;
   HIPCHK(launch_attention(ac, st));
   RC(gemm(s, L.o, s->ba, hq * hd, B, EPI_PARTIAL, st, &pend.in));
   return DFLASH_OK;
@@ -610,6 +613,7 @@ static int draft_context(dflash_state* s, hipStream_t st, int side_row0 = 0, int
   c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
   c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = rows;
   c.out = (char*)s->bu + (size_t)B * H * elem_bytes(d->gin); c.otype = d->gin; c.ldo = H; c.tiled = 1;
+  c.status = s->scal + SC_STATUS;
   HIPCHK(launch_norm(c, st));
   return DFLASH_OK;
 }
@@ -692,6 +696,7 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
       gc.S = s->gdn_S + (size_t)g * gh * dvv * dkk;
       gc.tape = s->gdn_tape + (size_t)g * s->B * gh * gdn_rec(t);   // tape rows are laid out per B
       gc.out = s->ba; gc.otype = t->gin; gc.ldo = gh * dvv;
+      gc.status = s->scal + SC_STATUS;
       if (B <= s->B) {
         HIPCHK(launch_gdn_verify(gc, st));
       } else {
@@ -1048,21 +1053,22 @@ extern "C" int dflash_prof_replay(dflash_state* s, const char* variant, int reps
 }
 
 extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* launches, double* ms, double* bytes,
-                                int cap, int* h_n) {
+                                double* io_bytes, int cap, int* h_n) {
   if (!s || !h_n) return fail(DFLASH_E_INVALID, "null argument");
   std::vector<const char*> nm;
   std::vector<int64_t> cnt;
-  std::vector<double> tms, tb;
+  std::vector<double> tms, tb, tio;
   for (auto& r : s->prof_recs) {
     HIPCHK(hipEventSynchronize(r.b));
     float e = 0.f;
     HIPCHK(hipEventElapsedTime(&e, r.a, r.b));
     size_t i = 0;
     while (i < nm.size() && std::strcmp(nm[i], r.name) != 0) ++i;
-    if (i == nm.size()) { nm.push_back(r.name); cnt.push_back(0); tms.push_back(0); tb.push_back(0); }
+    if (i == nm.size()) { nm.push_back(r.name); cnt.push_back(0); tms.push_back(0); tb.push_back(0); tio.push_back(0); }
     cnt[i] += 1;
     tms[i] += e;
     tb[i] += r.bytes;
+    tio[i] += r.io_bytes;
   }
   *h_n = (int)nm.size();
   for (int i = 0; i < (int)nm.size() && i < cap; ++i) {
@@ -1070,6 +1076,7 @@ extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* la
     if (launches) launches[i] = cnt[i];
     if (ms) ms[i] = tms[i];
     if (bytes) bytes[i] = tb[i];
+    if (io_bytes) io_bytes[i] = tio[i];
   }
   return DFLASH_OK;
 }

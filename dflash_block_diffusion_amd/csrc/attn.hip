@@ -369,7 +369,8 @@ constexpr int PF_KEYS = PF_PAGES * PAGE;               // 64 keys
 constexpr int PF_DMAS = 4 * PF_PAGES;                  // K (or V^T) DMAs per wave and stage
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_prefill_kernel(AttnArgs a, void* out,
-                                                                                           int otype, int ldo) {
+                                                                                           int otype, int ldo,
+                                                                                           int32_t* status) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ldsK0[PF_PAGES * 16384];
   __shared__ __attribute__((aligned(16))) uint8_t ldsV0[PF_PAGES * 16384];
@@ -571,20 +572,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      store_act(out, act_index(tok, qh * D + dt * 16 + 4 * g + v, ldo, fmK), otype, o[dt][v] * inv);
+      store_act(out, act_index(tok, qh * D + dt * 16 + 4 * g + v, ldo, fmK), otype, o[dt][v] * inv, status);
 }
 
-// thread are issued before any is consumed (no dependent load chain).
 // ------------------------------------------------------------ combine
 // Merge the per-split partials of one query row: M = max m_s,
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  All split loads of a
+// thread are issued before any is consumed (no dependent load chain).
 
 constexpr int COMBINE_MAX_SPLITS = 32;
 
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
                                                           int max_splits, int B, int hq, int d, void* out, int otype,
-                                                          int ldo) {
+                                                          int ldo, int32_t* status) {
   const int row = blockIdx.x;          // token * hq + qh
   const int tok = row / hq, qh = row % hq;
   const size_t stride = (size_t)B * hq;
@@ -619,8 +620,21 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   // 16-bit outputs feed the O projection: tiled layout with K = hq*d
   const int fmK = otype == T_F32 ? 0 : hq * d;
-  if (e0 < d) store_act(out, act_index(tok, qh * d + e0, ldo, fmK), otype, acc0 * inv);
-  if (e1 < d) store_act(out, act_index(tok, qh * d + e1, ldo, fmK), otype, acc1 * inv);
+  if (e0 < d) store_act(out, act_index(tok, qh * d + e0, ldo, fmK), otype, acc0 * inv, status);
+  if (e1 < d) store_act(out, act_index(tok, qh * d + e1, ldo, fmK), otype, acc1 * inv, status);
+}
+
+// compute units of the current device (looked up once per device)
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
@@ -645,16 +659,20 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
     if (c.block_rows > 64 && c.causal && c.d == 128 && c.npages <= 128) {
       // a prompt chunk: one pass over the keys, normalised output, no combine
-      hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4 * c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo);
+      hipLaunchKernelGGL(attn_prefill_kernel, dim3((nrb + 3) / 4 * c.hkv), dim3(256), 0, s, a, c.out, c.otype, c.ldo,
+                         c.status);
       return hipGetLastError();
     }
     // One work-group fits a CU (128 KiB of LDS).  Eight waves share one K / V^T
-    // staging only when the four-wave grid would spill past the 256 CUs and
-    // the row blocks fill whole groups of eight: with fewer splits, four-wave
-    // work-groups spread the score and P.V work over twice the CUs and are
-    // faster (8B shapes, block 32: 3.38 vs 3.53 ms a step at ctx 64, 4.02 vs
-    // 3.88 ms at ctx 4096).
-    if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > 256)
+    // staging only when the four-wave grid would spill past the device's CUs
+    // and the row blocks fill whole groups of eight: with fewer splits,
+    // four-wave work-groups spread the score and P.V work over twice the CUs
+    // and are faster (8B shapes, block 32: 3.38 vs 3.53 ms a step at ctx 64,
+    // 4.02 vs 3.88 ms at ctx 4096).  The grid is sized by the state's
+    // capacity (max_splits), not by the live context, so that one captured
+    // graph serves every context length: a state whose capacity passes the
+    // threshold runs the eight-wave shape at every length.
+    if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > device_cus())
       hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
@@ -663,7 +681,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
-                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo);
+                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status);
   return hipGetLastError();
 }
 

@@ -63,6 +63,20 @@ __device__ __forceinline__ void store_act(void* p, size_t i, int t, float v) {
 // value the stored element will read back as
 __device__ __forceinline__ float act_round(int t, float v) { return t == T_F32 ? v : round_bf16(v); }
 
+// Status word bit (DFLASH_STATUS_ACT_RANGE): a bf16 activation feeding an
+// fp16 GEMM input lay outside the finite fp16 range (|v| > 65504, where the
+// fp16 encoding reads back as inf) or was NaN.  bf16 values at or below
+// 65280 are finite in fp16; the next bf16 value, 65536, is not.
+constexpr int STATUS_ACT_RANGE = 4;
+__device__ __forceinline__ void flag_f16_range(int t, float v, int32_t* status) {
+  if (t == T_F16 && status && !(fabsf(v) <= 65504.0f)) atomicOr(status, STATUS_ACT_RANGE);
+}
+// store_act that also reports an fp16 range violation to *status (if not null)
+__device__ __forceinline__ void store_act(void* p, size_t i, int t, float v, int32_t* status) {
+  if (t == T_F16) flag_f16_range(t, round_bf16(v), status);
+  store_act(p, i, t, v);
+}
+
 // Fragment-major ("tiled") layout of 16-bit GEMM inputs X[t][k] with K
 // columns: 16-token blocks are outermost and contiguous; inside a block,
 // every 32-column step is one 1 KiB MFMA operand fragment in lane order
@@ -112,6 +126,7 @@ struct GemmCall {
   // ARGMAX
   float* logits; int ldl; int row0;         // optional fp32 logits of rows row0..m-1
   int32_t* am_out;                          // argmax of rows row0..m-1 -> am_out[0..]
+  int32_t* status;                          // SILU: range flag of fp16 outputs (or null)
 };
 
 struct Workspace {
@@ -131,7 +146,7 @@ int dense_splits(int fmt, int n, int k, int m, int epi);
 struct Workspace;
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
-                       double* bytes, int* splits);
+                       double* bytes, int* splits, double* io_bytes = nullptr);
 hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p);
 hipError_t launch_pack(int fmt, int n, int k, int gate_up, const void* src, const void* src_scales,
                        void* dst, void* dst_scales, hipStream_t s);
@@ -205,6 +220,7 @@ struct AttnCall {
   int hq, hkv, d; int max_splits; int npages;  // splits of ATTN_SPLIT keys; pages in the table
   float* o_part; float* ml_part;              // [max_splits][B*hq][d], [max_splits][B*hq][2]
   void* out; int otype; int ldo;              // [B][hq*d]
+  int32_t* status;                            // range flag of fp16 outputs (or null)
 };
 hipError_t launch_attention(const AttnCall& c, hipStream_t s);
 
@@ -237,6 +253,7 @@ struct NormCall {
   void* side; int side_type; int ld_side; int side_col0;   // tiled (K = ld_side) when 16-bit
   const float* gain; float eps; int h; int rows;
   void* out; int otype; int ldo; int tiled;
+  int32_t* status;                          // range flag of fp16 outputs (or null)
 };
 hipError_t launch_norm(const NormCall& c, hipStream_t s);
 hipError_t launch_embed(const void* table, int ttype, int h, int vocab, const int32_t* tokens,
@@ -268,6 +285,7 @@ struct GdnCall {
   const float* S;                            // committed state [gh][dv][dk]
   float* tape;                               // [B][gh][dk+dv+2]
   void* out; int otype; int ldo;             // o [B][gh*dv]
+  int32_t* status;                           // range flag of fp16 outputs (or null)
 };
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s);
 // a prompt chunk of c.rows = nblk * B committed tokens: verify and replay

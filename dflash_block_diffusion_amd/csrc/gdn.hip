@@ -303,7 +303,8 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     const int t = e / RW, il = i0 + e % RW;
     float o = sm.ga[t] * sm.QS[t][il];
     for (int s2 = 0; s2 <= t; ++s2) o = o + sm.Mq[t][s2] * sm.U[s2][il];
-    store_act(c.out, act_index(row0 + t, h * DV + il, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o);
+    store_act(c.out, act_index(row0 + t, h * DV + il, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o,
+              c.status);
   }
 }
 

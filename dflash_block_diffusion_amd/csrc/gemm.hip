@@ -378,7 +378,7 @@ void gemm_stream_kernel(GemmArgs a) {
           // (about 1 ulp each in fp32, before the bf16 rounding below);
           // e^-g = +inf for g << 0 gives g * 0 = -0
           const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
-          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
+          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv, a.status);
         }
       }
     } else {  // EPI_ARGMAX: ascending n within the lane keeps the lowest index on ties
@@ -724,7 +724,7 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
   a.n = W.n; a.k = W.k; a.ktiles = p.ktiles; a.ntile16 = p.ntile16; a.m = c.m; a.splits = p.S; a.align = p.align;
   a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
   a.logits = c.logits; a.ldl = c.ldl; a.row0 = c.row0;
-  a.am_val = w.am_val; a.am_idx = w.am_idx;
+  a.am_val = w.am_val; a.am_idx = w.am_idx; a.status = c.status;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   hipError_t e;
   if (W.fmt == W_BF16) e = dispatch<W_BF16>(p, a, s);
@@ -735,19 +735,21 @@ hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s
 }
 
 hipError_t launch_gemm(const GemmCall& c, const Workspace& w, hipStream_t s, const char** variant,
-                       double* bytes, int* splits) {
+                       double* bytes, int* splits, double* io_bytes) {
   const GemmW& W = *c.W;
   size_t wb, sb;
   packed_bytes(W.fmt, W.n, W.k, &wb, &sb);
-  // algorithmic bytes: packed weights and scales, the bf16 activations read
-  // once, and the product written once in its consumer's type (fp32 sums,
-  // bf16 SiLU rows, or the fp32 logits when they are kept)
-  if (bytes) {
+  // algorithmic bytes: the packed weights and their scales, streamed once
+  if (bytes) *bytes = (double)(wb + sb);
+  // besides them: the 16-bit activations read once and the product written
+  // once in its consumer's type (fp32 sums, bf16 SiLU rows, or the fp32
+  // logits when they are kept)
+  if (io_bytes) {
     double out_b = 0;
     if (c.epi == EPI_PARTIAL) out_b = 4.0 * c.m * W.n;
     else if (c.epi == EPI_SILU) out_b = 2.0 * c.m * (W.n / 2);
     else if (c.logits) out_b = 4.0 * c.m * W.n;
-    *bytes = (double)(wb + sb) + 2.0 * c.m * W.k + out_b;
+    *io_bytes = 2.0 * c.m * W.k + out_b;
   }
   if (W.fmt == W_F32) {
     if (variant) *variant = "gemm_f32";

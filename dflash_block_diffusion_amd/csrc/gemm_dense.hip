@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           const float gv = act_round(rnd, acc[tb][2 * p][v] * sg);
           const float uv = act_round(rnd, acc[tb][2 * p + 1][v] * su);
           const float sv = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * 1.4426950408889634f));
-          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv);
+          store_act(a.out, act_index(t, n_out, 0, half_n), a.otype, sv * uv, a.status);
         }
     }
   }
@@ -327,7 +327,7 @@ hipError_t launch_gemm_dense(const GemmCall& c, const Workspace& w, hipStream_t 
   GemmArgs a{};
   a.w = (const uint8_t*)W.w; a.s = (const uint16_t*)W.s; a.x = (const uint16_t*)c.x;
   a.n = W.n; a.k = W.k; a.ktiles = W.k / tile_k(W.fmt); a.ntile16 = W.n / 16; a.m = c.m; a.splits = S; a.align = 1;
-  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype;
+  a.epi = c.epi; a.part = c.part; a.out = c.out; a.otype = c.otype; a.status = c.status;
   a.mlo = 0x000F000Fu; a.mhi = 0x00F000F0u; a.magic = 0x64006400u;
   const int kt_per = (W.k / 128 + S - 1) / S;
   const dim3 grid(((a.ntile16 + 4 * rw - 1) / (4 * rw)) * ((c.m / 16 + mt - 1) / mt), 1, S);

@@ -52,6 +52,7 @@ struct GemmArgs {
   void* out; int otype;                      // EPI_SILU: tiled [m][n/2] (K = n/2)
   float* logits; int ldl; int row0;          // EPI_ARGMAX
   float* am_val; int* am_idx;                // EPI_ARGMAX: one (value, index) per work-group and token
+  int32_t* status;                           // EPI_SILU: range flag of fp16 outputs (or null)
   // dequant bit masks, passed as arguments so that they live in registers
   // (gfx9 VOP3 encodings take no literal constants)
   uint32_t mlo, mhi, magic;

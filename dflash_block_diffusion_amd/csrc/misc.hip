@@ -12,7 +12,8 @@ namespace dfl {
 // chunks, kept in registers between the reduction and the output, and writes
 // one 16-byte store per chunk (8 consecutive columns are contiguous in the
 // tiled layout as well as in a row-major one).  h % 8 == 0, h <= 8192.
-__device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float (&y)[8]) {
+__device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float (&y)[8],
+                                           int32_t* status = nullptr) {
   if (t == T_F32) {
     float4* q = (float4*)((float*)p + i);
     q[0] = float4{y[0], y[1], y[2], y[3]};
@@ -24,6 +25,8 @@ __device__ __forceinline__ void store8_act(void* p, size_t i, int t, const float
   for (int e = 0; e < 4; ++e) {
     uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
     if (t == T_F16) {
+      flag_f16_range(t, bf16_bits_to_f32(lo), status);
+      flag_f16_range(t, bf16_bits_to_f32(hi), status);
       lo = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(lo));
       hi = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(hi));
     }
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
       if (c.side) {
         const int col = c.side_col0 + j0;
         const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
-        store8_act(c.side, o, c.side_type, v);
+        store8_act(c.side, o, c.side_type, v, c.status);
       }
     }
   }
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] = v[e] * r * g[e];
   const size_t o = fmK ? fm_index(row, j0, fmK) : (size_t)row * c.ldo + j0;
-  store8_act(c.out, o, c.otype, y);
+  store8_act(c.out, o, c.otype, y, c.status);
 }
 
 hipError_t launch_norm(const NormCall& c, hipStream_t s) {

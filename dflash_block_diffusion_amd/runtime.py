@@ -273,10 +273,11 @@ class Pair:
         launches = (c_int64 * cap)()
         ms = (c_double * cap)()
         by = (c_double * cap)()
+        io = (c_double * cap)()
         n = c_int()
-        check(lib().dflash_prof_read(self.st, names, launches, ms, by, cap, byref(n)))
-        return [{"kernel": names[i].decode(), "launches": launches[i], "ms": ms[i], "bytes": by[i]}
-                for i in range(min(n.value, cap))]
+        check(lib().dflash_prof_read(self.st, names, launches, ms, by, io, cap, byref(n)))
+        return [{"kernel": names[i].decode(), "launches": launches[i], "ms": ms[i], "bytes": by[i],
+                 "io_bytes": io[i]} for i in range(min(n.value, cap))]
 
     def prof_replay(self, variant: str, reps: int = 1):
         """Kernel-only time of one GEMM variant's recorded launches, replayed

@@ -65,7 +65,14 @@ enum { DFLASH_LAYER_ATTN = 0, DFLASH_LAYER_GDN = 1 };
 
 enum {                       /* device status word bits */
   DFLASH_STATUS_CAPACITY = 1,    /* a commit would pass the context capacity; it was skipped */
-  DFLASH_STATUS_TOKEN_RANGE = 2  /* a token id outside [0, vocab) was clamped */
+  DFLASH_STATUS_TOKEN_RANGE = 2, /* a token id outside [0, vocab) was clamped */
+  DFLASH_STATUS_ACT_RANGE = 4    /* W8A16 / W4A16 stacks: a bf16 activation feeding an fp16 GEMM
+                                    input (RMSNorm output, residual row of a conditioning layer,
+                                    attention or GatedDeltaNet output, SiLU*mul output) was NaN
+                                    or larger than 65504 in magnitude, where its fp16 encoding is
+                                    inf; the results of that step are not valid.  (Magnitudes
+                                    below 2^-17 are rounded to the fp16 subnormal grid, an
+                                    absolute error of at most 2^-25; they are not flagged.) */
 };
 
 const char *dflash_last_error(void);   /* message of this thread's last failure */
@@ -341,12 +348,14 @@ int dflash_state_buffers(dflash_state *st, dflash_state_view *out);
  * launch stream (eager mode only; never while a graph is being captured).
  * Turning profiling on discards the previous records.
  * dflash_prof_read synchronises and returns per-kernel-variant totals:
- * names[i] (static strings), launches, total milliseconds and algorithmic
- * bytes (packed weights + scales) summed over launches, for up to cap
- * variants; *h_n receives the number of variants. */
+ * names[i] (static strings), launches, total milliseconds, algorithmic
+ * bytes (packed weights + scales, each streamed once) and, apart from
+ * them, io_bytes (the 16-bit activations read once and the product
+ * written once) summed over launches, for up to cap variants; any output
+ * array may be NULL; *h_n receives the number of variants. */
 int dflash_prof_enable(dflash_state *st, int on);
 int dflash_prof_read(dflash_state *st, const char **names, int64_t *launches,
-                     double *ms, double *bytes, int cap, int *h_n);
+                     double *ms, double *bytes, double *io_bytes, int cap, int *h_n);
 
 /* Kernel-only timing of one GEMM variant: re-launches, back to back on
  * `stream`, every launch of that variant recorded since profiling was

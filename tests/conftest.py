@@ -16,6 +16,33 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the HIP C-ABI)")
 
 
+# Parity records: every GPU lockstep appends its measured errors, noise floors
+# and compared / excluded token counts here; the session writes them to
+# gpurun_out/parity_records.json so that the numbers behind each tolerance
+# decision survive the run (pytest itself swallows the test's prints).
+PARITY_RECORDS = []
+CURRENT_TEST = {"id": None}
+
+
+@pytest.fixture(autouse=True)
+def _current_test(request):
+    CURRENT_TEST["id"] = request.node.nodeid
+    yield
+    CURRENT_TEST["id"] = None
+
+
+def record_parity(rec):
+    """Append one record and rewrite the file (a crash mid-session keeps
+    every record written so far)."""
+    rec = dict(rec)
+    rec["test"] = CURRENT_TEST["id"]
+    PARITY_RECORDS.append(rec)
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "parity_records.json"), "w") as f:
+        json.dump(PARITY_RECORDS, f, indent=1)
+
+
 @pytest.fixture(scope="session")
 def hand_cases():
     with open(os.path.join(GOLDEN, "hand_cases.json")) as f:

@@ -135,3 +135,26 @@ def test_linear_rows_beyond_the_limits_are_refused():
     assert L.dflash_linear_workspace_bytes(C.FMT_W8A16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 128) > 0
     assert L.dflash_linear_workspace_bytes(C.FMT_W4A16, 256, 512, 64) > 0
+
+
+def test_fp16_encoding_bound_of_bf16_activations():
+    """The quantised GEMMs read their bf16 activations as fp16 encodings.
+    Over every finite bf16 value: magnitudes up to 65280 (the largest bf16
+    value below the fp16 limit 65504) encode exactly down to 2^-17, with an
+    absolute error of at most 2^-25 below that, and 65536 and up become inf
+    -- the values the status bit DFLASH_STATUS_ACT_RANGE (|v| > 65504 or
+    NaN) reports."""
+    import numpy as np
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    v = v[np.isfinite(v)]
+    h = torch.from_numpy(v).to(torch.float16).float().numpy()
+    a = np.abs(v)
+    ok = a <= 65504.0
+    assert a[ok].max() == 65280.0 and a[~ok].min() == 65536.0
+    assert np.all(np.isinf(h[~ok]))
+    exact = ok & (a >= 2.0 ** -17)
+    assert np.array_equal(h[exact], v[exact])
+    assert np.max(np.abs(h[ok & ~exact] - v[ok & ~exact])) <= 2.0 ** -25
+    assert bn.STATUS_ACT_RANGE == 4

@@ -153,11 +153,14 @@ def test_linear_parity_full_size_sampled(name, fmt, n, k, m):
         assert np.all(np.abs(got - ref) <= bound(x, w, rows=(int(r0), int(r0) + 16))), (name, r0)
 
 
-def test_lm_head_argmax_full_size():
-    # 8B-class lm-head: 151936 x 4096 int4, every row's argmax (near ties excluded)
+@pytest.mark.parametrize("m", [8, 32])
+def test_lm_head_argmax_full_size(m):
+    # 8B-class lm-head: 151936 x 4096 int4, every row's argmax (near ties
+    # excluded); 32 rows is the verify of a 32-token block (the launch shape
+    # of the step: two 16-row token blocks on 512 work-groups)
     g = synth.HostSynth(21)
     w = g.weight("lm_full", 151936, 4096, C.FMT_W4A16)
-    x = x_values(np.random.default_rng(22), 8, 4096, C.FMT_W4A16)
+    x = x_values(np.random.default_rng(22), m, 4096, C.FMT_W4A16)
     logits, am, _ = run_linear(w, x, C.FMT_W4A16, epilogue=1)
     ref = linear(x, w)
     assert np.max(np.abs(logits - ref) / (bound(x, w))) <= 1.0

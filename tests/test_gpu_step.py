@@ -4,24 +4,28 @@ oracle, in lockstep on the same seeded models and the same committed tokens.
 Per step both sides draft from the same committed context; both then verify
 the GPU's (possibly injected) block; the oracle commits the GPU's accepted
 count so the two stay on one token stream.  Compared:
-  * draft tokens d_1..d_{B-1}, verify argmax y_0..y_{B-1}, accepted count a:
-    bit-exact, except positions whose oracle top-2 logit margin is below
-    max(1e-2, 2 x the step's logit noise floor) -- a margin smaller than the
-    logit error bound cannot decide the argmax (excluded and counted; a is
-    compared when no excluded y lies in 0..a);
-  * logits: max |err| <= 1e-4 (fp32 models) / 2e-2 (bf16 models), or twice
-    the bf16 noise floor when that is larger;
-  * conditioning-layer hidden states: max |err| <= 1e-4 (fp32) or
-    2e-2 + 2^-7 max|ref| (bf16: the absolute bound plus one bf16 rounding step
-    of the largest value), or twice the noise floor when that is larger.
+  * draft tokens d_1..d_{B-1} and verify argmax y_0..y_{B-1}: positions whose
+    oracle top-2 logit margin is below 1e-2 are excluded and counted; every
+    other position must give the oracle's token, except where the margin is
+    also below twice the measured noise floor -- there the GPU's token must
+    be a valid near-tie choice (its oracle logit within 2 x floor of the
+    maximum), and those positions are counted.  At least 90 % of all
+    positions are compared.  The accepted count a is compared when no
+    position in 0..a lies below max(1e-2, 2 x floor);
+  * logits and conditioning-layer hidden states: max |err| <= 1e-4 (fp32
+    models) / 2e-2 (bf16 models), or twice the noise floor when that is
+    larger.
 The noise floor is measured in the same run: a second oracle whose GEMMs
 accumulate in float32 instead of float64 runs in lockstep, and its distance
 from the float64 oracle is how far two valid evaluations of the same bf16
 model drift apart (one differing bf16 rounding cascades through every later
-materialisation point).  Token comparisons always use the float64 oracle.
-Depth-reduced configurations keep the real widths (hidden, heads, FFN,
-formats) with 2 target layers, 1 drafter layer and a 32768-token vocab;
-the full vocab lm-head is covered in test_gpu_linear.
+materialisation point).  For the bf16 stacks it is 3.5e-2 to 6.2e-2 in the
+logits and one bf16 step of the largest hidden value (0.0625 to 0.25), above
+the 2e-2 bound; for fp32 models it is about 1e-6.  Every lockstep writes its
+errors, floors and counts to gpurun_out/parity_records.json.  Token
+comparisons always use the float64 oracle.  Depth-reduced configurations
+keep the real widths (hidden, heads, FFN, formats) with 2 target layers, 1
+drafter layer and a 32768-token vocab; one test runs the whole 8B-class pair.
 """
 from dataclasses import replace
 
@@ -30,6 +34,7 @@ import pytest
 import torch
 
 from dflash_block_diffusion_amd import configs as C
+from dflash_block_diffusion_amd import binding as bn
 from dflash_block_diffusion_amd import synth
 from dflash_block_diffusion_amd.runtime import Pair
 from oracle.gdn import replay_pinned
@@ -37,7 +42,7 @@ from oracle.model import argmax_first, top2_margin
 from oracle.numerics import gemm_accumulation
 from oracle.spec import OraclePair, accept_length, greedy
 
-from conftest import tiny_hybrid_config
+from conftest import record_parity, tiny_hybrid_config
 
 pytestmark = pytest.mark.gpu
 TIE = 1e-2
@@ -49,10 +54,7 @@ def tol_logits(cfg):
 
 def check_hidden(cfg, got, ref, floor):
     err = np.max(np.abs(got - ref))
-    if cfg.drafter.fmt == C.FMT_F32:
-        assert err <= max(1e-4, 2 * floor)
-    else:
-        assert err <= max(2e-2 + 2.0 ** -7 * np.max(np.abs(ref)), 2 * floor), err
+    assert err <= max(tol_logits(cfg), 2 * floor), (err, floor)
 
 
 def reduced(name, layers=2, vocab=32768):
@@ -60,11 +62,55 @@ def reduced(name, layers=2, vocab=32768):
     return replace(cfg, target=replace(cfg.target, vocab=vocab), drafter=replace(cfg.drafter, vocab=vocab))
 
 
-def compare_tokens(got, ref, margin, stats, floor=0.0):
-    ok = margin >= max(TIE, 2 * floor)
-    stats["excluded"] += int((~ok).sum())
-    stats["compared"] += int(ok.sum())
-    assert np.array_equal(np.asarray(got)[ok], np.asarray(ref)[ok]), (got, ref, margin)
+def compare_tokens(got, ref, margin, stats, floor=0.0, ref_logits=None):
+    """Token ids against the oracle's argmax.  Positions whose oracle top-2
+    margin is below 1e-2 are excluded and counted.  Every other position is
+    compared: the token must equal the oracle's, except where the margin is
+    also below twice the measured noise floor (two valid evaluations of the
+    model disagree by that much); there the GPU's token must be a valid
+    near-tie choice -- its oracle logit within 2 x floor of the maximum --
+    and such positions are counted as band mismatches."""
+    got, ref, margin = np.asarray(got), np.asarray(ref), np.asarray(margin, dtype=np.float64)
+    compared = margin >= TIE
+    exact = got == ref
+    band = compared & (margin < 2 * floor)
+    stats["positions"] += int(margin.size)
+    stats["compared"] += int(compared.sum())
+    stats["excluded"] += int((~compared).sum())
+    stats["band"] += int(band.sum())
+    miss = compared & ~exact
+    stats["band_mismatch"] += int(miss.sum())
+    if miss.any():
+        assert ref_logits is not None and np.all(band[miss]), (got, ref, margin, floor)
+        lg = np.asarray(ref_logits, dtype=np.float64).reshape(len(got), -1)
+        rows = np.nonzero(miss)[0]
+        gap = lg[rows].max(axis=1) - lg[rows, got[rows]]
+        assert np.all(gap <= 2 * floor), (rows, gap, floor)
+
+
+def new_stats():
+    return {"positions": 0, "compared": 0, "excluded": 0, "band": 0,
+            "band_mismatch": 0, "draft_err": 0.0, "draft_floor": 0.0, "verify_err": 0.0,
+            "verify_floor": 0.0, "hidden_err": 0.0, "hidden_floor": 0.0, "hidden_absmax": 0.0,
+            "a_compared": 0, "steps": 0}
+
+
+def finish_stats(cfg, P, stats, extra=None):
+    """Record the lockstep's numbers (gpurun_out/parity_records.json) and
+    check the compared fraction."""
+    tl = tol_logits(cfg)
+    rec = dict(stats, config=cfg.name, prompt=P, tol=tl,
+               logits_within_tol=bool(max(stats["draft_err"], stats["verify_err"]) <= tl),
+               hidden_within_tol=bool(stats["hidden_err"] <= tl))
+    if extra:
+        rec.update(extra)
+    record_parity(rec)
+    print(f"[{cfg.name}] {rec}", flush=True)
+    assert stats["compared"] >= 0.9 * stats["positions"], stats
+
+
+def progress(cfg, msg):
+    print(f"[{cfg.name}] {msg}", flush=True)
 
 
 def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
@@ -72,6 +118,7 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
     max_draft > 0 both sides verify only the first max_draft drafts."""
     B, V = cfg.block, cfg.target.vocab
     ck = synth.make_pair(cfg)
+    progress(cfg, f"checkpoint ready, prompt {P}, {len(forced)} steps")
     prompt = synth.prompt(cfg, P)
     max_ctx = max_ctx or P + (len(forced) + 4) * B + 64
     pair = Pair(cfg, ck, max_ctx=max_ctx)
@@ -93,18 +140,21 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
     pair.rollback(P)
     if gdn_exact:
         tapes = tapes[:1]
+    progress(cfg, f"GPU prefill and reference stream done (n {nref})")
     op = OraclePair(cfg, ck, cap=max_ctx + 2 * B, max_draft=max_draft)
     op.prefill(prompt)
+    progress(cfg, "oracle prefill done")
     op32 = OraclePair(cfg, ck, cap=max_ctx + 2 * B, max_draft=max_draft)
     N = op.N                                    # drafts verified per step
     with gemm_accumulation("f32"):
         op32.prefill(prompt)
     op32.anchor = first
-    stats = {"excluded": 0, "compared": 0}
+    progress(cfg, "fp32-accumulated oracle prefill done")
+    stats = new_stats()
     # the first token: excluded as a near tie below the same noise floor the
     # steps use (float64 against fp32-accumulated oracle logits)
     pfloor = float(np.max(np.abs(op32.prefill_logits - op.prefill_logits)))
-    compare_tokens([first], [op.anchor], np.array([op.prefill_margin]), stats, pfloor)
+    compare_tokens([first], [op.anchor], np.array([op.prefill_margin]), stats, pfloor, op.prefill_logits)
     op.anchor = first
     dlog = torch.empty(B - 1, V, device="cuda")
     vlog = torch.empty(B, V, device="cuda")
@@ -128,8 +178,9 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
             _, dl_32 = op32.d.draft(op32.anchor, n)
         derr = float(np.max(np.abs(dlog.cpu().numpy() - dl_o)))
         dfloor = float(np.max(np.abs(dl_32 - dl_o)))
-        compare_tokens(raw, d_o, top2_margin(dl_o), stats, dfloor)
-        print(f"[{cfg.name} step {s}] draft logits max err {derr:.3e} (noise floor {dfloor:.3e})", flush=True)
+        compare_tokens(raw, d_o, top2_margin(dl_o), stats, dfloor, dl_o)
+        stats["draft_err"] = max(stats["draft_err"], derr)
+        stats["draft_floor"] = max(stats["draft_floor"], dfloor)
         assert derr <= max(tl, 2 * dfloor)
         sched.fill_(int(k))
         pair.inject(ref, sched, fill[s:s + 1].contiguous())
@@ -142,12 +193,15 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
         vm = top2_margin(fwd["logits"])
         verr = float(np.max(np.abs(vlog[:N + 1].cpu().numpy() - fwd["logits"])))
         vfloor = float(np.max(np.abs(fwd32["logits"] - fwd["logits"])))
-        compare_tokens(y, argmax_first(fwd["logits"]), vm, stats, vfloor)
+        compare_tokens(y, argmax_first(fwd["logits"]), vm, stats, vfloor, fwd["logits"])
         herr = float(np.max(np.abs(pair.side()[:N + 1].cpu().numpy() - fwd["hidden"])))
         hfloor = float(np.max(np.abs(fwd32["hidden"] - fwd["hidden"])))
-        print(f"[{cfg.name} step {s}] verify logits max err {verr:.3e} (floor {vfloor:.3e}), hidden max err "
-              f"{herr:.3e} (floor {hfloor:.3e}, |hidden| max {np.max(np.abs(fwd['hidden'])):.2f}), "
-              f"a={int(pair.acc.item())}", flush=True)
+        stats["verify_err"] = max(stats["verify_err"], verr)
+        stats["verify_floor"] = max(stats["verify_floor"], vfloor)
+        stats["hidden_err"] = max(stats["hidden_err"], herr)
+        stats["hidden_floor"] = max(stats["hidden_floor"], hfloor)
+        stats["hidden_absmax"] = max(stats["hidden_absmax"], float(np.max(np.abs(fwd["hidden"]))))
+        stats["steps"] += 1
         assert verr <= max(tl, 2 * vfloor)
         check_hidden(cfg, pair.side()[:N + 1].cpu().numpy(), fwd["hidden"], hfloor)
         pair.accept()
@@ -155,6 +209,7 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
         a = int(pair.acc.item())
         a_o = accept_length(block[1:], argmax_first(fwd["logits"]))
         if np.all(vm[:max(a, a_o) + 1] >= max(TIE, 2 * vfloor)):
+            stats["a_compared"] += 1
             assert a == a_o
             if on_ref:
                 assert a == min(k, N), "injected acceptance not realised"
@@ -171,10 +226,10 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
         op32.anchor = int(y[a])
         nn = pair.query()["n"]
         on_ref = on_ref and torch.equal(pair.tokens(nn + 1).cpu(), ref[:nn + 1].cpu())
+        progress(cfg, f"step {s} done: a {a}, n {nn}")
     q = pair.query()
     assert q["n"] == op.t.n and q["status"] == 0
-    print(f"[{cfg.name}] tokens compared {stats['compared']}, excluded as undecidable {stats['excluded']}",
-          flush=True)
+    finish_stats(cfg, P, stats, {"max_ctx": max_ctx, "max_draft": max_draft, "n_end": int(q["n"])})
     return pair, op, stats, tapes
 
 
@@ -267,6 +322,60 @@ def test_reduced_4b_dense_prompt_chunks_lockstep(P):
     cfg = reduced("4b")
     _, _, stats, _ = lockstep(cfg, P, [0, 15, 6])
     assert stats["compared"] >= 3 * cfg.block
+
+
+@pytest.mark.parametrize("P,forced", [(2048, [0, 31, 9]), (4096, [31, 5, 17])])
+def test_reduced_8b_lockstep_benchmark_contexts(P, forced):
+    # the benchmark's committed contexts (mirror-sd README, "Results":
+    # contexts 64 / 2048 / 4096 at block 32).  2048: a 2336-token cache, ten
+    # 256-key splits on the four-wave block attention, nine or ten of them
+    # live; 4096: a 4384-token cache, 18 splits x 8 KV heads x 2 row groups
+    # pass 256 work-groups, so the eight-wave instance runs with 16-17 live
+    # splits and the combine merges all of them
+    cfg = reduced("8b")
+    lockstep(cfg, P, forced)
+
+
+def test_reduced_27b_lockstep_ctx2048():
+    # 40 / 8 heads: five query heads per KV head, 160 query rows a KV head
+    # at block 32, ten 16-row blocks in three four-wave groups (the last
+    # holding two), over nine or ten live key splits
+    cfg = reduced("27b")
+    lockstep(cfg, 2048, [0, 31, 12])
+
+
+@pytest.mark.parametrize("name,layers", [("4b", 2), ("hybrid", 4)])
+def test_reduced_block16_lockstep_ctx2048(name, layers):
+    # block 16 at the 2048-token context of the 4B and hybrid workloads; the
+    # hybrid's 2048-token prompt runs two 1024-row chunks, 128 GatedDeltaNet
+    # blocks in turn
+    cfg = reduced(name, layers=layers)
+    lockstep(cfg, 2048, [0, 15, 6])
+
+
+def test_full_depth_8b_lockstep_ctx64():
+    # the whole 8B-class pair: 36 int4 target layers, 5 int8 drafter layers,
+    # the 151936-token vocabulary, block 32; measures the bf16 drift of a
+    # full-depth stack against the oracle and its noise floor
+    cfg = C.qwen8b()
+    lockstep(cfg, 64, [31, 9])
+
+
+def test_fp16_range_flag_reports_oversized_activations():
+    # a norm gain of 3e4 makes the RMSNorm output, an fp16 GEMM input of the
+    # int4 target, pass 65504: the status word reports it; the same model
+    # with unit gains leaves the bit clear (and so does every lockstep above)
+    cfg = reduced("8b")
+    ck = synth.make_pair(cfg)
+    prompt = synth.prompt(cfg, 40)
+    pair = Pair(cfg, ck, max_ctx=256)
+    pair.prefill(prompt)
+    pair.step()
+    assert pair.query()["status"] == 0
+    ck["target"]["layers"][1]["in_norm"] = np.full(cfg.target.hidden, 3e4, np.float32)
+    big = Pair(cfg, ck, max_ctx=256)
+    big.prefill(prompt)
+    assert big.query()["status"] & bn.STATUS_ACT_RANGE
 
 
 def test_rollback_replays_identically():
