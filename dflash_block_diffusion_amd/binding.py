@@ -55,6 +55,9 @@ SIGNATURES = {
     "dflash_linear_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "dflash_linear": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dflash_linear_noalloc_scratch_bytes": (c_size_t, []),
+    "dflash_linear_noalloc": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p]),
     "dflash_model_create": (c_int, [POINTER(ModelDesc), POINTER(c_void_p)]),
     "dflash_model_destroy": (None, [c_void_p]),
     "dflash_drafter_bind": (c_int, [c_void_p, c_void_p]),

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -114,20 +115,28 @@ extern "C" size_t dflash_linear_workspace_bytes(int fmt, int n, int k, int m) {
   return linear_ws_layout(fmt, n, k, m).total;
 }
 
-extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx, int m,
-                             int epilogue, float* out, int32_t* am, void* ws, size_t ws_bytes, void* stream) {
+// argument checks shared by dflash_linear and dflash_linear_noalloc (the
+// workspace is checked by the caller)
+static int linear_check(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx, int m,
+                        int epilogue, float* out, int32_t* am) {
   if (!fmt_ok(fmt)) return fail(DFLASH_E_INVALID, "unknown weight format");
   int rc = check_gemm_shape(fmt, n, k, 0);
   if (rc) return rc;
   if (!linear_rows_ok(fmt, n, k, m, epilogue))
     return fail(DFLASH_E_SHAPE, "m must be in [1, 64] (or, BF16/W8A16/W4A16 with epilogue 0, a multiple of 16 up to 1024)");
   if (fmt == DFLASH_FMT_F32 && ldx < k) return fail(DFLASH_E_SHAPE, "ldx must be >= k");
-  if (!w || !x || !ws || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
+  if (!w || !x || (fmt >= DFLASH_FMT_W8A16 && !sc)) return fail(DFLASH_E_INVALID, "null argument");
   if (epilogue == 0 && !out) return fail(DFLASH_E_INVALID, "epilogue 0 needs d_out");
   if (epilogue == 1 && !am) return fail(DFLASH_E_INVALID, "epilogue 1 needs d_argmax");
   if (epilogue != 0 && epilogue != 1) return fail(DFLASH_E_INVALID, "unknown epilogue");
+  return DFLASH_OK;
+}
+
+// enqueue one checked linear with its workspace at ws (device memory of at
+// least linear_ws_layout(...).total bytes)
+static int linear_run(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx, int m,
+                      int epilogue, float* out, int32_t* am, void* ws, void* stream) {
   const LinearWs L = linear_ws_layout(fmt, n, k, m);
-  if (ws_bytes < L.total) return fail(DFLASH_E_INVALID, "workspace too small");
   char* b = (char*)ws;
   Workspace W;
   W.part = (float*)(b + L.part_off); W.part_floats = L.part_floats;
@@ -144,6 +153,60 @@ extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* s
   HIPCHK(launch_gemm(c, W, (hipStream_t)stream, nullptr, nullptr, &S));
   if (epilogue == 0) HIPCHK(launch_sum_parts(W.part, S, (size_t)m * n, out, (hipStream_t)stream));
   return DFLASH_OK;
+}
+
+extern "C" int dflash_linear(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx, int m,
+                             int epilogue, float* out, int32_t* am, void* ws, size_t ws_bytes, void* stream) {
+  int rc = linear_check(fmt, n, k, w, sc, x, ldx, m, epilogue, out, am);
+  if (rc) return rc;
+  if (!ws) return fail(DFLASH_E_INVALID, "null workspace");
+  if (ws_bytes < linear_ws_layout(fmt, n, k, m).total) return fail(DFLASH_E_INVALID, "workspace too small");
+  return linear_run(fmt, n, k, w, sc, x, ldx, m, epilogue, out, am, ws, stream);
+}
+
+// ------------------------------------------------------------ static scratch
+// Workspace of dflash_linear_noalloc: a file-scope device array, one copy per
+// device, resident until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device (with that device current) by hipGetSymbolAddress and only
+// that address is handed to kernels.  Nothing in it has to start at zero:
+// every call writes the split partials and argmax partials it then reads.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[NOALLOC_MAX_DEVICES] = {nullptr};
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(DFLASH_E_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DFLASH_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return DFLASH_OK;
+}
+
+extern "C" size_t dflash_linear_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int dflash_linear_noalloc(int fmt, int n, int k, const void* w, const void* sc, const void* x, int ldx,
+                                     int m, int epilogue, float* out, int32_t* am, void* stream) {
+  int rc = linear_check(fmt, n, k, w, sc, x, ldx, m, epilogue, out, am);
+  if (rc) return rc;
+  const size_t need = linear_ws_layout(fmt, n, k, m).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(DFLASH_E_CAPACITY, "this linear needs " + std::to_string(need) + " bytes of workspace; the static "
+                "scratch holds " + std::to_string(NOALLOC_SCRATCH_BYTES) + " (use dflash_linear with a workspace)");
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return linear_run(fmt, n, k, w, sc, x, ldx, m, epilogue, out, am, ws, stream);
 }
 
 // ------------------------------------------------------------------ models

@@ -128,6 +128,23 @@ int dflash_linear(int fmt, int n, int k, const void *d_w, const void *d_s, const
                   int m, int epilogue, float *d_out, int32_t *d_argmax, void *d_ws, size_t ws_bytes,
                   void *stream);
 
+/* dflash_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same GEMM with the same kernels and results, but its workspace is a
+ * static device array of the library, one per device, allocated when the
+ * library's code is loaded on that device and held until the process ends.
+ * The call allocates nothing and takes no workspace argument; it runs on the
+ * current device (the caller's stream must belong to it).
+ * dflash_linear_noalloc_scratch_bytes() is the array's size (64 MiB); a
+ * call whose workspace (dflash_linear_workspace_bytes) is larger fails with
+ * DFLASH_E_CAPACITY before any launch.  Every call on one device uses that
+ * device's array: calls that overlap on one device (other streams, other
+ * threads) race and give wrong results; calls in stream order do not.
+ * Arguments and errors otherwise as dflash_linear. */
+size_t dflash_linear_noalloc_scratch_bytes(void);
+int dflash_linear_noalloc(int fmt, int n, int k, const void *d_w, const void *d_s, const void *d_x, int ldx,
+                          int m, int epilogue, float *d_out, int32_t *d_argmax, void *stream);
+
 /* ------------------------------------------------------------- models */
 typedef struct {
   int kind;                         /* DFLASH_LAYER_ATTN or DFLASH_LAYER_GDN */
