@@ -181,6 +181,35 @@ def cpu_baseline(cfg, ctx, host_ck):
             "tok_per_s": round((a + 1) / step_s, 4), "step_seconds": round(step_s, 2)}
 
 
+def read_floor(variant, bytes_per_launch, achieved):
+    """What a launch of the dominant kernel's size and grid can reach at all:
+    the same bytes read by a read-only kernel on the same number of
+    work-groups (dflash_read_floor), launched back to back over copies
+    that together exceed the last-level cache, timed like the kernel."""
+    import re
+    import torch
+    from ctypes import byref, c_double
+    from dflash_block_diffusion_amd import binding as bn
+    from dflash_block_diffusion_amd.runtime import stream_handle
+    m = re.search(r"_g(\d+)$", variant)
+    nwg = int(m.group(1)) if m else 256
+    nb = int(bytes_per_launch) // 16 * 16
+    copies = max(36, (640 << 20) // nb + 1)
+    buf = torch.ones(copies * nb // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(nwg, dtype=torch.int32, device="cuda")
+    ms = c_double()
+    bn.check(bn.lib().dflash_read_floor(buf.data_ptr(), nb, copies, nwg, 3, sink.data_ptr(), stream_handle(),
+                                        byref(ms)))
+    us = ms.value * 1e3 / (copies * 3)
+    gbs = nb / (us * 1e-6) / 1e9
+    del buf
+    log(f"read floor of {nb / 1e6:.2f} MB on {nwg} work-groups: {us:.2f} us, {gbs:.0f} GB/s")
+    return {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(us, 2),
+            "kernel_frac_of_floor": round(achieved / gbs, 4),
+            "what": "the same bytes per launch read by a kernel that only streams them (16-byte loads), "
+                    "on the same work-group count, back to back over copies exceeding the last-level cache"}
+
+
 def prefill_gemm_rate(pair, prompt, cfg, ctx):
     """MFMA throughput of the prompt pass's dense GEMMs: one profiled prompt
     pass records every launch; the dense ones are replayed back to back
@@ -381,6 +410,7 @@ def main():
                 "avg_launch_us_with_event_markers": round(top["ms"] / top["launches"] * 1e3, 2),
                 "all_gemms_GBps": round(gem_bytes / (gem_ms / 1e3) / 1e9, 1),
                 "gemm_ms_per_step_eager": round(gem_ms / K, 4)}
+        roof["read_floor"] = read_floor(top["kernel"], per_launch_bytes, achieved)
         for r in kernels:
             log(f"  {r['kernel']:18s} launches/step {r['launches'] / K:6.1f}  avg {r['ms'] / r['launches'] * 1e3:8.2f} us"
                 f"  {r['bytes'] / r['launches'] / 1e6:8.2f} MB/launch  "

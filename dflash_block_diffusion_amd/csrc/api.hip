@@ -1115,6 +1115,32 @@ extern "C" int dflash_prof_replay(dflash_state* s, const char* variant, int reps
   return DFLASH_OK;
 }
 
+namespace dfl {
+hipError_t launch_read_floor(const void* buf, size_t bytes, int nwg, uint32_t* sink, hipStream_t s);
+}
+
+extern "C" int dflash_read_floor(const void* d_buf, size_t bytes, int copies, int nwg, int reps, uint32_t* d_sink,
+                                 void* stream, double* h_ms) {
+  if (!d_buf || !d_sink || !h_ms || copies < 1 || reps < 1 || nwg < 1 || nwg > 65536 || bytes == 0 || bytes % 16)
+    return fail(DFLASH_E_INVALID, "bad argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t ea, eb;
+  HIPCHK(hipEventCreate(&ea));
+  HIPCHK(hipEventCreate(&eb));
+  HIPCHK(launch_read_floor(d_buf, bytes, nwg, d_sink, st));           // warm-up launch
+  HIPCHK(hipEventRecord(ea, st));
+  for (int r = 0; r < reps; ++r)
+    for (int c = 0; c < copies; ++c) HIPCHK(launch_read_floor((const char*)d_buf + (size_t)c * bytes, bytes, nwg, d_sink, st));
+  HIPCHK(hipEventRecord(eb, st));
+  HIPCHK(hipEventSynchronize(eb));
+  float ms = 0.f;
+  HIPCHK(hipEventElapsedTime(&ms, ea, eb));
+  hipEventDestroy(ea);
+  hipEventDestroy(eb);
+  *h_ms = ms;
+  return DFLASH_OK;
+}
+
 extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* launches, double* ms, double* bytes,
                                 double* io_bytes, int cap, int* h_n) {
   if (!s || !h_n) return fail(DFLASH_E_INVALID, "null argument");

@@ -304,4 +304,35 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t count, hipStream
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ read floor
+// The bytes of one weight-streaming launch, read by a kernel that does
+// nothing else: each work-group reads a contiguous share with 16-byte
+// non-temporal loads, eight in flight per lane.  It measures what a launch
+// of that size and grid can reach at all on this part; the sink is written
+// only if the data's XOR equals a value it never takes.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_floor_kernel(const u32x4_t* __restrict__ w, size_t n16,
+                                                         uint32_t* sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b = blockIdx.x * per, e = min(n16, b + per);
+  uint32_t acc = 0;
+  for (size_t i = b + threadIdx.x; i < e; i += 256 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t j = i + 256 * u;
+      v[u] = j < e ? __builtin_nontemporal_load(w + j) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u && threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+hipError_t launch_read_floor(const void* buf, size_t bytes, int nwg, uint32_t* sink, hipStream_t s) {
+  if (nwg < 1 || bytes % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_floor_kernel, dim3(nwg), dim3(256), 0, s, (const u32x4_t*)buf, bytes / 16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace dfl

@@ -388,6 +388,19 @@ int dflash_prof_read(dflash_state *st, const char **names, int64_t *launches,
 int dflash_prof_replay(dflash_state *st, const char *variant, int reps,
                        void *stream, double *h_ms, int64_t *h_launches);
 
+/* What a weight-streaming launch of a given size and grid can reach at all:
+ * reads `copies` consecutive regions of `bytes` each (d_buf holds copies *
+ * bytes, bytes % 16 == 0; use more than the 256 MiB last-level cache in
+ * total), one launch of nwg work-groups per region and nothing else (16-byte
+ * non-temporal loads, no arithmetic on the data), the whole series `reps`
+ * times back to back on `stream` after one warm-up launch; *h_ms receives
+ * the total milliseconds of the copies * reps launches.  d_sink holds nwg
+ * uint32 (written only in a case the data never produces).  Synchronises
+ * the stream.  Errors: DFLASH_E_INVALID for a bad argument, DFLASH_E_DEVICE
+ * if a launch fails. */
+int dflash_read_floor(const void *d_buf, size_t bytes, int copies, int nwg, int reps, uint32_t *d_sink,
+                      void *stream, double *h_ms);
+
 #ifdef __cplusplus
 }
 #endif

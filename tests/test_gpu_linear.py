@@ -67,7 +67,7 @@ FMTS = [C.FMT_F32, C.FMT_BF16, C.FMT_W8A16, C.FMT_W4A16]
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k,m", [(48, 256, 16), (80, 384, 17), (1040, 512, 32), (272, 4096, 33),
-                                   (1024, 4096, 64), (64, 1024, 1)])
+                                   (1024, 4096, 64), (64, 1024, 1), (6128, 4096, 32)])
 def test_linear_parity_small(fmt, n, k, m):
     # spans several row tiles, ragged row blocks (N/16 not a multiple of the
     # tile group), ragged token blocks (m not a multiple of 16) and split-K
