@@ -109,14 +109,32 @@ constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
 
 
 
-// round-to-nearest-even to bf16 of a finite value (softmax weights), branch-free
-__device__ __forceinline__ uint32_t bf16_bits_finite(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// 16 bytes per lane from sbase + voff to LDS at lds + 16 * lane.  The base
+// and the LDS offset are wave-uniform (page bases read with readlane, the
+// work-group's LDS buffers, the scalar wave index), so they stay in SGPRs and
+// a load costs no vector address arithmetic.  Issued from asm (untracked by
+// the compiler's wait analysis); callers wait with explicit vmcnt waits.
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ float round_bf16_finite(float f) { return __uint_as_float(bf16_bits_finite(f) << 16); }
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  return bf16_bits_finite(lo) | (bf16_bits_finite(hi) << 16);
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sgpr_ptr(sbase)),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+
+// K page granule swizzle: key bits 0-1 and 3-4, so that the 16 keys
+// {8a + 4h + b : a, b < 4} that one score tile reads (h fixed) fall in 16
+// different bank groups
+__device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
+
+// two fp32 values rounded to nearest-even bf16, packed (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float floatx2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){lo, hi}, bf16x2v));
 }
 
 // head_dim 128, bf16 q/k/v.  Work-group = (split of 256 keys, KV head, group
@@ -126,12 +144,15 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 //     direct global->LDS 16-byte loads (128 KiB in flight per work-group, no
 //     registers held).  16-byte granules are XOR-swizzled inside each row so
 //     that the fragment reads below hit 16 different bank groups:
-//       K page  granule (key, c = d/8)    at key*16 + (c ^ (key & 15))
+//       K page  granule (key, c = d/8)    at key*16 + (c ^ kswz(key))
 //       V^T page granule (d, c = key/8)   at d*8 + (c ^ ((d >> 1) & 7))
 //  2. S^T = K Q^T over the whole split (a lane holds 4 keys of one row per
-//     16-key tile), row max and exp2 in one pass, P^T fed to O^T = V^T P^T
-//     as the B operand.  Softmax weights stay fp32: each p enters the MFMA as
-//     p_hi + p_lo, two bf16 values whose sum carries 16 significant bits.
+//     16-key tile, tiles ordered so that a lane's 8 keys of a 32-key P.V
+//     step are consecutive), the row max on the raw scores, then
+//     p = exp2(s * scale*log2e - m) in one fma + exp per score.  Softmax
+//     weights stay fp32: each p enters the MFMA as p_hi + p_lo, two bf16
+//     values whose sum carries 16 significant bits (p_hi = p truncated,
+//     p_lo = the exact remainder rounded to nearest), O^T = V^T P^T.
 //  3. Unnormalised partial (o, max, sum) per row; attn_combine merges the
 //     splits.
 // NW waves per work-group (4 or 8): with 8, one staging of a split's K / V^T
@@ -142,28 +163,23 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int BPW = 16 / NW;                 // 1 KiB DMA blocks per page and wave
   constexpr int DMAS = BPW * ATTN_PAGES;       // V^T DMAs per wave (and K DMAs)
+  constexpr int NT = ATTN_SPLIT / 16;          // 16-key tiles per split
   // K and V^T staging as two LDS objects, so that waiting for the K loads
   // does not also wait for the V^T loads
   __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
   __shared__ __attribute__((aligned(16))) uint8_t ldsV[ATTN_PAGES * 16384];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
   const int h = blockIdx.y, sidx = blockIdx.x;
   const int key0 = sidx * ATTN_SPLIT;
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
 
-  // 1. stage K / V^T of the split (pages past the table re-read the last one;
-  //    their keys are masked below, and the arena holds finite values).  The
-  //    page indices and q are read together with the committed length, so
-  //    that no load waits on another; a split past the keys then leaves.
-  // (one vector load for the split's page indices: scalar loads of them
-  // would each wait for the previous one)
+  // 1. the split's page indices (one vector load: scalar loads of them would
+  //    each wait for the previous one), this wave's q fragments and the
+  //    committed length go out together; a split past the keys then leaves.
   const int my_page = a.pt[min(key0 / PAGE + (lane % ATTN_PAGES), a.npages - 1)];
-  size_t pbase[ATTN_PAGES];
-#pragma unroll
-  for (int p = 0; p < ATTN_PAGES; ++p)
-    pbase[p] = ((size_t)__builtin_amdgcn_readlane(my_page, p) * a.hkv + h) * PAGE * D;
   const int rbi = blockIdx.z * NW + wave;     // this wave's 16-row block
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
@@ -178,27 +194,30 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   const int n = *a.dev_n;
   const int kv_len = n + a.B;
   if (key0 >= kv_len) return;                 // uniform over the work-group
-  // K pages first, then V^T pages: the scores and the softmax run while the
-  // V^T loads are still in flight.  Each of the NW waves issues DMAS K and
-  // then DMAS V^T 1 KiB blocks (16 blocks per 16 KiB page).
+  // K pages first, then V^T pages (pages past the table re-read the last
+  // one; their keys are masked below, and the arena holds finite values):
+  // the scores and the softmax run while the V^T loads are still in flight.
+  // Each wave issues DMAS K and then DMAS V^T 1 KiB blocks (16 per 16 KiB
+  // page); a lane's byte offset inside a page is the same for every page.
+  uint32_t koff[BPW], voff[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int q = (wave + NW * j) * 64 + lane;  // 16-byte granule of the 16 KiB region
+    const int key = q >> 4, ck = (q & 15) ^ kswz(key);
+    const int d = q >> 3, cv = (q & 7) ^ ((d >> 1) & 7);
+    koff[j] = (uint32_t)(key * D + ck * 8) * 2u;
+    voff[j] = (uint32_t)(d * PAGE + cv * 8) * 2u;
+  }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int p = 0; p < ATTN_PAGES; ++p) {
+      const size_t pbase = ((size_t)__builtin_amdgcn_readlane(my_page, p) * a.hkv + h) * PAGE * D;
+      const uint16_t* base = (half == 0 ? a.kc : a.vc) + pbase;
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
-        const int blk = wave + NW * j;
-        const int q = blk * 64 + lane;         // 16-byte granule of the 16 KiB region
-        const uint16_t* src;
-        if (half == 0) {
-          const int key = q >> 4, c = (q & 15) ^ (key & 15);
-          src = a.kc + pbase[p] + key * D + c * 8;
-        } else {
-          const int d = q >> 3, c = (q & 7) ^ ((d >> 1) & 7);
-          src = a.vc + pbase[p] + d * PAGE + c * 8;
-        }
-        uint8_t* dst = (half == 0 ? ldsK : ldsV) + (size_t)p * 16384 + blk * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+        uint8_t* dst = (half == 0 ? ldsK : ldsV) + (size_t)p * 16384 + (wave + NW * j) * 1024;
+        dma16_s(half == 0 ? koff[j] : voff[j], base, lds_addr(dst));
       }
     }
   }
@@ -207,30 +226,36 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(vm_wait(DMAS));
   __builtin_amdgcn_s_barrier();
 
-  // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr),
-  //    row max, exp2 and the bf16 hi/lo split of p.  Splits that end at or
-  //    before n are visible to every row (the whole committed context), so
-  //    only the split holding the block needs the mask.
-  constexpr int NT = ATTN_SPLIT / 16;
+  // 2. scores of the 256 keys (tile kt holds keys 16kt + 4g + v of row lr).
+  //    Splits that end at or before n are visible to every row (the whole
+  //    committed context), so only the split holding the block needs the
+  //    mask.
   const bool full = key0 + ATTN_SPLIT <= n;    // uniform
   float mx = -INFINITY;
   float lsum = 0.f;
   uint32_t ph[NT / 2][4], pl[NT / 2][4];
   if (live) {
-    float sv[NT][4];
+    // Score tile kt = 2*ks2 + hh puts key 32*ks2 + 8*(i/4) + 4*hh + i%4 in
+    // its row i, so that after the MFMA a lane (lr, g) holds keys
+    // 32*ks2 + 8g + 4hh + v (v < 4): the 8 keys it feeds to the P.V step are
+    // consecutive and one 16-byte V^T read matches them.  Row i = lr reads
+    // key 32*(ks2%2) + 4*hh + 8*(lr/4) + lr%4 of page ks2/2, whose swizzle is
+    // kswz = lr; the tile's page and row offsets are immediates.
+    uint32_t kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kb[ks] = (uint32_t)((8 * (lr >> 2) + (lr & 3)) * 256 + (((4 * ks + g) ^ lr) << 4));
+    floatx4 acc[NT];
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
-      const int p = kt >> 2, key = (kt & 3) * 16 + lr;
-      const uint8_t* kpage = ldsK + (size_t)p * 16384 + (size_t)key * 256;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int ks2 = kt >> 1, hh = kt & 1;
+      const uint8_t* kt_base = ldsK + (ks2 >> 1) * 16384 + (32 * (ks2 & 1) + 4 * hh) * 256;
+      floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int c = (4 * ks + g) ^ (key & 15);
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kpage + c * 16));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kt_base + kb[ks]));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], c, 0, 0, 0);
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sv[kt][v] = acc[v] * a.scale2;
+      acc[kt] = c;
     }
     if (!full) {
       const int kmax = a.causal ? n + tok : kv_len - 1;     // last key this row sees
@@ -238,38 +263,35 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
       for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (key0 + kt * 16 + 4 * g + v > kmax) sv[kt][v] = -INFINITY;
+          if (key0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + v > kmax) acc[kt][v] = -INFINITY;
     }
+    // the row max on the raw scores (scale2 > 0)
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(sv[kt][0], sv[kt][1]), fmaxf(sv[kt][2], sv[kt][3])));
+    for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(acc[kt][0], acc[kt][1]), fmaxf(acc[kt][2], acc[kt][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // masked scores are -inf, so exp2(x - mref) is 0 for them; a row with no
-    // visible key in this split subtracts 0 instead of -inf (no NaN) and runs
-    // the wave-wide MFMAs with p = 0
-    const float mref = mx == -INFINITY ? 0.f : mx;
+    // masked scores are -inf, so exp2 of them is 0; a row with no visible key
+    // in this split subtracts 0 (no NaN) and runs the wave-wide MFMAs with p = 0
+    const float ms = mx == -INFINITY ? 0.f : mx * a.scale2;
+    mx = mx == -INFINITY ? -INFINITY : ms;       // the partial's max, log2 domain
 #pragma unroll
     for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
-      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 16*hh + 4g + v.
-      // p = hi + lo: hi keeps the top 16 bits of p (a bf16 by truncation),
-      // lo = p - hi (exact) rounded to bf16, so hi + lo carries 16 bits of p.
+      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 8g + e
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        uint32_t hb[4], lb[4];
+        float pe[4], lo[4];
+        uint32_t u[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float pe = __builtin_amdgcn_exp2f(sv[2 * ks2 + hh][v] - mref);
-          lsum += pe;
-          const uint32_t u = __float_as_uint(pe);
-          const float hv = __uint_as_float(u & 0xffff0000u);
-          const uint32_t lu = __float_as_uint(pe - hv);
-          hb[v] = u;
-          lb[v] = lu + 0x7fffu + ((lu >> 16) & 1u);
+          pe[v] = __builtin_amdgcn_exp2f(fmaf(acc[2 * ks2 + hh][v], a.scale2, -ms));
+          lsum += pe[v];
+          u[v] = __float_as_uint(pe[v]);
+          lo[v] = pe[v] - __uint_as_float(u[v] & 0xffff0000u);   // exact
         }
-        ph[ks2][2 * hh] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
-        ph[ks2][2 * hh + 1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-        pl[ks2][2 * hh] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
-        pl[ks2][2 * hh + 1] = __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u);
+        ph[ks2][2 * hh] = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
+        ph[ks2][2 * hh + 1] = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
+        pl[ks2][2 * hh] = pack_bf16_rne(lo[0], lo[1]);
+        pl[ks2][2 * hh + 1] = pack_bf16_rne(lo[2], lo[3]);
       }
     }
   }
@@ -279,19 +301,20 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   floatx4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // a lane's V^T fragment: row d = 16*dt + lr (swizzle (d/2)%8 = (lr/2)%8),
+  // keys 8g..8g+7 of the 32-key step = granule 4*(ks2%2) + g; the step's page
+  // and the row tile are immediates
+  uint32_t vb[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) vb[k] = (uint32_t)((lr * 8 + ((4 * k + g) ^ ((lr >> 1) & 7))) * 16);
 #pragma unroll
   for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
     const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[ks2][0], ph[ks2][1], ph[ks2][2], ph[ks2][3]});
     const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[ks2][0], pl[ks2][1], pl[ks2][2], pl[ks2][3]});
-    const int p = ks2 >> 1;
-    const uint8_t* vpage = ldsV + (size_t)p * 16384;
-    const int c0 = 4 * (ks2 & 1) + (g >> 1), hoff = (g & 1) * 8;
+    const uint8_t* vpage = ldsV + (ks2 >> 1) * 16384;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = dt * 16 + lr, sw = (d >> 1) & 7;
-      const uint2 lo = *(const uint2*)(vpage + (size_t)(d * 8 + (c0 ^ sw)) * 16 + hoff);
-      const uint2 hi = *(const uint2*)(vpage + (size_t)(d * 8 + ((c0 + 2) ^ sw)) * 16 + hoff);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const uint4*)(vpage + dt * 2048 + vb[ks2 & 1]));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
     }
