@@ -260,6 +260,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run each next draft's context rows on a second stream while the verify finishes")
     ap.add_argument("--max-draft", type=int, default=0,
                     help="verify only the first N drafts per step (0 = the whole block)")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -290,6 +292,8 @@ def main():
     if args.max_draft:
         pair.set_max_draft(args.max_draft)
         n_drafts = pair.accept_block - 1
+    if args.overlap:
+        pair.set_overlap(True)
     host_ck = None if args.no_cpu_baseline else host_checkpoint(ck)
     del ck
     torch.cuda.synchronize()
@@ -444,6 +448,7 @@ def main():
                                    if sampling else "injected acceptance")
                                 + (f", draft cap {n_drafts} ({pair.vrows} verify rows)" if args.max_draft else "")),
                    "block": B, "ctx": ctx, "global_batch": 1, "verify_rows": pair.vrows, "drafts_verified": n_drafts,
+                   "draft_verify_overlap": bool(args.overlap),
                    "target_format": fmt_name[cfg.target.fmt], "drafter_format": fmt_name[cfg.drafter.fmt]},
         "tok_per_s": round(tok_per_s, 1),
         "tokens_per_step": round(tokens / K, 3),

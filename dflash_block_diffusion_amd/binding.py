@@ -69,6 +69,7 @@ SIGNATURES = {
     "dflash_verify_block": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_accept": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_set_max_draft": (c_int, [c_void_p, c_int, POINTER(c_int), POINTER(c_int)]),
+    "dflash_set_overlap": (c_int, [c_void_p, c_int]),
     "dflash_set_sampling": (c_int, [c_void_p, c_float, c_uint64]),
     "dflash_accept_sampled": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dflash_sample_logits": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_uint64, c_int, c_int, c_int,

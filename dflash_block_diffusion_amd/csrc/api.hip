@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -376,6 +377,16 @@ struct dflash_state {
   bool prof = false;
   std::vector<ProfRec> prof_recs;
   std::vector<hipEvent_t> ev_pool;
+  // Draft/verify overlap: a second stream takes the next draft's context rows
+  // while the verify finishes (dflash_set_overlap)
+  bool ov_on = false;
+  hipStream_t ov_stream = nullptr;
+  hipEvent_t ov_fork = nullptr, ov_join = nullptr;
+  bool ov_pending = false;   // overlap work enqueued and not yet joined
+  bool ctx_ready = false;    // the last verify's context rows are in the drafter cache
+  Workspace ws2{};           // GEMM workspace of the overlap stream
+  void* bu2 = nullptr;       // context features of the overlap stream [B][H] drafter gin
+  std::vector<GemmW> dkv;    // each drafter layer's k/v rows of its QKV weight
 };
 
 struct Carver {
@@ -395,6 +406,25 @@ static int gdn_rec(const dflash_model* t) { return t->d.gdn_dk + t->d.gdn_dv + 2
 
 // rows of a dense prompt chunk (a multiple of both block sizes)
 constexpr int DENSE_PROMPT_ROWS = 1024;
+
+// The k and v output rows of a QKV projection (rows hq*d .. (hq+2*hkv)*d)
+// as a weight of their own: packed weights are stored row tile by row tile
+// (16 output rows, all K tiles), so a whole-tile row range is contiguous, and
+// so are its scales.
+static GemmW kv_rows(const GemmW& W, const dflash_model* m) {
+  const int r0 = m->d.n_q_heads * m->d.head_dim, rows = 2 * m->d.n_kv_heads * m->d.head_dim;
+  GemmW v = W;
+  v.n = rows;
+  if (W.fmt == W_F32) {
+    v.w = (const char*)W.w + (size_t)r0 * W.k * 4;
+    return v;
+  }
+  const int ktiles = W.k / tile_k(W.fmt);
+  v.w = (const char*)W.w + (size_t)(r0 / 16) * ktiles * 1024;
+  if (W.fmt == W_W8) v.s = (const char*)W.s + (size_t)r0 * 2;
+  if (W.fmt == W_W4) v.s = (const char*)W.s + (size_t)(r0 / 16) * ktiles * 64;
+  return v;
+}
 
 static void carve(dflash_state* s, Carver& c) {
   const dflash_model *t = s->t, *d = s->dr;
@@ -468,6 +498,21 @@ static void carve(dflash_state* s, Carver& c) {
   s->ws.am_idx = c.take<int>((size_t)am * 64);
   s->ws.am_cap = am;
   s->ws.logits_tmp = t->d.fmt == DFLASH_FMT_F32 ? c.take<float>((size_t)MAX_ROWS * t->d.vocab) : nullptr;
+  // the overlap stream's GEMMs: the fc projection and every drafter layer's
+  // k/v rows, B rows each
+  {
+    size_t pf2 = 1;
+    auto need2 = [&](const GemmW& g) {
+      const Plan p = make_plan(g.fmt, g.n, g.k, B, EPI_PARTIAL);
+      pf2 = std::max(pf2, (size_t)p.S * B * g.n);
+    };
+    need2(d->fc);
+    for (const Layer& L : d->layers) need2(kv_rows(L.qkv, d));
+    s->ws2.part = c.take<float>(pf2);
+    s->ws2.part_floats = pf2;
+    s->ws2.am_val = nullptr; s->ws2.am_idx = nullptr; s->ws2.am_cap = 0; s->ws2.logits_tmp = nullptr;
+    s->bu2 = c.take<char>((size_t)B * d->d.hidden * 4);
+  }
   s->ybuf = c.take<int32_t>(64);
   const size_t sf = (size_t)t->n_gdn * t->d.gdn_heads * t->d.gdn_dv * t->d.gdn_dk;
   s->gdn_S = t->n_gdn ? c.take<float>(sf) : nullptr;
@@ -540,6 +585,7 @@ extern "C" int dflash_state_init(dflash_state** out, const dflash_model* t, cons
   carve(s, c);
   s->base = base;
   s->bytes = c.off;
+  for (const Layer& L : d->layers) s->dkv.push_back(kv_rows(L.qkv, d));
   // zero the whole arena (KV pages are read whole: unwritten slots must be finite)
   hipError_t e = launch_fill_i32((int32_t*)base, c.off / 4, 0, nullptr);
   // RoPE table: angle pos * base^(-2i/d) in double, cos/sin rounded to fp32
@@ -570,6 +616,12 @@ extern "C" void dflash_state_destroy(dflash_state* s) {
   if (!s) return;
   for (auto& r : s->prof_recs) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
   for (auto ev : s->ev_pool) hipEventDestroy(ev);
+  if (s->ov_stream) {
+    hipStreamSynchronize(s->ov_stream);
+    hipStreamDestroy(s->ov_stream);
+    hipEventDestroy(s->ov_fork);
+    hipEventDestroy(s->ov_join);
+  }
   delete s;
 }
 
@@ -583,24 +635,31 @@ static hipEvent_t take_event(dflash_state* s) {
 
 // Enqueue one GEMM.  PARTIAL launches return (in *parts) the partial sums
 // the consuming kernel adds up.
-static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, hipStream_t st,
-                Parts* parts = nullptr, void* out = nullptr, int otype = 0, float* logits = nullptr,
-                int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
+static int gemm_ws(dflash_state* s, const Workspace& ws, int32_t* status, const GemmW& W, const void* x, int ldx,
+                   int m, int epi, hipStream_t st, Parts* parts = nullptr, void* out = nullptr, int otype = 0,
+                   float* logits = nullptr, int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
   GemmCall c{};
   c.W = &W; c.x = x; c.ldx = ldx; c.m = m; c.epi = epi;
-  c.part = s->ws.part; c.out = out; c.otype = otype;
+  c.part = ws.part; c.out = out; c.otype = otype;
   c.logits = logits; c.ldl = ldl; c.row0 = row0; c.am_out = am_out;
-  c.status = s->scal + SC_STATUS;
+  c.status = status;
   const char* name = nullptr;
   double bytes = 0, io = 0;
   int S = 1;
   hipEvent_t ea = nullptr, eb = nullptr;
   if (s->prof) { ea = take_event(s); eb = take_event(s); hipEventRecord(ea, st); }
-  hipError_t e = launch_gemm(c, s->ws, st, &name, &bytes, &S, &io);
+  hipError_t e = launch_gemm(c, ws, st, &name, &bytes, &S, &io);
   if (s->prof) { hipEventRecord(eb, st); s->prof_recs.push_back({name, bytes, io, ea, eb, c}); }
   if (e != hipSuccess) return fail(DFLASH_E_DEVICE, std::string("gemm: ") + hipGetErrorString(e));
-  if (parts) *parts = Parts{s->ws.part, S, (size_t)m * W.n, W.n};
+  if (parts) *parts = Parts{ws.part, S, (size_t)m * W.n, W.n};
   return DFLASH_OK;
+}
+
+static int gemm(dflash_state* s, const GemmW& W, const void* x, int ldx, int m, int epi, hipStream_t st,
+                Parts* parts = nullptr, void* out = nullptr, int otype = 0, float* logits = nullptr,
+                int ldl = 0, int row0 = 0, int32_t* am_out = nullptr) {
+  return gemm_ws(s, s->ws, s->scal + SC_STATUS, W, x, ldx, m, epi, st, parts, out, otype, logits, ldl, row0,
+                 am_out);
 }
 
 #define RC(x) do { int rc_ = (x); if (rc_) return rc_; } while (0)
@@ -623,16 +682,21 @@ static int norm(dflash_state* s, const dflash_model* m, Pending& pend, const flo
 
 // B = block rows of this pass: the whole block for a draft (plus as many
 // context rows), the verify rows for a verify.
+// ctx: a draft pass also projects the pending context rows (rows B..2B-1 of
+// the QKV input); after_norm (if set) runs once the layer's first norm -- which
+// completes the previous layer's residual and conditioning rows -- is enqueued.
 static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer& L, bool draft, Pending& pend,
-                      int B, hipStream_t st) {
+                      int B, hipStream_t st, bool ctx = true, const std::function<int()>* after_norm = nullptr) {
   const int H = m->d.hidden, hq = m->d.n_q_heads, hkv = m->d.n_kv_heads, hd = m->d.head_dim;
-  const int rows = draft ? 2 * B : B;
+  const bool with_ctx = draft && ctx;
+  const int rows = with_ctx ? 2 * B : B;
   RC(norm(s, m, pend, L.in_norm, s->bu, m->gin, B, st));
+  if (after_norm) RC((*after_norm)());
   Parts qkv;
   RC(gemm(s, L.qkv, s->bu, H, rows, EPI_PARTIAL, st, &qkv));
   RopeCall rc;
   rc.qkv = qkv; rc.atype = m->act;
-  rc.block_rows = B; rc.ctx_rows = draft ? B : 0;
+  rc.block_rows = B; rc.ctx_rows = with_ctx ? B : 0;
   rc.dev_n = s->scal + SC_N; rc.dev_p = draft ? s->scal + SC_P : nullptr;
   rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = m->d.eps;
   rc.cos_t = s->cos_t; rc.sin_t = s->sin_t; rc.q_out = s->bq;
@@ -712,15 +776,73 @@ static int draft_context_kv(dflash_state* s, hipStream_t st, int side_row0 = 0, 
   return DFLASH_OK;
 }
 
+// Draft/verify overlap (mirror-sd README, "How It Works": the drafter runs
+// while the target verifies).  The part of the next draft that depends on the
+// verify alone -- the drafter's context rows: the fc projection and hidden
+// norm of every verify row's conditioning features, then each drafter
+// layer's k/v of them with QK-norm and RoPE, written to the drafter cache at
+// the rows' positions -- goes to the overlap stream as soon as the last
+// conditioning layer's rows are complete, and runs while the target's last
+// layers, the lm-head, the acceptance and the commit run on the caller's
+// stream.  Rows past the accepted prefix land at positions that the next
+// draft's block rows overwrite before any read, so the drafter cache the draft
+// reads equals the sequential path's, and the draft then skips those rows.
+static int overlap_ctx(dflash_state* s, int rows, hipStream_t st) {
+  const dflash_model* d = s->dr;
+  const int H = d->d.hidden;
+  hipStream_t os = s->ov_stream;
+  HIPCHK(hipEventRecord(s->ov_fork, st));
+  HIPCHK(hipStreamWaitEvent(os, s->ov_fork, 0));
+  s->ov_pending = true;
+  int32_t* status = s->scal + SC_STATUS2;
+  Parts fc;
+  RC(gemm_ws(s, s->ws2, status, d->fc, s->side, d->d.n_sel * H, rows, EPI_PARTIAL, os, &fc));
+  NormCall c{};
+  c.mode = NORM_PROJ; c.in = fc; c.x = nullptr; c.xtype = d->act; c.ldx = H;
+  c.gain = d->d.hidden_norm; c.eps = d->d.eps; c.h = H; c.rows = rows;
+  c.out = s->bu2; c.otype = d->gin; c.ldo = H; c.tiled = 1;
+  c.status = status;
+  HIPCHK(launch_norm(c, os));
+  for (int l = 0; l < d->d.n_layers; ++l) {
+    const Layer& L = d->layers[l];
+    Parts kv;
+    RC(gemm_ws(s, s->ws2, status, s->dkv[l], s->bu2, H, rows, EPI_PARTIAL, os, &kv));
+    RopeCall rc;
+    rc.qkv = kv; rc.atype = d->act;
+    rc.block_rows = 0; rc.ctx_rows = rows; rc.ctx_at_n = 1;   // row j at the verify's n + j
+    rc.dev_n = s->scal + SC_VBASE; rc.dev_p = nullptr;
+    rc.q_norm = L.q_norm; rc.k_norm = L.k_norm; rc.eps = d->d.eps;
+    rc.cos_t = s->cos_t; rc.sin_t = s->sin_t; rc.q_out = nullptr;
+    rc.kc = s->dk[l]; rc.vc = s->dv[l];
+    rc.page_table = s->pt; rc.capacity = s->capacity;
+    rc.hq = 0; rc.hkv = d->d.n_kv_heads; rc.d = d->d.head_dim;   // the k/v columns only
+    HIPCHK(launch_qk_rope(rc, os));
+  }
+  HIPCHK(hipEventRecord(s->ov_join, os));
+  s->ctx_ready = true;
+  return DFLASH_OK;
+}
+
+// The caller's stream waits for the overlap work (if any is outstanding).
+static int overlap_join(dflash_state* s, hipStream_t st) {
+  if (!s->ov_pending) return DFLASH_OK;
+  HIPCHK(hipStreamWaitEvent(st, s->ov_join, 0));
+  s->ov_pending = false;
+  return DFLASH_OK;
+}
+
 static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t st) {
   const dflash_model *t = s->t, *d = s->dr;
   const int H = d->d.hidden, B = s->B;
-  RC(draft_context(s, st));
+  RC(overlap_join(s, st));
+  // the pending context rows, unless the overlap stream already wrote them
+  const bool ctx = !(s->ov_on && s->ctx_ready);
+  if (ctx) RC(draft_context(s, st));
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 1, d->d.mask_token, B, s->x, H,
                       s->scal + SC_STATUS, st));
   Pending pend;
   for (int l = 0; l < d->d.n_layers; ++l) {
-    RC(attn_layer(s, d, l, d->layers[l], true, pend, B, st));
+    RC(attn_layer(s, d, l, d->layers[l], true, pend, B, st, ctx));
     RC(ffn(s, d, d->layers[l], pend, B, st, nullptr, 0, 0, 0));
   }
   RC(norm(s, d, pend, d->d.final_norm, s->bu, t->gin, B, st));
@@ -739,20 +861,30 @@ static int do_draft(dflash_state* s, int32_t* block, float* logits, hipStream_t 
 
 // Target forward of rows 0..B-1 of block (B = s->B for prefill chunks, the
 // verify rows otherwise).
+// overlap: a block verify whose next draft's context rows go to the overlap
+// stream (once the last conditioning layer's rows are complete)
 static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, float* logits, int B, hipStream_t st,
-                     bool head = true) {
+                     bool head = true, bool overlap = false) {
   const dflash_model *t = s->t, *d = s->dr;
   const int H = t->d.hidden;
+  const int sel_last = d->d.n_sel ? d->d.sel_layers[d->d.n_sel - 1] : -1;
+  const bool ov = overlap && sel_last >= 0;
+  const std::function<int()> fork = [&]() { return overlap_ctx(s, B, st); };
+  if (ov) HIPCHK(launch_copy_tokens(s->scal + SC_N, s->scal + SC_VBASE, 1, st));
   HIPCHK(launch_embed(t->d.embed, t->act, H, t->d.vocab, block, 0, 0, B, s->x, H, s->scal + SC_STATUS, st));
   Pending pend;
   int sel = 0, g = 0;
   for (int l = 0; l < t->d.n_layers; ++l) {
     const Layer& L = t->layers[l];
+    // the first norm of the layer after the last conditioning layer completes
+    // that layer's conditioning rows
+    const std::function<int()>* hook = ov && l == sel_last + 1 ? &fork : nullptr;
     if (L.kind == DFLASH_LAYER_ATTN) {
-      RC(attn_layer(s, t, l, L, false, pend, B, st));
+      RC(attn_layer(s, t, l, L, false, pend, B, st, true, hook));
     } else {
       const int gh = t->d.gdn_heads, dkk = t->d.gdn_dk, dvv = t->d.gdn_dv;
       RC(norm(s, t, pend, L.in_norm, s->bu, t->gin, B, st));
+      if (hook) RC((*hook)());
       GdnCall gc;
       RC(gemm(s, L.qkv, s->bu, H, B, EPI_PARTIAL, st, &gc.proj));
       gc.atype = t->act; gc.rows = B; gc.gh = gh; gc.dk = dkk; gc.dv = dvv;
@@ -785,6 +917,7 @@ static int do_verify(dflash_state* s, const int32_t* block, int32_t* argmax, flo
   // (this norm also completes the last layer's residual update, which writes
   // its conditioning rows when that layer is a selected one)
   RC(norm(s, t, pend, t->d.final_norm, s->bu, t->gin, B, st));
+  if (ov && sel_last == t->d.n_layers - 1) RC(fork());
   // a prompt chunk before the last needs only the caches, the GatedDeltaNet
   // state and the conditioning rows: no logits
   if (!head) return DFLASH_OK;
@@ -821,6 +954,7 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
     return fail(DFLASH_E_CAPACITY, "prompt longer than the state's max_ctx");
   hipStream_t st = (hipStream_t)stream;
   const dflash_model* t = s->t;
+  RC(overlap_join(s, st));
   HIPCHK(launch_set_scalars(s->scal, 0, 0, 1, st));
   HIPCHK(launch_copy_tokens(d_tokens, s->tokens, n_tokens, st));
   if (t->n_gdn)
@@ -901,6 +1035,7 @@ extern "C" int dflash_prefill(dflash_state* s, const int32_t* d_tokens, int n_to
   HIPCHK(launch_copy_tokens(s->ybuf + last - 1, d_first, 1, st));
   HIPCHK(launch_set_scalars(s->scal, -1, 0, 0, st));
   s->snap_n = -1;
+  s->ctx_ready = true;            // every prompt row's context is in the drafter cache
   return DFLASH_OK;
 }
 
@@ -912,7 +1047,29 @@ extern "C" int dflash_draft_block(dflash_state* s, int32_t* d_block, float* d_lo
 extern "C" int dflash_verify_block(dflash_state* s, const int32_t* d_block, int32_t* d_argmax, float* d_logits,
                                    void* stream) {
   if (!s || !d_block || !d_argmax) return fail(DFLASH_E_INVALID, "null argument");
-  return do_verify(s, d_block, d_argmax, d_logits, s->vrows, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  RC(overlap_join(s, st));
+  s->ctx_ready = false;
+  return do_verify(s, d_block, d_argmax, d_logits, s->vrows, st, true, s->ov_on);
+}
+
+extern "C" int dflash_set_overlap(dflash_state* s, int on) {
+  if (!s) return fail(DFLASH_E_INVALID, "null state");
+  if (on && !s->ov_stream) {
+    hipStream_t os = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&os, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (os) hipStreamDestroy(os);
+      if (f) hipEventDestroy(f);
+      return fail(DFLASH_E_DEVICE, std::string("overlap stream: ") + hipGetErrorString(e));
+    }
+    s->ov_stream = os; s->ov_fork = f; s->ov_join = j;
+  }
+  s->ov_on = on != 0;
+  return DFLASH_OK;
 }
 
 // Draft cap (mlx-dspark v0.0.3 "Highlights" and "API", --max-draft): verify
@@ -1003,18 +1160,25 @@ extern "C" int dflash_accept(const int32_t* d_block, const int32_t* d_argmax, in
 
 extern "C" int dflash_kv_commit(dflash_state* s, const int32_t* d_accept, const int32_t* d_emit, void* stream) {
   if (!s || !d_accept) return fail(DFLASH_E_INVALID, "null argument");
-  return do_commit(s, d_accept, 0, d_emit, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  RC(do_commit(s, d_accept, 0, d_emit, st));
+  // the step ends with the overlap work joined, so that a captured step is
+  // self-contained
+  return overlap_join(s, st);
 }
 
 static int read_scalars(dflash_state* s, int32_t* h, hipStream_t st) {
   HIPCHK(hipStreamSynchronize(st));
+  if (s->ov_stream) HIPCHK(hipStreamSynchronize(s->ov_stream));
   HIPCHK(hipMemcpy(h, s->scal, SC_COUNT * sizeof(int32_t), hipMemcpyDeviceToHost));
+  h[SC_STATUS] |= h[SC_STATUS2];
   return DFLASH_OK;
 }
 
 extern "C" int dflash_kv_rollback(dflash_state* s, int new_len, int32_t* d_block, void* stream) {
   if (!s) return fail(DFLASH_E_INVALID, "null state");
   hipStream_t st = (hipStream_t)stream;
+  RC(overlap_join(s, st));
   int32_t h[SC_COUNT];
   RC(read_scalars(s, h, st));
   if (new_len < 1 || new_len > h[SC_N]) return fail(DFLASH_E_SHAPE, "rollback length outside [1, n]");
@@ -1025,6 +1189,7 @@ extern "C" int dflash_kv_rollback(dflash_state* s, int new_len, int32_t* d_block
     HIPCHK(launch_copy_f32(s->gdn_snap, s->gdn_S, sf, st));
   }
   HIPCHK(launch_rollback(s->scal, new_len, s->tokens, d_block, st));
+  s->ctx_ready = true;            // no pending context rows: positions < new_len are in the cache
   return DFLASH_OK;
 }
 

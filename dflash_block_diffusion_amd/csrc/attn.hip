@@ -58,9 +58,9 @@ __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
   }
   const float g1 = gain[i], g2 = gain[i + half];
   const int n = *c.dev_n;
-  const int p = c.dev_p ? *c.dev_p : 0;
-  const int pos = row < c.block_rows ? n + row : n - p + (row - c.block_rows);
-  if ((row >= c.block_rows && row - c.block_rows >= p) || pos < 0 || pos >= c.capacity) return;
+  const int p = c.dev_p && !c.ctx_at_n ? *c.dev_p : 0;
+  const int pos = row < c.block_rows ? n + row : (c.ctx_at_n ? n : n - p) + (row - c.block_rows);
+  if ((row >= c.block_rows && !c.ctx_at_n && row - c.block_rows >= p) || pos < 0 || pos >= c.capacity) return;
   const float cs = c.cos_t[(size_t)pos * half + i];
   const float sn = c.sin_t[(size_t)pos * half + i];
   const int page = kv ? c.page_table[pos / PAGE] : 0;

@@ -210,6 +210,8 @@ struct RopeCall {
   void* q_out;                              // [B][hq][d] act
   void* kc; void* vc; const int* page_table; int capacity;
   int hq, hkv, d;
+  int ctx_at_n = 0;                         // 1: context row j sits at position n+j and every
+                                            //    row is kept (dev_p unused; no block rows)
 };
 hipError_t launch_qk_rope(const RopeCall& c, hipStream_t s);
 
@@ -298,6 +300,9 @@ hipError_t launch_gdn_replay(float* S_all, const float* tape_all, int n_layers, 
                              int capacity, hipStream_t s);
 
 // scalar slots in the arena
-enum Scalar { SC_N = 0, SC_P = 1, SC_STEP = 2, SC_STATUS = 3, SC_SNAP_N = 4, SC_COUNT = 16 };
+enum Scalar { SC_N = 0, SC_P = 1, SC_STEP = 2, SC_STATUS = 3, SC_SNAP_N = 4,
+              SC_VBASE = 5,    // n when the last verify was enqueued (its row 0's position)
+              SC_STATUS2 = 6,  // status bits of work on the overlap stream
+              SC_COUNT = 16 };
 
 }  // namespace dfl

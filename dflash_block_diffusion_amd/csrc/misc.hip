@@ -224,7 +224,7 @@ hipError_t launch_commit(int32_t* scal, const int32_t* d_acc, int host_count, co
 __global__ void set_scalars_kernel(int32_t* scal, int n, int p, int clear) {
   if (n >= 0) scal[SC_N] = n;
   if (p >= 0) scal[SC_P] = p;
-  if (clear) { scal[SC_STATUS] = 0; scal[SC_STEP] = 0; }
+  if (clear) { scal[SC_STATUS] = 0; scal[SC_STATUS2] = 0; scal[SC_STEP] = 0; }
 }
 
 hipError_t launch_set_scalars(int32_t* scal, int n, int p, int clear_status, hipStream_t s) {

@@ -218,6 +218,11 @@ class Pair:
         self.vrows, self.accept_block = v.value, a.value
         return self.vrows
 
+    def set_overlap(self, on: bool):
+        """Run the next draft's context rows on a second stream while each
+        verify finishes (dflash_set_overlap)."""
+        check(lib().dflash_set_overlap(self.st, 1 if on else 0))
+
     def set_sampling(self, temperature: float, seed: int = 0):
         """Speculative sampling at `temperature` (0 = greedy) with Philox seed `seed`."""
         check(lib().dflash_set_sampling(self.st, float(temperature), int(seed) & (2 ** 64 - 1)))

@@ -257,6 +257,29 @@ int dflash_verify_block(dflash_state *st, const int32_t *d_block, int32_t *d_arg
  * calls enqueue, so a captured graph must be recaptured. */
 int dflash_set_max_draft(dflash_state *st, int max_draft, int *h_verify_rows, int *h_accept_block);
 
+/* Draft/verify overlap (mirror-sd README, "How It Works": the drafter runs
+ * concurrently with the target's verify).  With on != 0, each later
+ * dflash_verify_block also enqueues, on a second stream the state owns
+ * (default priority, created on the first call), the part of the next draft
+ * that depends on that verify alone: the drafter's context rows -- the fc
+ * projection and hidden norm of every verify row's conditioning features, then
+ * every drafter layer's k/v of them with QK-norm and RoPE, written to the
+ * drafter cache at the rows' positions n+i.  That work starts once the last
+ * conditioning layer's rows are complete (an event recorded on the verify's
+ * stream) and runs while the target's remaining layers, the lm-head, the
+ * acceptance and the commit run; dflash_kv_commit makes its stream wait for it
+ * (as do the next draft, verify, prefill and rollback, if no commit came in
+ * between), and the next dflash_draft_block skips those rows.  Rows past the
+ * accepted prefix are written at positions the next draft's block rows
+ * overwrite before any read, so every result equals the sequential path's (up
+ * to the rounding of a draft QKV projection over B instead of 2B rows).  A
+ * step captured into a graph (draft, verify, accept, commit) holds the fork and
+ * the join, so the graph has two concurrent branches.  on = 0 returns to the
+ * sequential path.  Errors: DFLASH_E_INVALID (null state), DFLASH_E_DEVICE
+ * (stream or event creation failed).  Host-only call; it changes what later
+ * calls enqueue, so a captured graph must be recaptured. */
+int dflash_set_overlap(dflash_state *st, int on);
+
 /* Temperature sampling (mlx-dspark v0.0.3, "Highlights": --temperature T > 0
  * stays lossless, an exact sample of the target at T).  temperature 0 (the
  * default) is greedy decoding; T > 0 switches later calls to speculative

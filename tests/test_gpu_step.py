@@ -113,15 +113,19 @@ def progress(cfg, msg):
     print(f"[{cfg.name}] {msg}", flush=True)
 
 
-def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
+def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None, overlap=False):
     """Run len(forced) injected steps on GPU and oracle in lockstep; with
-    max_draft > 0 both sides verify only the first max_draft drafts."""
+    max_draft > 0 both sides verify only the first max_draft drafts; with
+    overlap the GPU takes each next draft's context rows on its second
+    stream while the verify finishes (the oracle runs the steps in order)."""
     B, V = cfg.block, cfg.target.vocab
     ck = synth.make_pair(cfg)
     progress(cfg, f"checkpoint ready, prompt {P}, {len(forced)} steps")
     prompt = synth.prompt(cfg, P)
     max_ctx = max_ctx or P + (len(forced) + 4) * B + 64
     pair = Pair(cfg, ck, max_ctx=max_ctx)
+    if overlap:
+        pair.set_overlap(True)
     if max_draft:
         rows = pair.set_max_draft(max_draft)
         assert max_draft + 1 <= rows <= B
@@ -229,7 +233,8 @@ def lockstep(cfg, P, forced, gdn_exact=False, max_draft=0, max_ctx=None):
         progress(cfg, f"step {s} done: a {a}, n {nn}")
     q = pair.query()
     assert q["n"] == op.t.n and q["status"] == 0
-    finish_stats(cfg, P, stats, {"max_ctx": max_ctx, "max_draft": max_draft, "n_end": int(q["n"])})
+    finish_stats(cfg, P, stats, {"max_ctx": max_ctx, "max_draft": max_draft, "n_end": int(q["n"]),
+                                 "overlap": bool(overlap)})
     return pair, op, stats, tapes
 
 
@@ -393,6 +398,74 @@ def test_rollback_replays_identically():
         pair.step()
     assert pair.query()["n"] == n1
     assert np.array_equal(pair.tokens(n1 + 1).cpu().numpy(), toks1)
+
+
+# Draft/verify overlap (mirror-sd README, "How It Works": the drafter runs
+# while the target verifies): the next draft's context rows -- fc projection,
+# hidden norm, every drafter layer's k/v with QK-norm and RoPE -- go to a second
+# stream once the last conditioning layer's rows are complete.  The depth-
+# reduced stacks condition on target layers 0 and 1, so with 3 target layers
+# the fork sits in layer 2's first norm, with 2 after the final norm, and in
+# the 4-layer hybrid in a GatedDeltaNet layer's first norm.
+@pytest.mark.parametrize("name,layers,P,forced", [
+    ("8b", 3, 2048, [0, 31, 9]),
+    ("8b", 2, 300, [31, 5, 0]),
+    ("hybrid", 4, 100, [3, 15, 0]),
+])
+def test_reduced_lockstep_overlap(name, layers, P, forced):
+    cfg = reduced(name, layers=layers)
+    lockstep(cfg, P, forced, overlap=True)
+
+
+def test_tiny_lockstep_overlap():
+    cfg = C.tiny()
+    lockstep(cfg, 64, [0, 15, 7, 3, 15], overlap=True)
+
+
+def test_tiny_overlap_generate_equals_oracle_greedy():
+    cfg = C.tiny()
+    ck = synth.make_pair(cfg)
+    pr = synth.prompt(cfg, 64)
+    ref = greedy(cfg, ck, pr, cfg.new_tokens, cap=256)
+    pair = Pair(cfg, ck, max_ctx=256)
+    pair.set_overlap(True)
+    assert pair.generate(pr, cfg.new_tokens) == ref
+
+
+def test_overlap_step_graph_replays_match_eager():
+    # a captured step holds the fork and the join (two concurrent branches);
+    # every replay, with eager reads and synchronisations in between, must
+    # give the eager steps' tokens
+    cfg = reduced("8b", layers=3)
+    ck = synth.make_pair(cfg)
+    P = 300
+    prompt = synth.prompt(cfg, P)
+    pair = Pair(cfg, ck, max_ctx=1024)
+    pair.set_overlap(True)
+    pair.prefill(prompt)
+    ns = []
+    for _ in range(6):
+        pair.step()
+        ns.append(pair.query()["n"])
+    ref = pair.tokens(ns[-1] + 1).cpu().clone()
+    pair.rollback(P)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pair.step()                          # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    pair.rollback(P)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pair.step()
+    torch.cuda.synchronize()
+    pair.rollback(P)
+    for i in range(6):
+        g.replay()
+        torch.cuda.synchronize()
+        q = pair.query()
+        assert q["n"] == ns[i] and q["status"] == 0
+        assert torch.equal(pair.tokens(q["n"] + 1).cpu(), ref[:q["n"] + 1])
 
 
 def test_hybrid_gdn_replay_bitexact_vs_scratch_recompute():
