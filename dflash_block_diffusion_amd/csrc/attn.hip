@@ -34,10 +34,20 @@ static constexpr float LOG2E = 1.4426950408889634f;
 // ------------------------------------------------------------ QK norm + RoPE
 // One wave per (row, head); a work-group takes R consecutive rows of one
 // head: 4 when the launch has many rows (a prompt chunk), 1 otherwise.
+// Work-groups are numbered so that the G q heads and the k/v head of KV head
+// h come from work-groups h, h + hkv, h + 2 hkv, ...: the XCDs take
+// work-groups round-robin, so with hkv = 8 (every benchmark shape) the
+// outputs the attention of KV head h reads are written through XCD h's L2,
+// where that attention runs too.
 template <int R>
 __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
-  const int row = R == 1 ? (int)blockIdx.x : (int)blockIdx.x * R + (int)(threadIdx.x >> 6);
-  const int head = blockIdx.y, lane = R == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+  const int L = blockIdx.x + gridDim.x * blockIdx.y;
+  const int grp = c.hkv, per = c.hq / c.hkv + 1;       // a KV head's q heads and its k/v head
+  const int hk = L % grp, j = L / grp;
+  const int hi = j % per, rg = j / per;
+  const int head = hi < per - 1 ? hk * (per - 1) + hi : c.hq + hk;
+  const int row = R == 1 ? rg : rg * R + (int)(threadIdx.x >> 6);
+  const int lane = R == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
   if (R > 1 && row >= c.block_rows + c.ctx_rows) return;   // past the launch's rows (whole waves)
   if (row >= c.block_rows && head < c.hq) return;      // context rows only carry k/v
   const int d = c.d, half = d >> 1;
@@ -171,7 +181,15 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y, sidx = blockIdx.x;
+  // work-group L takes KV head L mod hkv: the XCDs take work-groups
+  // round-robin, so with hkv = 8 all of a KV head's splits (and both row
+  // groups, which then share the staged pages through L2) run on one XCD,
+  // the one whose L2 holds that head's q and new keys (qk_rope_kernel) and
+  // which runs the combine of its rows
+  const int Lw = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int h = Lw % a.hkv;
+  const int rest = Lw / a.hkv;
+  const int sidx = rest % gridDim.x, zg = rest / gridDim.x;   // split, row group
   const int key0 = sidx * ATTN_SPLIT;
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
@@ -180,7 +198,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   //    each wait for the previous one), this wave's q fragments and the
   //    committed length go out together; a split past the keys then leaves.
   const int my_page = a.pt[min(key0 / PAGE + (lane % ATTN_PAGES), a.npages - 1)];
-  const int rbi = blockIdx.z * NW + wave;     // this wave's 16-row block
+  const int rbi = zg * NW + wave;             // this wave's 16-row block
   const bool live = rbi < nrb;                 // wave-uniform
   const int rb = live ? rbi : nrb - 1;
   const int r = rb * 16 + lr;
@@ -608,9 +626,13 @@ constexpr int COMBINE_MAX_SPLITS = 32;
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
                                                           int max_splits, int B, int hq, int d, void* out, int otype,
-                                                          int ldo, int32_t* status) {
-  const int row = blockIdx.x;          // token * hq + qh
-  const int tok = row / hq, qh = row % hq;
+                                                          int ldo, int32_t* status, int hkv) {
+  // work-group L takes a row of KV head L mod hkv (the XCD whose L2 received
+  // that head's partials from the attention)
+  const int G = hq / hkv;
+  const int hk = blockIdx.x % hkv, j = blockIdx.x / hkv;
+  const int qh = hk * G + j % G, tok = j / G;
+  const int row = tok * hq + qh;
   const size_t stride = (size_t)B * hq;
   const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
   const int kv_len = *dev_n + B;
@@ -704,7 +726,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
-                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status);
+                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status, c.hkv);
   return hipGetLastError();
 }
 
