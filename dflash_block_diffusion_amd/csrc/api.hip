@@ -340,6 +340,7 @@ struct dflash_state {
   const dflash_model* t = nullptr;
   const dflash_model* dr = nullptr;
   int B = 0, max_ctx = 0, capacity = 0, pages = 0, max_splits = 0;
+  int split = ATTN_SPLIT;   // keys per block-attention split
   int vrows = 0;          // rows a verify runs (B, or fewer under a draft cap)
   int pm = 0;             // rows of a dense prompt chunk (0: prompts run in blocks of B)
   bool pm_draft = false;  // the drafter's context pass of a chunk runs dense as well
@@ -533,7 +534,13 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   const int need = max_ctx + 2 * block;
   s->pages = (need + PAGE - 1) / PAGE;
   s->capacity = s->pages * PAGE;
-  s->max_splits = (s->capacity + ATTN_SPLIT - 1) / ATTN_SPLIT;
+  // 128-key splits in small states: there a 256-key split holds mostly
+  // positions past the keys, and the halved staging and scores outweigh the
+  // combine's extra partials (8B shapes, attention + combine a layer: 11.1
+  // against 13.4 us at ctx 256, 13.2 against 15.1 at ctx 1024; 16.5 against
+  // 15.8 at ctx 1536, where 256-key splits stay)
+  s->split = t->act != T_F32 && t->d.head_dim == 128 && s->capacity <= ATTN_SMALL_CAP ? ATTN_SPLIT_SMALL : ATTN_SPLIT;
+  s->max_splits = (s->capacity + s->split - 1) / s->split;
   if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
   // dense prompt chunks: an int4 or bf16 target (the projections have the
   // dense kernel; GatedDeltaNet layers run the chunk's recurrence B tokens
@@ -706,7 +713,7 @@ static int attn_layer(dflash_state* s, const dflash_model* m, int l, const Layer
   AttnCall ac;
   ac.q = s->bq; ac.atype = m->act; ac.kc = rc.kc; ac.vc = rc.vc; ac.page_table = s->pt;
   ac.dev_n = s->scal + SC_N; ac.block_rows = B; ac.causal = draft ? 0 : 1;
-  ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits; ac.npages = s->pages;
+  ac.hq = hq; ac.hkv = hkv; ac.d = hd; ac.max_splits = s->max_splits; ac.npages = s->pages; ac.split = s->split;
   ac.o_part = s->o_part; ac.ml_part = s->ml_part; ac.out = s->ba; ac.otype = m->gin; ac.ldo = hq * hd;
   ac.status = s->scal + SC_STATUS;
   HIPCHK(launch_attention(ac, st));

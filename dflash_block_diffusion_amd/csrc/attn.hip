@@ -16,7 +16,8 @@
 // (causal=0): every block slot sees every committed context row and every
 // block slot (the drafter denoises the block in one bidirectional pass,
 // mlx-dspark v0.0.3 "Highlights").  Split-KV: each work-group takes 256 keys
-// of one KV head for all G*B query rows of that head (GQA) and writes an
+// (128 in small states) of one KV head for all G*B query rows of that head
+// (GQA) and writes an
 // unnormalised partial (o, max, sum); attn_combine merges the splits -- the
 // two-pass structure of the long-context verify attention in the dflash-mlx
 // note ("Technical challenges", JIT SDPA 2-pass for N >= 1024), here used at
@@ -115,7 +116,6 @@ struct AttnArgs {
   float* o_part; float* ml_part;
 };
 
-constexpr int ATTN_PAGES = ATTN_SPLIT / PAGE;       // pages per work-group (4)
 
 
 
@@ -147,12 +147,14 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){lo, hi}, bf16x2v));
 }
 
-// head_dim 128, bf16 q/k/v.  Work-group = (split of 256 keys, KV head, group
-// of NW row blocks), one wave per 16-row block of the head's G*B query rows
-// (row r = token r/G, query head h*G + r%G).
-//  1. Every wave issues its share of the 4 K pages and 4 V^T pages as
-//     direct global->LDS 16-byte loads (128 KiB in flight per work-group, no
-//     registers held).  16-byte granules are XOR-swizzled inside each row so
+// head_dim 128, bf16 q/k/v.  Work-group = (split of 64*ATTN_PAGES keys: 256,
+// or 128 for states of at most ATTN_SMALL_CAP positions, where most of a
+// 256-key split would be past the keys; KV head; group of NW row blocks), one
+// wave per 16-row block of the head's G*B query rows (row r = token r/G,
+// query head h*G + r%G).
+//  1. Every wave issues its share of the split's K pages and V^T pages as
+//     direct global->LDS 16-byte loads (128 or 64 KiB in flight per
+//     work-group, no registers held).  16-byte granules are XOR-swizzled inside each row so
 //     that the fragment reads below hit 16 different bank groups:
 //       K page  granule (key, c = d/8)    at key*16 + (c ^ kswz(key))
 //       V^T page granule (d, c = key/8)   at d*8 + (c ^ ((d >> 1) & 7))
@@ -168,12 +170,13 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 // NW waves per work-group (4 or 8): with 8, one staging of a split's K / V^T
 // serves all 8 row blocks of a 32-token block's 128 query rows per KV head
 // (G = 4), so each split is read from HBM once, not once per 4 row blocks.
-template <int NW>
+template <int NW, int ATTN_PAGES>
 __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
+  constexpr int SPLIT = ATTN_PAGES * PAGE;     // keys per split
   constexpr int BPW = 16 / NW;                 // 1 KiB DMA blocks per page and wave
   constexpr int DMAS = BPW * ATTN_PAGES;       // V^T DMAs per wave (and K DMAs)
-  constexpr int NT = ATTN_SPLIT / 16;          // 16-key tiles per split
+  constexpr int NT = SPLIT / 16;               // 16-key tiles per split
   // K and V^T staging as two LDS objects, so that waiting for the K loads
   // does not also wait for the V^T loads
   __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   const int h = Lw % a.hkv;
   const int rest = Lw / a.hkv;
   const int sidx = rest % gridDim.x, zg = rest / gridDim.x;   // split, row group
-  const int key0 = sidx * ATTN_SPLIT;
+  const int key0 = sidx * SPLIT;
   const int G = a.hq / a.hkv;
   const int nrb = G * a.B / 16;
 
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   //    Splits that end at or before n are visible to every row (the whole
   //    committed context), so only the split holding the block needs the
   //    mask.
-  const bool full = key0 + ATTN_SPLIT <= n;    // uniform
+  const bool full = key0 + SPLIT <= n;         // uniform
   float mx = -INFINITY;
   float lsum = 0.f;
   uint32_t ph[NT / 2][4], pl[NT / 2][4];
@@ -625,8 +628,8 @@ constexpr int COMBINE_MAX_SPLITS = 32;
 
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
-                                                          int max_splits, int B, int hq, int d, void* out, int otype,
-                                                          int ldo, int32_t* status, int hkv) {
+                                                          int max_splits, int split, int B, int hq, int d, void* out,
+                                                          int otype, int ldo, int32_t* status, int hkv) {
   // work-group L takes a row of KV head L mod hkv (the XCD whose L2 received
   // that head's partials from the attention)
   const int G = hq / hkv;
@@ -636,7 +639,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const size_t stride = (size_t)B * hq;
   const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
   const int kv_len = *dev_n + B;
-  const int ns = min((kv_len + ATTN_SPLIT - 1) / ATTN_SPLIT, max_splits);
+  const int ns = min((kv_len + split - 1) / split, max_splits);
   float ms[COMBINE_MAX_SPLITS], ls[COMBINE_MAX_SPLITS], o0[COMBINE_MAX_SPLITS], o1[COMBINE_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
@@ -686,6 +689,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   const float scale2 = LOG2E / sqrtf((float)c.d);
   dim3 grid(c.max_splits, c.hkv);
   if (c.atype == T_F32) {
+    if (c.split != ATTN_SPLIT) return hipErrorInvalidValue;
     if (c.d == 64)
       hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(256), 0, s, (const float*)c.q, (const float*)c.kc,
                          (const float*)c.vc, c.page_table, c.dev_n, c.block_rows, c.causal, c.hq, c.hkv, scale2,
@@ -717,16 +721,26 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     // capacity (max_splits), not by the live context, so that one captured
     // graph serves every context length: a state whose capacity passes the
     // threshold runs the eight-wave shape at every length.
-    if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > device_cus())
-      hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+    if (c.split != ATTN_SPLIT && (c.split != ATTN_SPLIT_SMALL || c.d != 128)) return hipErrorInvalidValue;
+    const bool small = c.split == ATTN_SPLIT_SMALL;
+    if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > device_cus()) {
+      if (small)
+        hipLaunchKernelGGL((attn_mfma_kernel<8, 2>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<8, 4>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
+    } else {
+      if (small)
+        hipLaunchKernelGGL((attn_mfma_kernel<4, 2>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<4, 4>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
-                     c.dev_n, c.max_splits, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status, c.hkv);
+                     c.dev_n, c.max_splits, c.split, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status,
+                     c.hkv);
   return hipGetLastError();
 }
 

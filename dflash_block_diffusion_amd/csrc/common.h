@@ -13,7 +13,9 @@ enum ElemType { T_F32 = 0, T_BF16 = 1, T_F16 = 2 };
 enum WFmt { W_F32 = 0, W_BF16 = 1, W_W8 = 2, W_W4 = 3 };
 
 constexpr int PAGE = 64;         // tokens per KV page
-constexpr int ATTN_SPLIT = 256;  // keys per attention work-group (4 pages)
+constexpr int ATTN_SPLIT = 256;  // keys per attention work-group (4 pages) ...
+constexpr int ATTN_SPLIT_SMALL = 128;  // ... or 2 pages, for states of at most ATTN_SMALL_CAP positions
+constexpr int ATTN_SMALL_CAP = 1792;
 constexpr int MAX_ROWS = 64;     // max GEMM rows (tokens) per call
 
 inline int elem_bytes(int t) { return t == T_F32 ? 4 : 2; }
@@ -219,7 +221,8 @@ struct AttnCall {
   const void* q; int atype;                  // [B][hq][d] act (bf16 or f32)
   const void* kc; const void* vc; const int* page_table;
   const int* dev_n; int block_rows; int causal;
-  int hq, hkv, d; int max_splits; int npages;  // splits of ATTN_SPLIT keys; pages in the table
+  int hq, hkv, d; int max_splits; int npages;  // key splits of the state; pages in the table
+  int split = ATTN_SPLIT;                     // keys per split (ATTN_SPLIT or ATTN_SPLIT_SMALL)
   float* o_part; float* ml_part;              // [max_splits][B*hq][d], [max_splits][B*hq][2]
   void* out; int otype; int ldo;              // [B][hq*d]
   int32_t* status;                            // range flag of fp16 outputs (or null)
