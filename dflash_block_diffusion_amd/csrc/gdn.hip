@@ -398,21 +398,36 @@ __global__ __launch_bounds__(4 * DV) void gdn_replay_kernel(float* S_all, const 
                                                             const int32_t* d_acc, int host_count,
                                                             const int32_t* scal, int capacity) {
   constexpr int REC = DK + DV + 2;
-  __shared__ float rec[REC];
+  constexpr int NT = 4 * DV;
+  constexpr int PERT = (GDN_MAXT * REC + NT - 1) / NT;
+  __shared__ float recs[GDN_MAXT][REC];
   const int cnt = d_acc ? d_acc[0] + 1 : host_count;
   if (scal[SC_N] + cnt + B > capacity) return;      // the commit will be refused
+  if (cnt > GDN_MAXT) return;                       // (B <= GDN_MAXT: not reached)
   const int h = blockIdx.x, l = blockIdx.y;
   const int tid = threadIdx.x, i = tid >> 2, r = tid & 3;
   float* Sg = S_all + (((size_t)l * gh + h) * DV + i) * DK;
+  const float* tape = tape_all + (size_t)l * B * gh * REC;
+  // every committed token's record in one round of loads, issued together
+  // with the state row's, then into LDS: the token loop below reads no
+  // global memory
+  float v[PERT];
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {
+    const int e = tid + u * NT;
+    v[u] = e < cnt * REC ? tape[((size_t)(e / REC) * gh + h) * REC + e % REC] : 0.f;
+  }
   float S[DK / 4];
 #pragma unroll
   for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
-  const float* tape = tape_all + (size_t)l * B * gh * REC;
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {
+    const int e = tid + u * NT;
+    if (e < cnt * REC) recs[e / REC][e % REC] = v[u];
+  }
+  __syncthreads();
   for (int t = 0; t < cnt; ++t) {
-    __syncthreads();
-    const float* tr = tape + ((size_t)t * gh + h) * REC;
-    for (int e = tid; e < REC; e += 4 * DV) rec[e] = tr[e];
-    __syncthreads();
+    const float* rec = recs[t];
     apply_token<DK>(S, rec, rec[DK + i], rec[DK + DV], rec[DK + DV + 1], r);
   }
 #pragma unroll
