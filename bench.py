@@ -309,6 +309,9 @@ def main():
               f"MI355X (requested --gpus {args.gpus}); the library uses no second GPU.",
               file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
