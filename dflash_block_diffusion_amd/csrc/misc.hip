@@ -136,9 +136,120 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
   store8_act(c.out, o, c.otype, y, c.status);
 }
 
+// The case every bf16-activation step takes: a bf16 residual stream, a tiled
+// 16-bit output (OT = T_BF16, or T_F16 for the fp16 encoding of the bf16
+// value), SS pending splits (0: NORM_ONLY) and h a multiple of 512, so that
+// every thread owns exactly one chunk and every wave is full.  The arithmetic
+// and its order are norm_kernel's; what goes is the run-time type and mode
+// dispatch, the dead-lane handling and the per-element range atomics (one
+// atomic per wave that met an out-of-range fp16 code), which on this
+// one-wave-chain-per-row kernel cost about as much time as the memory round
+// trips.
+template <int OT>
+__device__ __forceinline__ uint4 pack8_act(const float (&y)[8], bool& bad) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
+    if (OT == T_F16) {
+      const float fl = bf16_bits_to_f32(lo), fh = bf16_bits_to_f32(hi);
+      bad = bad || !(fabsf(fl) <= 65504.0f) || !(fabsf(fh) <= 65504.0f);
+      lo = __builtin_bit_cast(uint16_t, (_Float16)fl);
+      hi = __builtin_bit_cast(uint16_t, (_Float16)fh);
+    }
+    w[e] = lo | (hi << 16);
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+template <int SS, int OT>
+__global__ __launch_bounds__(1024) void norm_bf16_kernel(NormCall c) {
+  const int row = blockIdx.x;
+  const int j0 = threadIdx.x * 8;
+  float4 pa[SS > 0 ? SS : 1], pb[SS > 0 ? SS : 1];
+  if (SS > 0) {
+    const float* q = c.in.p + (size_t)row * c.in.ld + j0;
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      pa[s] = *(const float4*)(q + (size_t)s * c.in.stride);
+      pb[s] = *(const float4*)(q + (size_t)s * c.in.stride + 4);
+    }
+  }
+  uint16_t* xr = (uint16_t*)c.x + (size_t)row * c.ldx + j0;
+  const uint4 xw = *(const uint4*)xr;
+  const float4 g0 = *(const float4*)(c.gain + j0), g1 = *(const float4*)(c.gain + j0 + 4);
+  const uint32_t w[4] = {xw.x, xw.y, xw.z, xw.w};
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+  if (SS > 0) {
+    // the splits are added in split order
+    float y[8] = {pa[0].x, pa[0].y, pa[0].z, pa[0].w, pb[0].x, pb[0].y, pb[0].z, pb[0].w};
+#pragma unroll
+    for (int s = 1; s < SS; ++s) {
+      y[0] = y[0] + pa[s].x; y[1] = y[1] + pa[s].y; y[2] = y[2] + pa[s].z; y[3] = y[3] + pa[s].w;
+      y[4] = y[4] + pb[s].x; y[5] = y[5] + pb[s].y; y[6] = y[6] + pb[s].z; y[7] = y[7] + pb[s].w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e] + round_bf16(y[e]));
+    bool unused = false;
+    *(uint4*)xr = pack8_act<T_BF16>(v, unused);
+    if (c.side) {
+      const int col = c.side_col0 + j0;
+      const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
+      store8_act(c.side, o, c.side_type, v, c.status);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  ss = wave_sum(ss);
+  __shared__ float part[16];
+  const int nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  // fixed-order sum of the wave partials
+  float tot = part[0];
+  for (int i = 1; i < nw; ++i) tot = tot + part[i];
+  const float r = 1.0f / sqrtf(tot / (float)c.h + c.eps);
+  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = v[e] * r * g[e];
+  bool bad = false;
+  *(uint4*)((uint16_t*)c.out + fm_index(row, j0, c.h)) = pack8_act<OT>(y, bad);
+  if (OT == T_F16 && c.status) {
+    const uint64_t b = __ballot(bad);
+    if (b && (threadIdx.x & 63) == __builtin_ctzll(b)) atomicOr(c.status, STATUS_ACT_RANGE);
+  }
+}
+
+template <int SS>
+static void launch_norm_bf16(const NormCall& c, hipStream_t s) {
+  const dim3 grid(c.rows), block(c.h / 8);
+  if (c.otype == T_F16) hipLaunchKernelGGL((norm_bf16_kernel<SS, T_F16>), grid, block, 0, s, c);
+  else hipLaunchKernelGGL((norm_bf16_kernel<SS, T_BF16>), grid, block, 0, s, c);
+}
+
 hipError_t launch_norm(const NormCall& c, hipStream_t s) {
   if (c.rows <= 0) return hipSuccess;
   if (c.h % 8 || c.h > 8 * 1024 || c.in.S > MAX_SPLITS) return hipErrorInvalidValue;
+  const bool bf16_path = c.xtype == T_BF16 && c.tiled && (c.otype == T_F16 || c.otype == T_BF16) &&
+                         c.h % 512 == 0 && (c.mode == NORM_ONLY || (c.mode == NORM_RESID && c.in.S >= 1));
+  if (bf16_path) {
+    switch (c.mode == NORM_ONLY ? 0 : c.in.S) {
+      case 0: launch_norm_bf16<0>(c, s); break;
+      case 1: launch_norm_bf16<1>(c, s); break;
+      case 2: launch_norm_bf16<2>(c, s); break;
+      case 3: launch_norm_bf16<3>(c, s); break;
+      case 4: launch_norm_bf16<4>(c, s); break;
+      case 5: launch_norm_bf16<5>(c, s); break;
+      case 6: launch_norm_bf16<6>(c, s); break;
+      case 7: launch_norm_bf16<7>(c, s); break;
+      default: launch_norm_bf16<8>(c, s); break;
+    }
+    return hipGetLastError();
+  }
   const int threads = ((c.h / 8 + 63) / 64) * 64;
   hipLaunchKernelGGL(norm_kernel, dim3(c.rows), dim3(threads), 0, s, c);
   return hipGetLastError();
