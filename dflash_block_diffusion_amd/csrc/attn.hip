@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
   // the QKV projection is materialised in the activation format
   const float x1 = act ? act_round(c.atype, parts_add(c.qkv, q1)) : 0.f;
   const float x2 = act ? act_round(c.atype, parts_add(c.qkv, q2)) : 0.f;
-  const float ss = wave_sum(x1 * x1 + x2 * x2);
+  const float ss = wave_sum_full(x1 * x1 + x2 * x2);   // every lane of the wave is active here
   const float r = 1.0f / sqrtf(ss / (float)d + c.eps);
   const float a = x1 * r * g1;
   const float b = x2 * r * g2;
@@ -139,13 +139,6 @@ __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32
 // {8a + 4h + b : a, b < 4} that one score tile reads (h fixed) fall in 16
 // different bank groups
 __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
-
-// two fp32 values rounded to nearest-even bf16, packed (v_cvt_pk_bf16_f32)
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float floatx2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){lo, hi}, bf16x2v));
-}
 
 // head_dim 128, bf16 q/k/v.  Work-group = (split of 64*ATTN_PAGES keys: 256,
 // or 128 for states of at most ATTN_SMALL_CAP positions, where most of a

@@ -42,6 +42,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rn;
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+// two fp32 values rounded to nearest-even bf16 and packed, low half first: one
+// v_cvt_pk_bf16_f32, equal to f32_to_bf16_bits on every non-NaN input
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float floatx2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){lo, hi}, bf16x2v));
+}
 
 // Load one activation element as fp32.
 __device__ __forceinline__ float load_act(const void* p, size_t i, int t) {
@@ -98,6 +105,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over a full wave (every lane active), left in every lane: DPP steps
+// inside each row of 16 lanes (quad swaps, then the 8- and 16-lane mirrors,
+// after which all 16 lanes hold the row's sum bit for bit), then the four
+// row sums in a fixed order.  No LDS round trip.
+#define DFL_DPP_ADD(v, ctrl) \
+  ((v) + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, true)))
+__device__ __forceinline__ float wave_sum_full(float v) {
+  v = DFL_DPP_ADD(v, 0xB1);   // quad_perm [1,0,3,2]
+  v = DFL_DPP_ADD(v, 0x4E);   // quad_perm [2,3,0,1]
+  v = DFL_DPP_ADD(v, 0x141);  // row_half_mirror
+  v = DFL_DPP_ADD(v, 0x140);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+#undef DFL_DPP_ADD
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

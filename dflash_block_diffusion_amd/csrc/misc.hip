@@ -136,32 +136,36 @@ __global__ __launch_bounds__(1024) void norm_kernel(NormCall c) {
   store8_act(c.out, o, c.otype, y, c.status);
 }
 
-// The case every bf16-activation step takes: a bf16 residual stream, a tiled
-// 16-bit output (OT = T_BF16, or T_F16 for the fp16 encoding of the bf16
-// value), SS pending splits (0: NORM_ONLY) and h a multiple of 512, so that
-// every thread owns exactly one chunk and every wave is full.  The arithmetic
-// and its order are norm_kernel's; what goes is the run-time type and mode
-// dispatch, the dead-lane handling and the per-element range atomics (one
-// atomic per wave that met an out-of-range fp16 code), which on this
-// one-wave-chain-per-row kernel cost about as much time as the memory round
-// trips.
+// 8 fp32 values -> 8 16-bit codes: bf16 (round to nearest even), or for
+// OT = T_F16 the fp16 encoding of that bf16 value; bad is set when an fp16
+// code lies outside the finite fp16 range
 template <int OT>
 __device__ __forceinline__ uint4 pack8_act(const float (&y)[8], bool& bad) {
   uint32_t w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    uint32_t lo = f32_to_bf16_bits(y[2 * e]), hi = f32_to_bf16_bits(y[2 * e + 1]);
+    w[e] = pack_bf16_rne(y[2 * e], y[2 * e + 1]);
     if (OT == T_F16) {
-      const float fl = bf16_bits_to_f32(lo), fh = bf16_bits_to_f32(hi);
+      const float fl = __uint_as_float(w[e] << 16), fh = __uint_as_float(w[e] & 0xffff0000u);
       bad = bad || !(fabsf(fl) <= 65504.0f) || !(fabsf(fh) <= 65504.0f);
-      lo = __builtin_bit_cast(uint16_t, (_Float16)fl);
-      hi = __builtin_bit_cast(uint16_t, (_Float16)fh);
+      w[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)fl) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)fh) << 16);
     }
-    w[e] = lo | (hi << 16);
   }
   return uint4{w[0], w[1], w[2], w[3]};
 }
 
+// The case every bf16-activation step takes: a bf16 residual stream, a tiled
+// 16-bit output (OT = T_BF16, or T_F16 for the fp16 encoding of the bf16
+// value), SS pending splits (0: NORM_ONLY) and h a multiple of 512, so that
+// every thread owns exactly one chunk and every wave is full.  The arithmetic
+// and its order are norm_kernel's; what goes is the run-time type and mode
+// dispatch, the dead-lane handling, the per-element range atomics (one
+// atomic per wave that met an out-of-range fp16 code), the integer bf16
+// rounding (one v_cvt_pk_bf16_f32 per pair instead) and the LDS shuffles of
+// the wave sum (DPP instead), which on this one-wave-chain-per-row kernel
+// cost about as much time as the memory round trips: 6.2 -> 4.0 us a launch
+// at 32 rows x 4096.  Only the wave sum's association order differs.
 template <int SS, int OT>
 __global__ __launch_bounds__(1024) void norm_bf16_kernel(NormCall c) {
   const int row = blockIdx.x;
@@ -190,10 +194,15 @@ __global__ __launch_bounds__(1024) void norm_bf16_kernel(NormCall c) {
       y[0] = y[0] + pa[s].x; y[1] = y[1] + pa[s].y; y[2] = y[2] + pa[s].z; y[3] = y[3] + pa[s].w;
       y[4] = y[4] + pb[s].x; y[5] = y[5] + pb[s].y; y[6] = y[6] + pb[s].z; y[7] = y[7] + pb[s].w;
     }
+    uint32_t nb[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e] + round_bf16(y[e]));
-    bool unused = false;
-    *(uint4*)xr = pack8_act<T_BF16>(v, unused);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t r = pack_bf16_rne(y[2 * e], y[2 * e + 1]);
+      nb[e] = pack_bf16_rne(v[2 * e] + __uint_as_float(r << 16), v[2 * e + 1] + __uint_as_float(r & 0xffff0000u));
+      v[2 * e] = __uint_as_float(nb[e] << 16);
+      v[2 * e + 1] = __uint_as_float(nb[e] & 0xffff0000u);
+    }
+    *(uint4*)xr = uint4{nb[0], nb[1], nb[2], nb[3]};
     if (c.side) {
       const int col = c.side_col0 + j0;
       const size_t o = c.side_type == T_F32 ? (size_t)row * c.ld_side + col : fm_index(row, col, c.ld_side);
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(1024) void norm_bf16_kernel(NormCall c) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-  ss = wave_sum(ss);
+  ss = wave_sum_full(ss);
   __shared__ float part[16];
   const int nw = blockDim.x >> 6;
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
