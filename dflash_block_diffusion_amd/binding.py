@@ -85,6 +85,7 @@ SIGNATURES = {
     "dflash_prof_enable": (c_int, [c_void_p, c_int]),
     "dflash_prof_replay": (c_int, [c_void_p, c_char_p, c_int, c_void_p, POINTER(c_double), POINTER(c_int64)]),
     "dflash_read_floor": (c_int, [c_void_p, c_size_t, c_int, c_int, c_int, c_void_p, c_void_p, POINTER(c_double)]),
+    "dflash_check_bf16_rounding": (c_int, [c_void_p, c_void_p, POINTER(c_uint64)]),
     "dflash_prof_read": (c_int, [c_void_p, POINTER(c_char_p), POINTER(c_int64), POINTER(c_double),
                                  POINTER(c_double), POINTER(c_double), c_int, POINTER(c_int)]),
 }

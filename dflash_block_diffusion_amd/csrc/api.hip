@@ -1289,6 +1289,7 @@ extern "C" int dflash_prof_replay(dflash_state* s, const char* variant, int reps
 
 namespace dfl {
 hipError_t launch_read_floor(const void* buf, size_t bytes, int nwg, uint32_t* sink, hipStream_t s);
+hipError_t launch_bf16_round_check(unsigned long long* counts, hipStream_t s);
 }
 
 extern "C" int dflash_read_floor(const void* d_buf, size_t bytes, int copies, int nwg, int reps, uint32_t* d_sink,
@@ -1339,5 +1340,15 @@ extern "C" int dflash_prof_read(dflash_state* s, const char** names, int64_t* la
     if (bytes) bytes[i] = tb[i];
     if (io_bytes) io_bytes[i] = tio[i];
   }
+  return DFLASH_OK;
+}
+
+extern "C" int dflash_check_bf16_rounding(uint64_t* d_counts, void* stream, uint64_t* h_counts) {
+  if (!d_counts || !h_counts) return fail(DFLASH_E_INVALID, "bad argument");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(launch_fill_i32((int32_t*)d_counts, 4, 0, st));
+  HIPCHK(launch_bf16_round_check((unsigned long long*)d_counts, st));
+  HIPCHK(hipMemcpyAsync(h_counts, d_counts, 2 * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
   return DFLASH_OK;
 }

@@ -455,4 +455,29 @@ hipError_t launch_read_floor(const void* buf, size_t bytes, int nwg, uint32_t* s
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ bf16 rounding check
+// Every fp32 bit pattern a, paired with b = a ^ 0x9e3779b9 so both halves of
+// the packed conversion see every pattern: pack_bf16_rne (v_cvt_pk_bf16_f32)
+// against the integer round-to-nearest-even f32_to_bf16_bits.  counts[0]
+// gets the mismatches on non-NaN inputs, counts[1] those on NaN inputs.
+__global__ __launch_bounds__(256) void bf16_round_check_kernel(unsigned long long* counts) {
+  unsigned long long bad_num = 0, bad_nan = 0;
+  const uint64_t nthreads = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < (1ull << 32); i += nthreads) {
+    const uint32_t a = (uint32_t)i, b = a ^ 0x9e3779b9u;
+    const uint32_t hw = pack_bf16_rne(__uint_as_float(a), __uint_as_float(b));
+    const uint32_t sw = f32_to_bf16_bits(__uint_as_float(a)) | (f32_to_bf16_bits(__uint_as_float(b)) << 16);
+    const bool nan_a = (a & 0x7fffffffu) > 0x7f800000u, nan_b = (b & 0x7fffffffu) > 0x7f800000u;
+    if ((hw ^ sw) & 0xffffu) { if (nan_a) ++bad_nan; else ++bad_num; }
+    if ((hw ^ sw) >> 16) { if (nan_b) ++bad_nan; else ++bad_num; }
+  }
+  if (bad_num) atomicAdd(&counts[0], bad_num);
+  if (bad_nan) atomicAdd(&counts[1], bad_nan);
+}
+
+hipError_t launch_bf16_round_check(unsigned long long* counts, hipStream_t s) {
+  hipLaunchKernelGGL(bf16_round_check_kernel, dim3(16384), dim3(256), 0, s, counts);
+  return hipGetLastError();
+}
+
 }  // namespace dfl

@@ -424,6 +424,17 @@ int dflash_prof_replay(dflash_state *st, const char *variant, int reps,
 int dflash_read_floor(const void *d_buf, size_t bytes, int copies, int nwg, int reps, uint32_t *d_sink,
                       void *stream, double *h_ms);
 
+/* Check of the hardware bf16 rounding the small kernels use: every fp32 bit
+ * pattern is converted by the packed v_cvt_pk_bf16_f32 and by the integer
+ * round-to-nearest-even: the rounding every bf16 activation of the step
+ * goes through (the models of the dflash-mlx note, "Benchmarks" and
+ * "Supported Models", run in bf16).  d_counts: 2 uint64 of device scratch
+ * (cleared by the call);
+ * h_counts[0] receives the mismatches on non-NaN inputs, h_counts[1] on NaN
+ * inputs.  Synchronises the stream.  Errors: DFLASH_E_INVALID for a null
+ * pointer, DFLASH_E_DEVICE if a launch or copy fails. */
+int dflash_check_bf16_rounding(uint64_t *d_counts, void *stream, uint64_t *h_counts);
+
 #ifdef __cplusplus
 }
 #endif

@@ -258,3 +258,15 @@ def test_linear_dense_w4_full_size_sampled(name, n, k, m):
         got = y[:, r0:r0 + 16]
         assert np.all(np.abs(got - ref) <= bound(x, w, rows=(int(r0), int(r0) + 16))), (name, r0)
 
+
+
+def test_bf16_rounding_hardware_equals_integer_rne():
+    """The packed hardware bf16 conversion the norm and attention kernels use
+    rounds every fp32 bit pattern (both halves of the pair) exactly as the
+    integer round-to-nearest-even the other kernels use; NaN inputs too."""
+    from ctypes import c_uint64
+    L = bn.lib()
+    d = torch.zeros(2, dtype=torch.int64, device="cuda")
+    h = (c_uint64 * 2)(7, 7)
+    bn.check(L.dflash_check_bf16_rounding(d.data_ptr(), stream_handle(), h))
+    assert (h[0], h[1]) == (0, 0)
