@@ -114,6 +114,7 @@ struct AttnArgs {
   const int* dev_n; int B; int causal; int hq, hkv; float scale2;   // scale * log2(e)
   int npages;
   float* o_part; float* ml_part;
+  void* out; int otype; int32_t* status;   // final rows when one split holds every key
 };
 
 
@@ -159,7 +160,9 @@ __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) &
 //     values whose sum carries 16 significant bits (p_hi = p truncated,
 //     p_lo = the exact remainder rounded to nearest), O^T = V^T P^T.
 //  3. Unnormalised partial (o, max, sum) per row; attn_combine merges the
-//     splits.
+//     splits.  While the keys fit one split (kv_len <= SPLIT) that split's
+//     work-groups write the normalised rows themselves and the combine
+//     leaves them alone.
 // NW waves per work-group (4 or 8): with 8, one staging of a split's K / V^T
 // serves all 8 row blocks of a 32-token block's 128 query rows per KV head
 // (G = 4), so each split is read from HBM once, not once per 4 row blocks.
@@ -337,6 +340,35 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   // 3. partials: o (unnormalised), m (log2 domain) and l per query row
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  if (kv_len <= SPLIT) {
+    // One split holds every key: the rows are final here and the combine
+    // skips them.  o / l rounded to the O projection's 16-bit input format
+    // (tiled, K = hq*D), the combine's arithmetic for one split; a lane's 4
+    // consecutive columns go out in one 8-byte store.
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    uint16_t* outp = (uint16_t*)a.out;
+    bool bad = false;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint32_t w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        w[e] = pack_bf16_rne(o[dt][2 * e] * inv, o[dt][2 * e + 1] * inv);
+        if (a.otype == T_F16) {
+          const float fl = __uint_as_float(w[e] << 16), fh = __uint_as_float(w[e] & 0xffff0000u);
+          bad = bad || !(fabsf(fl) <= 65504.0f) || !(fabsf(fh) <= 65504.0f);
+          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)fl) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)fh) << 16);
+        }
+      }
+      *(uint2*)(outp + fm_index(tok, qh * D + dt * 16 + 4 * g, a.hq * D)) = uint2{w[0], w[1]};
+    }
+    if (a.otype == T_F16 && a.status) {
+      const uint64_t b = __ballot(bad);
+      if (b && lane == __builtin_ctzll(b)) atomicOr(a.status, STATUS_ACT_RANGE);
+    }
+    return;
+  }
   const size_t row = ((size_t)sidx * a.B + tok) * a.hq + qh;
   float* op = a.o_part + row * D;
 #pragma unroll
@@ -622,7 +654,8 @@ constexpr int COMBINE_MAX_SPLITS = 32;
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
                                                           int max_splits, int split, int B, int hq, int d, void* out,
-                                                          int otype, int ldo, int32_t* status, int hkv) {
+                                                          int otype, int ldo, int32_t* status, int hkv,
+                                                          int direct1) {
   // work-group L takes a row of KV head L mod hkv (the XCD whose L2 received
   // that head's partials from the attention)
   const int G = hq / hkv;
@@ -633,6 +666,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
   const int kv_len = *dev_n + B;
   const int ns = min((kv_len + split - 1) / split, max_splits);
+  if (direct1 && ns == 1) return;             // the attention wrote these rows itself
   float ms[COMBINE_MAX_SPLITS], ls[COMBINE_MAX_SPLITS], o0[COMBINE_MAX_SPLITS], o1[COMBINE_MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
@@ -697,6 +731,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     a.pt = c.page_table; a.dev_n = c.dev_n; a.B = c.block_rows; a.causal = c.causal;
     a.hq = c.hq; a.hkv = c.hkv; a.scale2 = scale2; a.o_part = c.o_part; a.ml_part = c.ml_part;
     a.npages = c.npages;
+    a.out = c.out; a.otype = c.otype; a.status = c.status;
     const int nrb = (c.hq / c.hkv) * c.block_rows / 16;
     if (nrb < 1 || (c.hq / c.hkv) * c.block_rows % 16) return hipErrorInvalidValue;
     if (c.block_rows > 64 && c.causal && c.d == 128 && c.npages <= 128) {
@@ -715,6 +750,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
     // graph serves every context length: a state whose capacity passes the
     // threshold runs the eight-wave shape at every length.
     if (c.split != ATTN_SPLIT && (c.split != ATTN_SPLIT_SMALL || c.d != 128)) return hipErrorInvalidValue;
+    if (c.otype == T_F32) return hipErrorInvalidValue;   // rows of one split are written as 16-bit here
     const bool small = c.split == ATTN_SPLIT_SMALL;
     if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > device_cus()) {
       if (small)
@@ -733,7 +769,7 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
                      c.dev_n, c.max_splits, c.split, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status,
-                     c.hkv);
+                     c.hkv, c.atype != T_F32 ? 1 : 0);
   return hipGetLastError();
 }
 
