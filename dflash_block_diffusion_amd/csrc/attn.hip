@@ -163,22 +163,32 @@ __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) &
 //     splits.  While the keys fit one split (kv_len <= SPLIT) that split's
 //     work-groups write the normalised rows themselves and the combine
 //     leaves them alone.
-// NW waves per work-group (4 or 8): with 8, one staging of a split's K / V^T
-// serves all 8 row blocks of a 32-token block's 128 query rows per KV head
-// (G = 4), so each split is read from HBM once, not once per 4 row blocks.
-template <int NW, int ATTN_PAGES>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
+// NW row-block waves per work-group (4 or 8): with 8, one staging of a
+// split's K / V^T serves all 8 row blocks of a 32-token block's 128 query
+// rows per KV head (G = 4), so each split is read from HBM once, not once per
+// 4 row blocks.  KH = 2 gives each row block two waves, one per half of the
+// split's keys (the halves' partials merged in LDS before the write): twice
+// the waves on the same staging, half the dependent score / softmax / P.V
+// chain per wave; a half wholly past the keys skips its work.
+template <int NW, int ATTN_PAGES, int KH>
+__global__ __launch_bounds__(64 * NW * KH) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int SPLIT = ATTN_PAGES * PAGE;     // keys per split
-  constexpr int BPW = 16 / NW;                 // 1 KiB DMA blocks per page and wave
+  constexpr int NWT = NW * KH;                 // waves per work-group
+  constexpr int BPW = 16 / NWT;                // 1 KiB DMA blocks per page and wave
   constexpr int DMAS = BPW * ATTN_PAGES;       // V^T DMAs per wave (and K DMAs)
   constexpr int NT = SPLIT / 16;               // 16-key tiles per split
+  constexpr int NTH = NT / KH;                 // 16-key tiles of one key part
+  static_assert(KH == 1 || KH == 2, "one or two key parts");
+  static_assert((NTH / 2) % 2 == 0, "a key part holds whole 64-key pages");
   // K and V^T staging as two LDS objects, so that waiting for the K loads
   // does not also wait for the V^T loads
   __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
   __shared__ __attribute__((aligned(16))) uint8_t ldsV[ATTN_PAGES * 16384];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave of the work-group
+  const int wave = wt % NW;                    // its row block in the group
+  const int kh = wt / NW;                      // its key part: tiles [kh*NTH, (kh+1)*NTH)
   const int lr = lane & 15, g = lane >> 4;
   // work-group L takes KV head L mod hkv: the XCDs take work-groups
   // round-robin, so with hkv = 8 all of a KV head's splits (and both row
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   uint32_t koff[BPW], voff[BPW];
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
-    const int q = (wave + NW * j) * 64 + lane;  // 16-byte granule of the 16 KiB region
+    const int q = (wt + NWT * j) * 64 + lane;   // 16-byte granule of the 16 KiB region
     const int key = q >> 4, ck = (q & 15) ^ kswz(key);
     const int d = q >> 3, cv = (q & 7) ^ ((d >> 1) & 7);
     koff[j] = (uint32_t)(key * D + ck * 8) * 2u;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
       const uint16_t* base = (half == 0 ? a.kc : a.vc) + pbase;
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
-        uint8_t* dst = (half == 0 ? ldsK : ldsV) + (size_t)p * 16384 + (wave + NW * j) * 1024;
+        uint8_t* dst = (half == 0 ? ldsK : ldsV) + (size_t)p * 16384 + (wt + NWT * j) * 1024;
         dma16_s(half == 0 ? koff[j] : voff[j], base, lds_addr(dst));
       }
     }
@@ -248,10 +258,12 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   //    committed context), so only the split holding the block needs the
   //    mask.
   const bool full = key0 + SPLIT <= n;         // uniform
+  // a key part wholly past the keys contributes nothing (m = -inf, l = 0)
+  const bool work = live && key0 + kh * (SPLIT / KH) < kv_len;   // wave-uniform
   float mx = -INFINITY;
   float lsum = 0.f;
-  uint32_t ph[NT / 2][4], pl[NT / 2][4];
-  if (live) {
+  uint32_t ph[NTH / 2][4], pl[NTH / 2][4];
+  if (work) {
     // Score tile kt = 2*ks2 + hh puts key 32*ks2 + 8*(i/4) + 4*hh + i%4 in
     // its row i, so that after the MFMA a lane (lr, g) holds keys
     // 32*ks2 + 8g + 4hh + v (v < 4): the 8 keys it feeds to the P.V step are
@@ -261,9 +273,10 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
     uint32_t kb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kb[ks] = (uint32_t)((8 * (lr >> 2) + (lr & 3)) * 256 + (((4 * ks + g) ^ lr) << 4));
-    floatx4 acc[NT];
+    floatx4 acc[NTH];
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
+    for (int j = 0; j < NTH; ++j) {
+      const int kt = kh * NTH + j;
       const int ks2 = kt >> 1, hh = kt & 1;
       const uint8_t* kt_base = ldsK + (ks2 >> 1) * 16384 + (32 * (ks2 & 1) + 4 * hh) * 256;
       floatx4 c = {0.f, 0.f, 0.f, 0.f};
@@ -272,19 +285,21 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4*)(kt_base + kb[ks]));
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], c, 0, 0, 0);
       }
-      acc[kt] = c;
+      acc[j] = c;
     }
     if (!full) {
       const int kmax = a.causal ? n + tok : kv_len - 1;     // last key this row sees
 #pragma unroll
-      for (int kt = 0; kt < NT; ++kt)
+      for (int j = 0; j < NTH; ++j) {
+        const int kt = kh * NTH + j;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (key0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + v > kmax) acc[kt][v] = -INFINITY;
+          if (key0 + 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + v > kmax) acc[j][v] = -INFINITY;
+      }
     }
     // the row max on the raw scores (scale2 > 0)
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(acc[kt][0], acc[kt][1]), fmaxf(acc[kt][2], acc[kt][3])));
+    for (int j = 0; j < NTH; ++j) mx = fmaxf(mx, fmaxf(fmaxf(acc[j][0], acc[j][1]), fmaxf(acc[j][2], acc[j][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // masked scores are -inf, so exp2 of them is 0; a row with no visible key
@@ -292,8 +307,8 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
     const float ms = mx == -INFINITY ? 0.f : mx * a.scale2;
     mx = mx == -INFINITY ? -INFINITY : ms;       // the partial's max, log2 domain
 #pragma unroll
-    for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
-      // B operand: key slots e = hh*4+v <-> key 32*ks2 + 8g + e
+    for (int ks2 = 0; ks2 < NTH / 2; ++ks2) {
+      // B operand: key slots e = hh*4+v <-> key 32*(kh*NTH/2 + ks2) + 8g + e
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         float pe[4], lo[4];
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();                  // every wave's V^T loads are in LDS
-  if (!live) return;
+  if (KH == 1 && !live) return;
   floatx4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -324,22 +339,50 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   uint32_t vb[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) vb[k] = (uint32_t)((lr * 8 + ((4 * k + g) ^ ((lr >> 1) & 7))) * 16);
+  if (work) {
 #pragma unroll
-  for (int ks2 = 0; ks2 < NT / 2; ++ks2) {
-    const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[ks2][0], ph[ks2][1], ph[ks2][2], ph[ks2][3]});
-    const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[ks2][0], pl[ks2][1], pl[ks2][2], pl[ks2][3]});
-    const uint8_t* vpage = ldsV + (ks2 >> 1) * 16384;
+    for (int ks2 = 0; ks2 < NTH / 2; ++ks2) {
+      const bf16x8 pfh = __builtin_bit_cast(bf16x8, uint4{ph[ks2][0], ph[ks2][1], ph[ks2][2], ph[ks2][3]});
+      const bf16x8 pfl = __builtin_bit_cast(bf16x8, uint4{pl[ks2][0], pl[ks2][1], pl[ks2][2], pl[ks2][3]});
+      const uint8_t* vpage = ldsV + ((kh * NTH / 2 + ks2) >> 1) * 16384;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const uint4*)(vpage + dt * 2048 + vb[ks2 & 1]));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, *(const uint4*)(vpage + dt * 2048 + vb[ks2 & 1]));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, o[dt], 0, 0, 0);
+      }
     }
   }
 
   // 3. partials: o (unnormalised), m (log2 domain) and l per query row
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  if (KH == 2) {
+    // The second key part hands its (o, m, l) to the first through LDS (the
+    // K staging, free since every wave passed the barrier after its scores);
+    // the first merges them the way the combine merges splits.
+    __shared__ float ml2[NW][2][16];
+    floatx4* ob = (floatx4*)ldsK + (size_t)wave * 8 * 64;
+    if (kh == 1 && live) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) ob[dt * 64 + lane] = o[dt];
+      if (g == 0) { ml2[wave][0][lr] = mx; ml2[wave][1][lr] = lsum; }
+    }
+    __syncthreads();
+    if (kh == 1 || !live) return;
+    const float m1 = ml2[wave][0][lr], l1 = ml2[wave][1][lr];
+    const float M = fmaxf(mx, m1);
+    const float w0 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - M);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const floatx4 o1 = ob[dt * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[dt][v] = o[dt][v] * w0 + o1[v] * w1;
+    }
+    lsum = lsum * w0 + l1 * w1;
+    mx = M;
+  }
   if (kv_len <= SPLIT) {
     // One split holds every key: the rows are final here and the combine
     // skips them.  o / l rounded to the O projection's 16-bit input format
@@ -740,28 +783,34 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
                          c.status);
       return hipGetLastError();
     }
-    // One work-group fits a CU (128 KiB of LDS).  Eight waves share one K / V^T
-    // staging only when the four-wave grid would spill past the device's CUs
-    // and the row blocks fill whole groups of eight: with fewer splits,
-    // four-wave work-groups spread the score and P.V work over twice the CUs
-    // and are faster (8B shapes, block 32: 3.38 vs 3.53 ms a step at ctx 64,
-    // 4.02 vs 3.88 ms at ctx 4096).  The grid is sized by the state's
-    // capacity (max_splits), not by the live context, so that one captured
-    // graph serves every context length: a state whose capacity passes the
-    // threshold runs the eight-wave shape at every length.
+    // One work-group fits a CU (128 KiB of LDS).  Eight row blocks share one
+    // K / V^T staging only when the four-row-block grid would spill past the
+    // device's CUs and the row blocks fill whole groups of eight: with fewer
+    // splits, four-row-block work-groups spread the score and P.V work over
+    // twice the CUs and are faster (8B shapes, block 32: 3.38 vs 3.53 ms a
+    // step at ctx 64, 4.02 vs 3.88 ms at ctx 4096).  Four-row-block groups
+    // over 256-key splits run two waves per row block, one per half of the
+    // keys (attention + combine 10.5 -> 9.3 us a layer at ctx 64, 17.2 ->
+    // 16.6 at ctx 2048); over 128-key splits the halves are too short to pay
+    // for the merge (7.8 -> 8.1 us at ctx 64), and eight-row-block groups
+    // keep one wave per row block too (with two, 1024 threads, 22.7 -> 24.3
+    // us at ctx 4096).  The grid is sized by the state's capacity
+    // (max_splits), not by the live context, so that one captured graph
+    // serves every context length: a state whose capacity passes the
+    // threshold runs the eight-row-block shape at every length.
     if (c.split != ATTN_SPLIT && (c.split != ATTN_SPLIT_SMALL || c.d != 128)) return hipErrorInvalidValue;
     if (c.otype == T_F32) return hipErrorInvalidValue;   // rows of one split are written as 16-bit here
     const bool small = c.split == ATTN_SPLIT_SMALL;
     if (nrb % 8 == 0 && c.max_splits * c.hkv * (nrb / 4) > device_cus()) {
       if (small)
-        hipLaunchKernelGGL((attn_mfma_kernel<8, 2>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<8, 2, 1>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_mfma_kernel<8, 4>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<8, 4, 1>), dim3(c.max_splits, c.hkv, nrb / 8), dim3(512), 0, s, a);
     } else {
       if (small)
-        hipLaunchKernelGGL((attn_mfma_kernel<4, 2>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<4, 2, 1>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_mfma_kernel<4, 4>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<4, 4, 2>), dim3(c.max_splits, c.hkv, (nrb + 3) / 4), dim3(512), 0, s, a);
     }
   }
   hipError_t e = hipGetLastError();
