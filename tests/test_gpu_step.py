@@ -303,6 +303,19 @@ def test_reduced_8b_lockstep_long_cache_eight_wave_attention():
     assert stats["compared"] >= 4 * cfg.block
 
 
+@pytest.mark.parametrize("P,forced", [(60, [0, 0, 5]), (200, [0, 31, 5])])
+def test_reduced_8b_lockstep_two_key_halves(P, forced):
+    # a 2400-token cache takes 256-key splits on four-row-block work-groups,
+    # with two waves per row block, one per half of a split's keys, merged in
+    # LDS.  Prompt 60: every key in the first half of the first split (the
+    # second half has no key and skips its work, the split writes the final
+    # rows itself); prompt 200: one split with both halves live, then a
+    # second split whose second half is empty
+    cfg = reduced("8b")
+    _, _, stats, _ = lockstep(cfg, P, forced, max_ctx=2400)
+    assert stats["compared"] >= len(forced) * cfg.block
+
+
 @pytest.mark.parametrize("P", [1200, 1025, 700, 545, 96, 33])
 def test_reduced_8b_dense_prompt_chunks_lockstep(P):
     # the whole prompt runs as chunks, the last padded to 16 rows, whose
