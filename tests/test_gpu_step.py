@@ -346,20 +346,24 @@ def test_reduced_4b_dense_prompt_chunks_lockstep(P):
 def test_reduced_8b_lockstep_benchmark_contexts(P, forced):
     # the benchmark's committed contexts (mirror-sd README, "Results":
     # contexts 64 / 2048 / 4096 at block 32).  2048: a 2336-token cache, ten
-    # 256-key splits on the four-wave block attention, nine or ten of them
-    # live; 4096: a 4384-token cache, 18 splits x 8 KV heads x 2 row groups
-    # pass 256 work-groups, so the eight-wave instance runs with 16-17 live
-    # splits and the combine merges all of them
+    # 256-key splits on four-row-block work-groups (two waves a row block,
+    # one per half of the keys), nine or ten of them live; 4096: a 4384-token
+    # cache, 18 splits x 8 KV heads x 2 row groups pass 256 work-groups, so
+    # the eight-row-block instance runs with 16-17 live splits and the
+    # combine merges all of them
     cfg = reduced("8b")
     lockstep(cfg, P, forced)
 
 
-def test_reduced_27b_lockstep_ctx2048():
+@pytest.mark.parametrize("P,forced", [(2048, [0, 31, 12]), (4096, [31, 5, 17])])
+def test_reduced_27b_lockstep_benchmark_contexts(P, forced):
     # 40 / 8 heads: five query heads per KV head, 160 query rows a KV head
-    # at block 32, ten 16-row blocks in three four-wave groups (the last
-    # holding two), over nine or ten live key splits
+    # at block 32, ten 16-row blocks in three four-row-block groups (the last
+    # holding two), over nine or ten live key splits at 2048; at 4096 the 18
+    # splits x 8 KV heads x 3 groups (432 work-groups) take two rounds of the
+    # device's CUs and the combine merges 16-17 live splits
     cfg = reduced("27b")
-    lockstep(cfg, 2048, [0, 31, 12])
+    lockstep(cfg, P, forced)
 
 
 @pytest.mark.parametrize("name,layers", [("4b", 2), ("hybrid", 4)])
