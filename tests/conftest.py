@@ -18,8 +18,10 @@ def pytest_configure(config):
 
 # Parity records: every GPU lockstep appends its measured errors, noise floors
 # and compared / excluded token counts here; the session writes them to
-# gpurun_out/parity_records.json so that the numbers behind each tolerance
-# decision survive the run (pytest itself swallows the test's prints).
+# parity_records.json in the run's results folder (RECORDS_DIR) so that the
+# numbers behind each tolerance decision survive the run (pytest itself
+# swallows the test's prints).
+RECORDS_DIR = "gpurun_out"
 PARITY_RECORDS = []
 CURRENT_TEST = {"id": None}
 
@@ -37,7 +39,7 @@ def record_parity(rec):
     rec = dict(rec)
     rec["test"] = CURRENT_TEST["id"]
     PARITY_RECORDS.append(rec)
-    out = os.path.join(ROOT, "gpurun_out")
+    out = os.path.join(ROOT, RECORDS_DIR)
     os.makedirs(out, exist_ok=True)
     with open(os.path.join(out, "parity_records.json"), "w") as f:
         json.dump(PARITY_RECORDS, f, indent=1)

@@ -22,7 +22,7 @@ model drift apart (one differing bf16 rounding cascades through every later
 materialisation point).  For the bf16 stacks it is 3.5e-2 to 6.2e-2 in the
 logits and one bf16 step of the largest hidden value (0.0625 to 0.25), above
 the 2e-2 bound; for fp32 models it is about 1e-6.  Every lockstep writes its
-errors, floors and counts to gpurun_out/parity_records.json.  Token
+errors, floors and counts to parity_records.json (conftest.py).  Token
 comparisons always use the float64 oracle.  Depth-reduced configurations
 keep the real widths (hidden, heads, FFN, formats) with 2 target layers, 1
 drafter layer and a 32768-token vocab; one test runs the whole 8B-class pair.
@@ -96,7 +96,7 @@ def new_stats():
 
 
 def finish_stats(cfg, P, stats, extra=None):
-    """Record the lockstep's numbers (gpurun_out/parity_records.json) and
+    """Record the lockstep's numbers (parity_records.json) and
     check the compared fraction."""
     tl = tol_logits(cfg)
     rec = dict(stats, config=cfg.name, prompt=P, tol=tl,
