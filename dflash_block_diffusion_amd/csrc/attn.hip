@@ -689,10 +689,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ------------------------------------------------------------ combine
 // Merge the per-split partials of one query row: M = max m_s,
-// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  All split loads of a
-// thread are issued before any is consumed (no dependent load chain).
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, the sums in split order.
+// Lane s holds split s's (m, l) and its weight; lane e's two output elements
+// take the weights from lane s in turn.  All split loads of a lane are issued
+// before any is consumed (no dependent load chain).
 
 constexpr int COMBINE_MAX_SPLITS = 32;
+
+// max over a full wave (every lane active), in every lane: DPP steps inside
+// each row of 16 lanes, then the four row maxima
+#define DFL_DPP_MAX(v, ctrl) \
+  fmaxf((v), __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, true)))
+__device__ __forceinline__ float wave_max_full(float v) {
+  v = DFL_DPP_MAX(v, 0xB1);   // quad_perm [1,0,3,2]
+  v = DFL_DPP_MAX(v, 0x4E);   // quad_perm [2,3,0,1]
+  v = DFL_DPP_MAX(v, 0x141);  // row_half_mirror
+  v = DFL_DPP_MAX(v, 0x140);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+#undef DFL_DPP_MAX
 
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ ml_part, const int* dev_n,
@@ -706,40 +726,45 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const int qh = hk * G + j % G, tok = j / G;
   const int row = tok * hq + qh;
   const size_t stride = (size_t)B * hq;
-  const int e0 = threadIdx.x, e1 = threadIdx.x + 64;
+  const int lane = threadIdx.x;
+  const int e = 2 * lane;                      // this lane's output elements e, e + 1 (d even, <= 128)
+  const bool lv = e < d;
+  // the (m, l) pairs of the state's split slots go out with the committed length
+  float2 ml = {-INFINITY, 0.f};
+  if (lane < max_splits) ml = *(const float2*)(ml_part + ((size_t)lane * stride + row) * 2);
   const int kv_len = *dev_n + B;
   const int ns = min((kv_len + split - 1) / split, max_splits);
   if (direct1 && ns == 1) return;             // the attention wrote these rows itself
-  float ms[COMBINE_MAX_SPLITS], ls[COMBINE_MAX_SPLITS], o0[COMBINE_MAX_SPLITS], o1[COMBINE_MAX_SPLITS];
+  float2 o[COMBINE_MAX_SPLITS];
+  const float* op = o_part + (size_t)row * d + (lv ? e : 0);
+  const size_t sstride = stride * d;           // floats between two splits' rows
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
-    if (s < ns) {
-      const size_t r = s * stride + row;
-      ms[s] = ml_part[r * 2];
-      ls[s] = ml_part[r * 2 + 1];
-      o0[s] = e0 < d ? o_part[r * d + e0] : 0.f;
-      o1[s] = e1 < d ? o_part[r * d + e1] : 0.f;
-    }
+    if (s < ns) o[s] = lv ? *(const float2*)op : float2{0.f, 0.f};
+    op += sstride;
   }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < COMBINE_MAX_SPLITS; ++s)
-    if (s < ns) M = fmaxf(M, ms[s]);
+  if (lane >= ns) ml = float2{-INFINITY, 0.f};
+  const float M = wave_max_full(ml.x);
+  const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+  const int wb = __builtin_bit_cast(int, w);
   float L = 0.f, acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int s = 0; s < COMBINE_MAX_SPLITS; ++s) {
-    if (s < ns && ms[s] != -INFINITY) {
-      const float w = exp2f(ms[s] - M);
-      L += w * ls[s];
-      acc0 += w * o0[s];
-      acc1 += w * o1[s];
+    if (s < ns) {
+      const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, s));
+      const float ls = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ml.y), s));
+      L += ws * ls;
+      acc0 += ws * o[s].x;
+      acc1 += ws * o[s].y;
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   // 16-bit outputs feed the O projection: tiled layout with K = hq*d
   const int fmK = otype == T_F32 ? 0 : hq * d;
-  if (e0 < d) store_act(out, act_index(tok, qh * d + e0, ldo, fmK), otype, acc0 * inv, status);
-  if (e1 < d) store_act(out, act_index(tok, qh * d + e1, ldo, fmK), otype, acc1 * inv, status);
+  if (lv) {
+    store_act(out, act_index(tok, qh * d + e, ldo, fmK), otype, acc0 * inv, status);
+    store_act(out, act_index(tok, qh * d + e + 1, ldo, fmK), otype, acc1 * inv, status);
+  }
 }
 
 // compute units of the current device (looked up once per device)
