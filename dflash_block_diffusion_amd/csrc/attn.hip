@@ -40,8 +40,14 @@ static constexpr float LOG2E = 1.4426950408889634f;
 // work-groups round-robin, so with hkv = 8 (every benchmark shape) the
 // outputs the attention of KV head h reads are written through XCD h's L2,
 // where that attention runs too.
-template <int R>
+// S is the QKV projection's K-split count: the partial sums are loaded as
+// straight-line code (a run-time count made every load conditional and let
+// the compiler wait for all of them at branch boundaries).
+template <int R, int S>
 __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
+  // the committed length and the pending context count go out first (scalar loads)
+  const int n = *c.dev_n;
+  const int p = c.dev_p && !c.ctx_at_n ? *c.dev_p : 0;
   const int L = blockIdx.x + gridDim.x * blockIdx.y;
   const int grp = c.hkv, per = c.hq / c.hkv + 1;       // a KV head's q heads and its k/v head
   const int hk = L % grp, j = L / grp;
@@ -59,25 +65,34 @@ __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
   const int src = head * d;                 // q heads, then k heads, then v heads
   const int vs = (c.hq + c.hkv + kh) * d;
   const float* gain = kv ? c.k_norm : c.q_norm;
-  // the loads that do not depend on the committed length go out with it
-  float q1[MAX_SPLITS], q2[MAX_SPLITS], v1[MAX_SPLITS], v2[MAX_SPLITS];
-  parts_fetch(c.qkv, row, src + i, q1);
-  parts_fetch(c.qkv, row, src + i + half, q2);
+  // every load that does not depend on the committed length
+  const float* base = c.qkv.p + (size_t)row * c.qkv.ld;
+  float q1[S], q2[S], v1[S], v2[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    q1[s] = base[(size_t)s * c.qkv.stride + src + i];
+    q2[s] = base[(size_t)s * c.qkv.stride + src + i + half];
+  }
   if (kv) {
-    parts_fetch(c.qkv, row, vs + i, v1);
-    parts_fetch(c.qkv, row, vs + i + half, v2);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      v1[s] = base[(size_t)s * c.qkv.stride + vs + i];
+      v2[s] = base[(size_t)s * c.qkv.stride + vs + i + half];
+    }
   }
   const float g1 = gain[i], g2 = gain[i + half];
-  const int n = *c.dev_n;
-  const int p = c.dev_p && !c.ctx_at_n ? *c.dev_p : 0;
   const int pos = row < c.block_rows ? n + row : (c.ctx_at_n ? n : n - p) + (row - c.block_rows);
   if ((row >= c.block_rows && !c.ctx_at_n && row - c.block_rows >= p) || pos < 0 || pos >= c.capacity) return;
   const float cs = c.cos_t[(size_t)pos * half + i];
   const float sn = c.sin_t[(size_t)pos * half + i];
   const int page = kv ? c.page_table[pos / PAGE] : 0;
-  // the QKV projection is materialised in the activation format
-  const float x1 = act ? act_round(c.atype, parts_add(c.qkv, q1)) : 0.f;
-  const float x2 = act ? act_round(c.atype, parts_add(c.qkv, q2)) : 0.f;
+  // the QKV projection is materialised in the activation format; the splits
+  // are added in split order
+  float y1 = q1[0], y2 = q2[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) { y1 = y1 + q1[s]; y2 = y2 + q2[s]; }
+  const float x1 = act ? act_round(c.atype, y1) : 0.f;
+  const float x2 = act ? act_round(c.atype, y2) : 0.f;
   const float ss = wave_sum_full(x1 * x1 + x2 * x2);   // every lane of the wave is active here
   const float r = 1.0f / sqrtf(ss / (float)d + c.eps);
   const float a = x1 * r * g1;
@@ -90,21 +105,39 @@ __global__ __launch_bounds__(64 * R) void qk_rope_kernel(RopeCall c) {
     store_act(c.q_out, q + i, c.atype, o1);
     store_act(c.q_out, q + i + half, c.atype, o2);
   } else {
+    float w1 = v1[0], w2 = v2[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) { w1 = w1 + v1[s]; w2 = w2 + v2[s]; }
     const size_t slot = (((size_t)page * c.hkv + kh) * PAGE + (pos % PAGE)) * d;
     store_act(c.kc, slot + i, c.atype, o1);
     store_act(c.kc, slot + i + half, c.atype, o2);
     const size_t vt = ((size_t)page * c.hkv + kh) * PAGE * d + (pos % PAGE);   // V^T page: [d][64]
-    store_act(c.vc, vt + (size_t)i * PAGE, c.atype, parts_add(c.qkv, v1));
-    store_act(c.vc, vt + (size_t)(i + half) * PAGE, c.atype, parts_add(c.qkv, v2));
+    store_act(c.vc, vt + (size_t)i * PAGE, c.atype, w1);
+    store_act(c.vc, vt + (size_t)(i + half) * PAGE, c.atype, w2);
+  }
+}
+
+template <int R>
+static void launch_qk_rope_r(const RopeCall& c, dim3 grid, hipStream_t s) {
+  switch (c.qkv.S) {
+    case 1: hipLaunchKernelGGL((qk_rope_kernel<R, 1>), grid, dim3(64 * R), 0, s, c); break;
+    case 2: hipLaunchKernelGGL((qk_rope_kernel<R, 2>), grid, dim3(64 * R), 0, s, c); break;
+    case 3: hipLaunchKernelGGL((qk_rope_kernel<R, 3>), grid, dim3(64 * R), 0, s, c); break;
+    case 4: hipLaunchKernelGGL((qk_rope_kernel<R, 4>), grid, dim3(64 * R), 0, s, c); break;
+    case 5: hipLaunchKernelGGL((qk_rope_kernel<R, 5>), grid, dim3(64 * R), 0, s, c); break;
+    case 6: hipLaunchKernelGGL((qk_rope_kernel<R, 6>), grid, dim3(64 * R), 0, s, c); break;
+    case 7: hipLaunchKernelGGL((qk_rope_kernel<R, 7>), grid, dim3(64 * R), 0, s, c); break;
+    default: hipLaunchKernelGGL((qk_rope_kernel<R, 8>), grid, dim3(64 * R), 0, s, c); break;
   }
 }
 
 hipError_t launch_qk_rope(const RopeCall& c, hipStream_t s) {
   const int rows = c.block_rows + c.ctx_rows;
+  if (c.qkv.S < 1 || c.qkv.S > MAX_SPLITS) return hipErrorInvalidValue;
   if (rows > 64)
-    hipLaunchKernelGGL(qk_rope_kernel<4>, dim3((rows + 3) / 4, c.hq + c.hkv), dim3(256), 0, s, c);
+    launch_qk_rope_r<4>(c, dim3((rows + 3) / 4, c.hq + c.hkv), s);
   else
-    hipLaunchKernelGGL(qk_rope_kernel<1>, dim3(rows, c.hq + c.hkv), dim3(64), 0, s, c);
+    launch_qk_rope_r<1>(c, dim3(rows, c.hq + c.hkv), s);
   return hipGetLastError();
 }
 
