@@ -222,13 +222,14 @@ void gemm_stream_kernel(GemmArgs a) {
   const int S = a.splits;
   const int sidx = blockIdx.x % S, wr = blockIdx.x / S, PR = gridDim.x / S;
   // row tiles [rtb, rte) of this work-group
-  const int units = a.ntile16 / a.align;
-  const int rtb = (int)((long long)units * wr / PR) * a.align;
-  const int rte = (int)((long long)units * (wr + 1) / PR) * a.align;
+  // 32-bit products: the launcher keeps units * PR and ktiles * S below 2^32
+  const uint32_t units = (uint32_t)(a.ntile16 / a.align);
+  const int rtb = (int)(units * (uint32_t)wr / (uint32_t)PR) * a.align;
+  const int rte = (int)(units * (uint32_t)(wr + 1) / (uint32_t)PR) * a.align;
   const int nch = (rte - rtb + RT - 1) / RT;
   // K tiles [t0, t1) of this wave
-  const int kt0 = (int)((long long)a.ktiles * sidx / S);
-  const int kt1 = (int)((long long)a.ktiles * (sidx + 1) / S);
+  const int kt0 = (int)((uint32_t)a.ktiles * (uint32_t)sidx / (uint32_t)S);
+  const int kt1 = (int)((uint32_t)a.ktiles * (uint32_t)(sidx + 1) / (uint32_t)S);
   const int nk = kt1 - kt0;
   const int t0 = kt0 + nk * wave / NW, t1 = kt0 + nk * (wave + 1) / NW;
   const int nt = t1 - t0;
@@ -718,6 +719,10 @@ static const char* variant_name(int fmt, const Plan& p) {
 hipError_t launch_gemm_plan(const GemmCall& c, const Workspace& w, hipStream_t s, const Plan& p) {
   const GemmW& W = *c.W;
   if (p.S < 1 || p.S > MAX_SPLITS || p.PR < 1 || p.nwg != p.PR * p.S) return hipErrorInvalidValue;
+  // the kernel splits row tiles and K tiles with 32-bit products
+  if (p.align < 1 || (uint64_t)(p.ntile16 / p.align) * p.PR >= (1ull << 32) ||
+      (uint64_t)p.ktiles * p.S >= (1ull << 32))
+    return hipErrorInvalidValue;
   if (p.RT != 2 && p.RT != 3 && p.RT != 4 && p.RT != 6 && p.RT != 8) return hipErrorInvalidValue;
   if (p.MB >= 3 && p.RT != 2) return hipErrorInvalidValue;
   if (p.NW != 4 && !(p.NW == 8 && p.MB == 2)) return hipErrorInvalidValue;
