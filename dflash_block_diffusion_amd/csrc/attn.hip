@@ -256,9 +256,10 @@ __global__ __launch_bounds__(64 * NW * KH) void attn_mfma_kernel(AttnArgs a) {
   // live path uses them, so the compiler would otherwise issue them after the
   // committed length has arrived, one memory round trip later): attention +
   // combine 13.8 -> 13.6 us a layer at ctx 2048, 14.3 -> 13.9 for the 27B
-  // shapes.  Small states leave more of their 128-key splits dead, whose
-  // loads then cost more than the earlier issue saves (10.3 -> 10.5 us).
-  if (KH == 2) asm volatile("" ::: "memory");
+  // shapes, 18.0 -> 17.8 at ctx 4096 (eight row blocks).  Small states leave
+  // more of their 128-key splits dead, whose loads then cost more than the
+  // earlier issue saves (10.3 -> 10.5 us).
+  if (ATTN_PAGES == 4) asm volatile("" ::: "memory");
   const int kv_len = n + a.B;
   if (key0 >= kv_len) return;                 // uniform over the work-group
   // K pages first, then V^T pages (pages past the table re-read the last
