@@ -268,7 +268,8 @@ hipError_t launch_norm(const NormCall& c, hipStream_t s) {
 // other slots the mask token (the drafter's noise block).
 __global__ __launch_bounds__(256) void embed_kernel(const void* __restrict__ table, int ttype, int h, int vocab,
                                                     const int32_t* __restrict__ tokens, int mask_mode,
-                                                    int mask_token, void* out, int ldo, int32_t* status) {
+                                                    int mask_token, void* out, int ldo, int32_t* status,
+                                                    int vec16) {
   const int row = blockIdx.x;
   int tok = (mask_mode && row > 0) ? mask_token : tokens[row];
   if (tok < 0 || tok >= vocab) {
@@ -278,6 +279,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* __restrict__ tab
   const size_t tb = (size_t)tok * h, ob = (size_t)row * ldo;
   if (ttype == T_F32) {
     for (int j = threadIdx.x; j < h; j += 256) ((float*)out)[ob + j] = ((const float*)table)[tb + j];
+  } else if (vec16) {
+    // 8 elements (16 bytes) a lane: the launcher checked h % 8, ldo % 8 and
+    // the 16-byte alignment of both bases
+    const uint4* src = (const uint4*)((const uint16_t*)table + tb);
+    uint4* dst = (uint4*)((uint16_t*)out + ob);
+    for (int j = threadIdx.x; j < (h >> 3); j += 256) dst[j] = src[j];
   } else {
     for (int j = threadIdx.x; j < h; j += 256) ((uint16_t*)out)[ob + j] = ((const uint16_t*)table)[tb + j];
   }
@@ -285,8 +292,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* __restrict__ tab
 
 hipError_t launch_embed(const void* table, int ttype, int h, int vocab, const int32_t* tokens, int mask_mode,
                         int mask_token, int rows, void* out, int ldo, int32_t* status, hipStream_t s) {
+  const int vec16 = ttype != T_F32 && h % 8 == 0 && ldo % 8 == 0 && (uintptr_t)table % 16 == 0 &&
+                    (uintptr_t)out % 16 == 0;
   hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, table, ttype, h, vocab, tokens, mask_mode,
-                     mask_token, out, ldo, status);
+                     mask_token, out, ldo, status, vec16);
   return hipGetLastError();
 }
 
