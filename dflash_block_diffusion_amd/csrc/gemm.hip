@@ -654,6 +654,11 @@ Plan make_plan(int fmt, int n, int k, int m, int epi) {
     // on 128 work-groups per split): chunks of 3, so no dead fourth tile is
     // streamed and multiplied (7.7 against 8.6 us a launch)
     if (p.RT == 4 && (p.ntile16 + p.PR - 1) / p.PR == 3) p.RT = 3;
+    // ... whose 12 tiles a wave split over eight waves (two per SIMD, 6 tiles
+    // each) overlap one wave's dequantisation with the other's MFMAs better
+    // than the wider epilogue skew costs (7.6 against 7.3 us a launch; every
+    // other partial-sum shape measured slower with eight waves)
+    if (p.RT == 3 && p.MB == 2) p.NW = 8;
   } else if (epi == EPI_SILU) {
     const int tiles256 = (p.ntile16 + 255) / 256;
     p.PR = std::min(units, tiles256 > p.RT ? 512 : 256);
