@@ -123,39 +123,34 @@ struct GdnSmem {
 
 
 // The projections of the T tokens at rows row0.. of a block (materialised in
-// the activation format later, at the LDS store): element idx = tid + u NT of
-// the block's T x (k, q, v, a, b) values.  The K splits are added in their
-// fixed order, one split's loads all in flight at once.
+// the activation format later, at the LDS store): thread e takes column e of
+// the head's k, q, v, a, b (NCOL <= threads) for every token, raw[t] for
+// token t, so its address is one base plus t rows and every load of the
+// block goes out before any is used.  The K splits are added in their fixed
+// order.
 template <int DK, int DV, int TM>
-__device__ __forceinline__ void gdn_load_block(const GdnCall& c, int row0, int T,
-                                               float (&raw)[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)]) {
-  constexpr int NT = 4 * DV, NCOL = 2 * DK + DV + 2, PER = (TM * NCOL + NT - 1) / NT;
-  const int h = blockIdx.x, tid = threadIdx.x, gh = c.gh;
+__device__ __forceinline__ void gdn_load_block(const GdnCall& c, int row0, int T, float (&raw)[TM]) {
+  constexpr int NT = 4 * DV, NCOL = 2 * DK + DV + 2;
+  static_assert(NCOL <= NT, "one projection column per thread");
+  const int h = blockIdx.x, e = threadIdx.x, gh = c.gh;
   const size_t qo = (size_t)h * DK, ko = (size_t)gh * DK + (size_t)h * DK;
   const size_t vo = (size_t)2 * gh * DK + (size_t)h * DV;
   const size_t ao = (size_t)2 * gh * DK + (size_t)gh * DV + h, bo = ao + gh;
-  // offsets within one split (< 2^31 floats: at most 1024 rows of the
-  // projection); -1 past the block
-  int off[PER];
+  const bool live = e < NCOL;
+  const size_t col = e < DK ? ko + e : e < 2 * DK ? qo + (e - DK) : e < 2 * DK + DV ? vo + (e - 2 * DK)
+                                                                                   : (e == 2 * DK + DV ? ao : bo);
+  const float* p = c.proj.p + (size_t)row0 * c.proj.ld + (live ? col : 0);
+  // unconditional loads (rows past the block re-read its last row, idle
+  // threads column 0), zeroed after: no branch between the loads
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int idx = tid + u * NT;
-    off[u] = -1;
-    if (idx < T * NCOL) {
-      const int t = idx / NCOL, e = idx % NCOL;
-      const size_t col = e < DK ? ko + e : e < 2 * DK ? qo + (e - DK) : e < 2 * DK + DV ? vo + (e - 2 * DK)
-                                                                                         : (e == 2 * DK + DV ? ao : bo);
-      off[u] = (row0 + t) * c.proj.ld + (int)col;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) raw[u] = off[u] >= 0 ? c.proj.p[off[u]] : 0.f;
+  for (int t = 0; t < TM; ++t) raw[t] = p[(size_t)min(t, T - 1) * c.proj.ld];
   for (int sp = 1; sp < c.proj.S; ++sp) {
-    const float* ps = c.proj.p + (size_t)sp * c.proj.stride;
+    const float* ps = p + (size_t)sp * c.proj.stride;
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (off[u] >= 0) raw[u] = raw[u] + ps[off[u]];
+    for (int t = 0; t < TM; ++t) raw[t] = raw[t] + ps[(size_t)min(t, T - 1) * c.proj.ld];
   }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) raw[t] = live && t < T ? raw[t] : 0.f;
 }
 
 // The block of T tokens at projection / output rows row0..row0+T-1 against
@@ -169,7 +164,7 @@ __device__ __forceinline__ void gdn_load_block(const GdnCall& c, int row0, int T
 template <int DK, int DV, int TM>
 __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, float* tape_base,
                                              GdnSmem<DK, DV>& sm,
-                                             float (&raw)[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)],
+                                             float (&raw)[TM],
                                              int next_row0, int next_T) {
   constexpr int NT = 4 * DV;
   constexpr int RW = GDN_RW<DV>;
@@ -182,20 +177,15 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
   const int gh = c.gh;
 
   // 1a. the block's projections, materialised in the activation format:
-  //     row t of kq takes k, q (lane-major), v, a, b
+  //     row t of kq takes k, q (lane-major), v, a, b; thread e holds column e
   constexpr int NCOL = 2 * DK + DV + 2;
-  constexpr int PER = (TM * NCOL + NT - 1) / NT;
-  {
+  if (tid < NCOL) {
+    const int e = tid;
+    const int pos = e < DK ? kcol<DK, true>(e & 3, e >> 2)
+                           : e < 2 * DK ? KB + kcol<DK, true>((e - DK) & 3, (e - DK) >> 2) : VO + (e - 2 * DK);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < T * NCOL) {
-        const int t = idx / NCOL, e = idx % NCOL;
-        const int pos = e < DK ? kcol<DK, true>(e & 3, e >> 2)
-                               : e < 2 * DK ? KB + kcol<DK, true>((e - DK) & 3, (e - DK) >> 2) : VO + (e - 2 * DK);
-        sm.kq[t][pos] = act_round(c.atype, raw[u]);
-      }
-    }
+    for (int t = 0; t < TM; ++t)
+      if (t < T) sm.kq[t][pos] = act_round(c.atype, raw[t]);
   }
   if (next_row0 >= 0) gdn_load_block<DK, DV, TM>(c, next_row0, next_T, raw);
   __syncthreads();
@@ -315,6 +305,10 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   __shared__ GdnSmem<DK, DV> sm;
   const int h = blockIdx.x, tid = threadIdx.x, r = tid & 3;
   const int i = blockIdx.y * GDN_RW<DV> + (tid >> 2);
+  // the block's projections go out first and the state rows after them, so
+  // both are in flight together (the state's LDS stores wait for its loads)
+  float raw[GDN_MAXT];
+  gdn_load_block<DK, DV, GDN_MAXT>(c, 0, c.rows, raw);
   if (tid < 4 * GDN_RW<DV>) {
     const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
@@ -322,8 +316,6 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   }
   // (verify_block's first barrier orders these stores before their reads);
   // the head's first work-group records the tape
-  float raw[(GDN_MAXT * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)];
-  gdn_load_block<DK, DV, GDN_MAXT>(c, 0, c.rows, raw);
   verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm, raw, -1, 0);
 }
 
@@ -344,7 +336,7 @@ __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk,
 #pragma unroll
     for (int m = 0; m < DK / 4; ++m) S[m] = Sg[r + 4 * m];
   // block j + 1's projections load while block j is worked on
-  float raw[(TM * (2 * DK + DV + 2) + 4 * DV - 1) / (4 * DV)];
+  float raw[TM];
   gdn_load_block<DK, DV, TM>(c, 0, B, raw);
   for (int j = 0; j < nblk; ++j) {
     if (owner)
