@@ -538,8 +538,12 @@ static int setup_dims(dflash_state* s, const dflash_model* t, const dflash_model
   // positions past the keys, and the halved staging and scores outweigh the
   // combine's extra partials (8B shapes, attention + combine a layer: 11.1
   // against 13.4 us at ctx 256, 13.2 against 15.1 at ctx 1024; 16.5 against
-  // 15.8 at ctx 1536, where 256-key splits stay)
-  s->split = t->act != T_F32 && t->d.head_dim == 128 && s->capacity <= ATTN_SMALL_CAP ? ATTN_SPLIT_SMALL : ATTN_SPLIT;
+  // 15.8 at ctx 1536, where 256-key splits stay); and in block-16 states of
+  // up to 32 such splits, whose query rows make a single row group a KV
+  // head, so 256-key splits would leave most CUs idle (4B shapes at ctx
+  // 2048: 11.4 against 13.0 us; block 32 keeps 256: 13.6 against 14.0 us)
+  const bool small = s->capacity <= ATTN_SMALL_CAP || (block == 16 && s->capacity <= 32 * ATTN_SPLIT_SMALL);
+  s->split = t->act != T_F32 && t->d.head_dim == 128 && small ? ATTN_SPLIT_SMALL : ATTN_SPLIT;
   s->max_splits = (s->capacity + s->split - 1) / s->split;
   if (s->max_splits > 32) return fail(DFLASH_E_CAPACITY, "max_ctx too large (at most 32 attention splits)");
   // dense prompt chunks: an int4 or bf16 target (the projections have the
