@@ -214,6 +214,8 @@ __global__ __launch_bounds__(64 * NW * KH) void attn_mfma_kernel(AttnArgs a) {
   constexpr int NTH = NT / KH;                 // 16-key tiles of one key part
   static_assert(KH == 1 || KH == 2, "one or two key parts");
   static_assert((NTH / 2) % 2 == 0, "a key part holds whole 64-key pages");
+  static_assert(KH == 1 || NW * 8 * 64 * 16 <= ATTN_PAGES * 16384,
+                "the key-part merge keeps 8 KiB of partial outputs a wave in the K staging");
   // K and V^T staging as two LDS objects, so that waiting for the K loads
   // does not also wait for the V^T loads
   __shared__ __attribute__((aligned(16))) uint8_t ldsK[ATTN_PAGES * 16384];
@@ -822,6 +824,8 @@ static int device_cus() {
 }
 
 hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
+  // the combine takes one split a lane: checked before any launch
+  if (c.max_splits < 1 || c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   const float scale2 = LOG2E / sqrtf((float)c.d);
   dim3 grid(c.max_splits, c.hkv);
   if (c.atype == T_F32) {
@@ -881,7 +885,6 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (c.max_splits > COMBINE_MAX_SPLITS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(c.block_rows * c.hq), dim3(64), 0, s, c.o_part, c.ml_part,
                      c.dev_n, c.max_splits, c.split, c.block_rows, c.hq, c.d, c.out, c.otype, c.ldo, c.status,
                      c.hkv, c.atype != T_F32 ? 1 : 0);
