@@ -11,6 +11,13 @@
 //         raw codes, one fp32 partial per group, scaled and accumulated
 // Integer codes are exact in fp16, so the MFMA products are the exact products
 // of the dequantised weights (scale * code is applied in fp32 afterwards).
+// The W4 codes enter the MFMA in offset binary c = q + 8 as the fp16 subnormals
+// c * 2^-24 (a shift and an AND per pair of codes; the MFMA multiplies fp16
+// subnormal operands exactly); each group's accumulator starts at
+// -8 * 2^-24 * (sum of the group's activations), itself an MFMA of the
+// activation fragments against the constant operand -8 * 2^-24, so the group
+// sum is 2^-24 * sum (c - 8) * x, and the factor 2^24 is applied with the
+// per-row scale of the epilogue (a power of two: exact).
 // X for the quantised formats is stored as the fp16 encoding of its bf16 value.
 //
 // Packed layout: per tile of 16 weight rows x KT columns (KT = 32/64/128 for
@@ -19,8 +26,10 @@
 // ss of the tile, the 8 columns KT*t + 32*ss + 8*(l/16) + e, e = 0..7 -- one
 // lane's share of a 16x32 MFMA operand.  So every wave load is one fully
 // coalesced 1 KiB read and needs no shuffling.  W4 scales are packed per
-// (row tile, K tile) as 16 dwords, dword r = the two group scales of row r, so
-// that lane l reads its row's pair with one 4-byte load.  The activations come
+// (row tile, K tile) as 16 dwords, dword r = the two group scales of row r; one
+// 4-byte load per four row tiles fetches them (lane l: dword l % 16 of row tile
+// l / 16 of the four), and two lane-swap steps give every lane its row's pair
+// of all four.  The activations come
 // in the matching tiled layout (fm_index in common.h): every operand fragment
 // is a contiguous 1 KiB read as well.
 //
@@ -191,7 +200,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 template <int FMT, int RT, int MB>
 struct Stage {
   uint4 w[RT];
-  uint32_t s[RT];                 // W4: the two group scales of this lane's row
+  uint32_t s[(RT + 3) / 4];       // W4: scale pairs of four row tiles, one per 16 lanes
   uint4 x[MB][tile_k(FMT) / 32];
 };
 
@@ -233,7 +242,7 @@ void gemm_stream_kernel(GemmArgs a) {
   const int nk = kt1 - kt0;
   const int t0 = kt0 + nk * wave / NW, t1 = kt0 + nk * (wave + 1) / NW;
   const int nt = t1 - t0;
-  const uint32_t mlo = a.mlo, mhi = a.mhi, magic = a.magic;
+  const uint32_t mlo = a.mlo, magic = a.magic;
 
   floatx4 acc[RT][MB];
 #pragma unroll
@@ -257,7 +266,11 @@ void gemm_stream_kernel(GemmArgs a) {
     for (int r = 0; r < RT; ++r) {
       const uint32_t tile = (uint32_t)min(rtb + c * RT + r, rte - 1) * a.ktiles + t;
       f.w[r] = buf_load16(rw, vlane, tile * 1024u, true);
-      if (FMT == W_W4) f.s[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, vrow, tile * 64u, 0);
+      // lane (lr, g) fetches row lr's scale pair of row tile r + g
+      if (FMT == W_W4 && r % 4 == 0) {
+        const uint32_t rti = (uint32_t)min(rtb + c * RT + r + g, rte - 1);
+        f.s[r / 4] = __builtin_amdgcn_raw_buffer_load_b32(rs, rti * a.ktiles * 64u + vrow, (uint32_t)t * 64u, 0);
+      }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -267,6 +280,33 @@ void gemm_stream_kernel(GemmArgs a) {
   };
 
   auto compute = [&](const Stage<FMT, RT, MB>& f) {
+    // W4: the scale pair of row tile 4q + j sits in lane lr + 16 j of f.s[q];
+    // the 16-lane row swap and the 32-lane half swap put all four in every lane
+    uint32_t sq[RT];
+    // and the code offset of each group: -8 * 2^-24 * sum of its 64 activation columns
+    floatx4 corr[MB][2];
+    if (FMT == W_W4) {
+#pragma unroll
+      for (int q = 0; q < (RT + 3) / 4; ++q) {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(f.s[q], f.s[q], false, false);
+        const auto p0 = __builtin_amdgcn_permlane32_swap(p16[0], p16[0], false, false);
+        const auto p1 = __builtin_amdgcn_permlane32_swap(p16[1], p16[1], false, false);
+        if (4 * q + 0 < RT) sq[4 * q + 0] = p0[0];
+        if (4 * q + 1 < RT) sq[4 * q + 1] = p1[0];
+        if (4 * q + 2 < RT) sq[4 * q + 2] = p0[1];
+        if (4 * q + 3 < RT) sq[4 * q + 3] = p1[1];
+      }
+      const half8 neg8 = __builtin_bit_cast(half8, uint4{0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u});
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), neg8,
+                                                                    floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          corr[mb][gg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]),
+                                                                neg8, c0, 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       if (FMT == W_BF16) {
@@ -287,16 +327,16 @@ void gemm_stream_kernel(GemmArgs a) {
         }
       } else {  // W4: two 64-wide groups per tile, sub-steps (0,1) and (2,3)
         const uint32_t wd[4] = {f.w[r].x, f.w[r].y, f.w[r].z, f.w[r].w};
-        const half2v sc = h2(f.s[r]);
+        const half2v sc = h2(sq[r]);
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
-          const half8 b0 = deq_w4(wd[2 * gg], mlo, mhi, magic);
-          const half8 b1 = deq_w4(wd[2 * gg + 1], mlo, mhi, magic);
+          const half8 b0 = deq_w4_sub(wd[2 * gg], mlo);
+          const half8 b1 = deq_w4_sub(wd[2 * gg + 1], mlo);
           const float sg = (float)sc[gg];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), b0,
-                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                                                                 corr[mb][gg], 0, 0, 0);
             tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]), b1, tmp,
                                                          0, 0, 0);
 #pragma unroll
@@ -314,7 +354,8 @@ void gemm_stream_kernel(GemmArgs a) {
   for (int mb = 0; mb < MB; ++mb) { best[mb] = -INFINITY; bidx[mb] = 0x7fffffff; }
   const uint16_t* sc8 = (FMT == W_W8) ? a.s : nullptr;
   auto scale_of = [&](int n) -> float {
-    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : 1.0f;
+    // W4: the group sums carry the 2^-24 of the subnormal codes
+    return FMT == W_W8 ? (float)__builtin_bit_cast(_Float16, sc8[n]) : (FMT == W_W4 ? 16777216.0f : 1.0f);
   };
 
   // Chunk epilogue: fixed-order reduction of the NW wave partials,

@@ -31,6 +31,14 @@ __device__ __forceinline__ half8 deq_w4(uint32_t w, uint32_t mlo, uint32_t mhi, 
   return r;
 }
 
+// 8 int4 codes (one dword, offset binary, nibble slots as packed) -> the 8
+// fp16 subnormals c * 2^-24 in deq_w4's order: with mlo = 0x000F000F each AND
+// leaves one code in the low bits of each half
+__device__ __forceinline__ half8 deq_w4_sub(uint32_t w, uint32_t mlo) {
+  const uint32_t a = w & mlo, b = (w >> 4) & mlo, c = (w >> 8) & mlo, d = (w >> 12) & mlo;
+  return __builtin_bit_cast(half8, uint4{a, b, c, d});
+}
+
 // 8 int8 codes (two dwords, bytes in column order, offset binary) -> 8 halves:
 // byte pairs are spread to the low bytes of two fp16 lanes over the magic 0x64.
 __device__ __forceinline__ half8 deq_w8(uint32_t lo, uint32_t hi, uint32_t magic) {
