@@ -284,7 +284,31 @@ void gemm_stream_kernel(GemmArgs a) {
     // the 16-lane row swap and the 32-lane half swap put all four in every lane
     uint32_t sq[RT];
     // and the code offset of each group: -8 * 2^-24 * sum of its 64 activation columns
-    floatx4 corr[MB][2];
+    // (with three or four token blocks one group at a time, below)
+    constexpr int CG = MB <= 2 ? 2 : 1;
+    floatx4 corr[MB][CG];
+    const half8 neg8 = __builtin_bit_cast(half8, uint4{0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u});
+    auto offset_sum = [&](int mb, int gg, int slot) {
+      const floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), neg8,
+                                                                floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      corr[mb][slot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]),
+                                                              neg8, c0, 0, 0, 0);
+    };
+    // group gg of row tile r: the two MFMAs over its 64 columns, then the scale
+    auto w4_group = [&](int r, int gg, int slot) {
+      const half8 b0 = deq_w4_sub(gg == 0 ? f.w[r].x : f.w[r].z, mlo);
+      const half8 b1 = deq_w4_sub(gg == 0 ? f.w[r].y : f.w[r].w, mlo);
+      const float sg = (float)h2(sq[r])[gg];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), b0,
+                                                             corr[mb][slot], 0, 0, 0);
+        tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]), b1, tmp,
+                                                     0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[r][mb][v] += sg * tmp[v];
+      }
+    };
     if (FMT == W_W4) {
 #pragma unroll
       for (int q = 0; q < (RT + 3) / 4; ++q) {
@@ -296,16 +320,23 @@ void gemm_stream_kernel(GemmArgs a) {
         if (4 * q + 2 < RT) sq[4 * q + 2] = p0[1];
         if (4 * q + 3 < RT) sq[4 * q + 3] = p1[1];
       }
-      const half8 neg8 = __builtin_bit_cast(half8, uint4{0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u});
+      if constexpr (MB <= 2) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+          offset_sum(mb, 0, 0);
+          offset_sum(mb, 1, 1);
+        }
+      } else {
+        // group-major: each accumulator still takes group 0 before group 1
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
-          const floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), neg8,
-                                                                    floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          corr[mb][gg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]),
-                                                                neg8, c0, 0, 0, 0);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) offset_sum(mb, gg, 0);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) w4_group(r, gg, 0);
         }
+        return;
+      }
     }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -326,23 +357,8 @@ void gemm_stream_kernel(GemmArgs a) {
                                                               acc[r][mb], 0, 0, 0);
         }
       } else {  // W4: two 64-wide groups per tile, sub-steps (0,1) and (2,3)
-        const uint32_t wd[4] = {f.w[r].x, f.w[r].y, f.w[r].z, f.w[r].w};
-        const half2v sc = h2(sq[r]);
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          const half8 b0 = deq_w4_sub(wd[2 * gg], mlo);
-          const half8 b1 = deq_w4_sub(wd[2 * gg + 1], mlo);
-          const float sg = (float)sc[gg];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            floatx4 tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg]), b0,
-                                                                 corr[mb][gg], 0, 0, 0);
-            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f.x[mb][2 * gg + 1]), b1, tmp,
-                                                         0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[r][mb][v] += sg * tmp[v];
-          }
-        }
+        w4_group(r, 0, 0);
+        w4_group(r, 1, CG - 1);
       }
     }
   };
