@@ -17,7 +17,9 @@
 // Thread layout: 4 consecutive lanes own value row i; lane r holds columns
 // j = r + 4m (m < dk/4).  The halving tree's strides dk/2 .. 4 stay inside a
 // lane; strides 2 and 1 are the xor-2 / xor-1 lane exchanges.
-// This file is compiled with -ffp-contract=off: no multiply-add fusion.
+// This file is compiled with -ffp-contract=off: no multiply-add fusion, except
+// in the verify's chunk-form outputs (steps 3-5 of verify_block), which feed
+// no state.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -252,6 +254,11 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     }
   }
   __syncthreads();
+  {
+  // Steps 3-5 feed only the block's outputs O (the tape and the state are
+  // set above and by the pinned replay), so their products and sums may fuse
+  // into multiply-adds: the forward substitution's dependent chain halves.
+#pragma clang fp contract(fast)
   // 3. A and M o QK^T (T x T each); gamma_t once per token
   if (tid < T) sm.ga[tid] = expf(sm.lga[tid]);
   for (int e = tid; e < 2 * T * T; e += NT) {
@@ -298,17 +305,20 @@ __device__ __forceinline__ void verify_block(const GdnCall& c, int row0, int T, 
     store_act(c.out, act_index(row0 + t, h * DV + il, c.ldo, c.otype == T_F32 ? 0 : c.gh * DV), c.otype, o,
               c.status);
   }
+  }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int TM>
 __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   __shared__ GdnSmem<DK, DV> sm;
   const int h = blockIdx.x, tid = threadIdx.x, r = tid & 3;
   const int i = blockIdx.y * GDN_RW<DV> + (tid >> 2);
   // the block's projections go out first and the state rows after them, so
   // both are in flight together (the state's LDS stores wait for its loads)
-  float raw[GDN_MAXT];
-  gdn_load_block<DK, DV, GDN_MAXT>(c, 0, c.rows, raw);
+  // TM: the most tokens of the instance (16 for 16-token blocks: no loads of
+  // rows past the block)
+  float raw[TM];
+  gdn_load_block<DK, DV, TM>(c, 0, c.rows, raw);
   if (tid < 4 * GDN_RW<DV>) {
     const float* Sg = c.S + ((size_t)h * DV + i) * DK;
 #pragma unroll
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(4 * DV) void gdn_verify_kernel(GdnCall c) {
   }
   // (verify_block's first barrier orders these stores before their reads);
   // the head's first work-group records the tape
-  verify_block<DK, DV, GDN_MAXT>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm, raw, -1, 0);
+  verify_block<DK, DV, TM>(c, 0, c.rows, blockIdx.y == 0 ? c.tape : nullptr, sm, raw, -1, 0);
 }
 
 // A prompt chunk of nblk blocks of B tokens, all committed: per block the
@@ -357,12 +367,18 @@ __global__ __launch_bounds__(4 * DV) void gdn_prompt_kernel(GdnCall c, int nblk,
 
 hipError_t launch_gdn_verify(const GdnCall& c, hipStream_t s) {
   if (c.rows < 1 || c.rows > 32) return hipErrorInvalidValue;    // one chunk of at most 32 tokens
-  if (c.dk == 128 && c.dv == 128)
-    hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), dim3(c.gh, 128 / GDN_RW<128>), dim3(512), 0, s, c);
-  else if (c.dk == 32 && c.dv == 32)
-    hipLaunchKernelGGL((gdn_verify_kernel<32, 32>), dim3(c.gh, 32 / GDN_RW<32>), dim3(128), 0, s, c);
-  else
+  const bool t16 = c.rows <= 16;
+  if (c.dk == 128 && c.dv == 128) {
+    const dim3 grid(c.gh, 128 / GDN_RW<128>);
+    if (t16) hipLaunchKernelGGL((gdn_verify_kernel<128, 128, 16>), grid, dim3(512), 0, s, c);
+    else hipLaunchKernelGGL((gdn_verify_kernel<128, 128, GDN_MAXT>), grid, dim3(512), 0, s, c);
+  } else if (c.dk == 32 && c.dv == 32) {
+    const dim3 grid(c.gh, 32 / GDN_RW<32>);
+    if (t16) hipLaunchKernelGGL((gdn_verify_kernel<32, 32, 16>), grid, dim3(128), 0, s, c);
+    else hipLaunchKernelGGL((gdn_verify_kernel<32, 32, GDN_MAXT>), grid, dim3(128), 0, s, c);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
